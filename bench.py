@@ -1,0 +1,328 @@
+"""Benchmark: effective HBM bandwidth and tokens/s of the causal depthwise
+short conv on one MI355X.
+
+Headline step: one conv1d_fwd_varlen call on the long single-sequence
+prefill -- dim 8192, T 14807, width 4, SiLU, bias, initial state, bf16 x
+stored token-contiguous (dim, T) as the benchmark page draws it.  K steps run
+back to back, rotating over 4 independent buffer sets (each 485 MB, together
+larger than the 256 MB Infinity Cache) so every step streams from HBM.
+
+Printed: ONE JSON line with the metric, the roofline of the kernel (its
+algorithmic bytes over its HIP-event-timed average duration, against the
+8 TB/s HBM peak), the single-threaded CPU oracle on the same workload, and
+secondary measurements (other prefill sizes, the T=1 decode latency, the
+varlen batch, the paged step, a same-size device copy).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extra] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective HBM GB/s (% of peak) + tokens/s, bf16 causal conv1d dim 8192 width 4"
+HEADLINE = dict(dim=8192, T=14807, width=4)
+KERNEL_SOURCES = ["causal_depthwise_short_conv1d_amd/csrc/fwd_tokmajor.hip",
+                  "causal_depthwise_short_conv1d_amd/csrc/sconv_device.h",
+                  "causal_depthwise_short_conv1d_amd/csrc/sconv_params.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_tokmajor_dim8192_T14807_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_bytes(dim, lengths, width, bias=True, n_init=None, n_state=None,
+              cache_indices=False, has_init=True):
+    """Algorithmic bytes of one varlen forward: x read and out written once per
+    processed token, weights and bias once, the state read for sequences that
+    continue from it and written for every processed sequence, and the index
+    arrays (query_start_loc, cache_indices, has_initial_state)."""
+    B = len(lengths)
+    n_init = B if n_init is None else n_init
+    n_state = B if n_state is None else n_state
+    toks = sum(lengths)
+    return (4 * toks * dim + 2 * dim * width + (2 * dim if bias else 0)
+            + 2 * (width - 1) * dim * (n_init + n_state)
+            + 4 * (B + 1) + (4 * B if cache_indices else 0) + (B if has_init else 0))
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def event_time_ms(fn, reps, flush=None, stream=None):
+    """Median per-launch time (HIP events on the launch stream); `flush` runs
+    untimed before each launch."""
+    import torch
+    times = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return statistics.median(times)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true", help="headline only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs on one GPU; multi-GPU runs are not part of it "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import causal_depthwise_short_conv1d_amd as S
+    import workloads as W
+
+    S.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dim, T, width = HEADLINE["dim"], HEADLINE["T"], HEADLINE["width"]
+    nbytes = fwd_bytes(dim, [T], width)
+
+    # ---- headline buffers: 4 sets rotated so each step misses the caches
+    log(f"[bench] headline dim={dim} T={T} width={width}: {nbytes/1e6:.2f} MB per step")
+    base = W.single_sequence(dim=dim, T=T, width=width, seed=W.seed_for(3, 0), device=dev)
+    sets = []
+    for i in range(4):
+        sets.append(dict(x=base["x"].clone(), out=torch.empty_like(base["x"]),
+                         st=base["conv_states"].clone()))
+    qsl, hi = base["query_start_loc"], base["has_initial_state"]
+    w, b = base["weight"], base["bias"]
+
+    def step(i):
+        s = sets[i % len(sets)]
+        S.conv1d_fwd_varlen(s["x"], w, b, s["st"], qsl, has_initial_state=hi,
+                            activation="silu", out=s["out"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = ev0.elapsed_time(ev1) / args.steps
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    log(f"[bench] {args.steps} steps: {ms_per_step*1e3:.1f} us/step wall, "
+        f"{kern_ms*1e3:.1f} us/launch (events) -> {achieved:.0f} GB/s")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("kernel_hash") == kernel_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16",
+        "data": "synthetic (randn*0.02 bf16, seeded, drawn on the GPU)",
+        "config": {"workload": "long single-sequence prefill, dim 8192, T 14807, width 4, "
+                               "SiLU, bias, initial state, x (dim,T) token-contiguous bf16",
+                   "dim": dim, "T": T, "width": width, "layout": "(dim,T)",
+                   "bytes_per_step": nbytes},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "fwd_tokmajor_kernel<4,true>",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(kern_ms * 1e3, 2)},
+    }
+    del sets
+
+    if not args.no_extra:
+        result["extra"] = extras(torch, S, W, dev)
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(torch, W, nbytes, base)
+    print(json.dumps(result), flush=True)
+
+
+def extras(torch, S, W, dev):
+    """Secondary measurements, each launch timed alone after a 1 GiB write that
+    evicts the caches (median of the repetitions)."""
+    ex = {}
+    scratch = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+    flush = lambda: scratch.fill_(1)
+
+    sweep = {}
+    for dim, Ts in ((4096, (1, 128, 256, 514, 1024)), (8192, (4195, 11027, 14807))):
+        for T in Ts:
+            for layout in ("dim_tok", "tok_dim"):
+                d = W.single_sequence(dim=dim, T=T, width=4, seed=W.seed_for(3, T % 97),
+                                      device=dev, layout=layout)
+                out = torch.empty_like(d["x"])
+                fn = lambda: S.conv1d_fwd_varlen(d["x"], d["weight"], d["bias"],
+                                                 d["conv_states"], d["query_start_loc"],
+                                                 has_initial_state=d["has_initial_state"],
+                                                 out=out)
+                fn()
+                ms = event_time_ms(fn, 15, flush)
+                nb = fwd_bytes(dim, [T], 4)
+                sweep[f"dim{dim}_T{T}_{layout}"] = {"us": round(ms * 1e3, 2),
+                                                    "GB/s": round(nb / ms / 1e6, 1)}
+                log(f"[bench] prefill dim{dim} T{T} {layout}: {ms*1e3:.2f} us {nb/ms/1e6:.0f} GB/s")
+    ex["prefill_sweep"] = sweep
+
+    # decode: T=1 at dim 4096 through the decode entry point
+    d = W.decode_batch(batch=1, dim=4096, width=4, seed=W.seed_for(2, 1), device=dev)
+    xo = d["x"].clone()
+    fn = lambda: S.conv1d_update_decode(d["x"], d["conv_state"], d["weight"], d["bias"],
+                                        activation="silu", cache_indices=d["cache_indices"],
+                                        out=xo)
+    fn()
+    kern = event_time_ms(fn, 200, None)
+    lat = []
+    for _ in range(1000):
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        lat.append(time.perf_counter() - t0)
+    dec_bytes = 4 * 4096 + 4 * 3 * 4096 + 2 * 4096 * 4 + 2 * 4096 + 4
+    ex["decode_dim4096_T1"] = {"kernel_us": round(kern * 1e3, 2),
+                               "host_latency_us_median": round(statistics.median(lat) * 1e6, 2),
+                               "bytes": dec_bytes}
+    log(f"[bench] decode dim4096 T1: kernel {kern*1e3:.2f} us, host latency "
+        f"{statistics.median(lat)*1e6:.1f} us")
+
+    # varlen continuous batch, widths 2..5, channel-contiguous
+    vl = {}
+    for width in (2, 3, 4, 5):
+        d = W.varlen_batch(dim=8192, width=width, seed=W.seed_for(4, width), device=dev)
+        out = torch.empty_like(d["x"])
+        lens = d["lengths"].tolist()
+        lines = d["cache_indices"].tolist()
+        init = d["has_initial_state"].tolist()
+        kept = [l for l, c in zip(lens, lines) if c != -1]
+        n_init = sum(1 for l, c, h in zip(lens, lines, init) if c != -1 and h and l > 0)
+        n_state = sum(1 for l, c in zip(lens, lines) if c != -1 and l > 0)
+        nb = fwd_bytes(8192, kept, width, n_init=n_init, n_state=n_state,
+                       cache_indices=True) + 4 * (len(lens) - len(kept)) + (len(lens) - len(kept))
+        cs = d["conv_states"]
+        fn = lambda: S.conv1d_fwd_varlen(d["x"], d["weight"], d["bias"], cs,
+                                         d["query_start_loc"], cache_indices=d["cache_indices"],
+                                         has_initial_state=d["has_initial_state"], out=out)
+        fn()
+        ms = event_time_ms(fn, 10, flush)
+        vl[f"W{width}"] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
+                           "tokens": sum(kept), "tokens_per_s": round(sum(kept) / ms * 1e3, 1)}
+        log(f"[bench] varlen W{width}: {ms*1e3:.1f} us {nb/ms/1e6:.0f} GB/s")
+        del d, out, cs
+    ex["varlen_64seq_dim8192"] = vl
+
+    # paged mixed step
+    cfg = W.PAGED_MIXED
+    d = W.paged_batch(H=cfg["H"], ws=cfg["ws"], N=cfg["N"], D=cfg["D"], off_s=cfg["off_s"],
+                      num_blocks=cfg["num_blocks"], width=cfg["width"], n_decode=cfg["n_decode"],
+                      n_prefill=cfg["n_prefill"], chunk=cfg["chunk"], max_pos=cfg["max_pos"],
+                      pad_frac=cfg["pad_frac"], seed=W.seed_for(5), device=dev)
+    out = torch.empty_like(d["x"])
+    fn = lambda: S.sconv_paged_fused(d["x"], d["weight"], d["cache"], d["positions"],
+                                     d["slot_mapping"], d["query_start_loc"], d["block_table"],
+                                     d["off_s"], d["ws"], activation="silu", use_residual=True,
+                                     out=out)
+    fn()
+    ms = event_time_ms(fn, 20, flush)
+    Tp, C = d["x"].shape
+    valid = int((d["slot_mapping"] >= 0).sum())
+    R = d["query_start_loc"].numel() - 1
+    # cached taps read: width-1 positions per request (all >= 0 by construction)
+    nb = 2 * C * Tp * 2 + 2 * C * valid + 2 * C * 3 * R + 2 * C * 4 + 16 * Tp + 4 * (R + 1)
+    ex["paged_mixed_T4128_C4096"] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
+                                     "bytes": nb}
+    log(f"[bench] paged: {ms*1e3:.1f} us {nb/ms/1e6:.0f} GB/s")
+    del d, out
+
+    # practical copy ceiling: a device copy moving the headline's byte count
+    n = 8192 * 14807
+    src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    fn = lambda: dst.copy_(src)
+    fn()
+    ms = event_time_ms(fn, 15, flush)
+    ex["device_copy_same_bytes"] = {"us": round(ms * 1e3, 2), "GB/s": round(4 * n / ms / 1e6, 1),
+                                    "bytes": 4 * n}
+    log(f"[bench] copy: {ms*1e3:.1f} us {4*n/ms/1e6:.0f} GB/s")
+    del scratch, src, dst
+    torch.cuda.synchronize()
+    return ex
+
+
+def cpu_baseline(torch, W, nbytes, base):
+    """The oracle (plain C, one thread) on the headline workload, repeated
+    until at least 10 s of CPU time have been spent (at most 3 passes)."""
+    import oracle
+    x = base["x"].cpu()
+    wgt, b = base["weight"].cpu(), base["bias"].cpu()
+    qsl, hi = base["query_start_loc"].cpu(), base["has_initial_state"].cpu()
+    out = torch.empty_like(x)
+    times = []
+    while sum(times) < 10.0 and len(times) < 3:
+        st = base["conv_states"].cpu().clone()
+        t0 = time.perf_counter()
+        oracle.fwd_varlen(x, wgt, b, st, qsl, out, has_initial_state=hi, activation="silu")
+        times.append(time.perf_counter() - t0)
+    per = sum(times) / len(times)
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    log(f"[bench] cpu oracle: {per:.2f} s per pass ({len(times)} passes)")
+    return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the full headline workload (dim 8192 x T 14807, width 4), "
+                      f"{len(times)} pass(es), {per:.2f} s each, single thread",
+            "tokens_per_s": round(HEADLINE['T'] / per, 1),
+            "host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,266 @@
+"""libsconv: causal depthwise short convolution on MI355X (gfx950).
+
+Thin Python binding over the C ABI declared in include/sconv.h.  It only
+marshals torch tensors into device pointers, element strides and the current
+HIP stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if libsconv.so is missing or a call is rejected, the
+binding raises.
+
+Entry points (same names as the C ABI):
+  conv1d_fwd_varlen    -- varlen prefill with per-sequence conv state
+  conv1d_update_decode -- decode update (state shift), in place allowed
+  sconv_paged_fused    -- paged sliding-window cache insert + conv
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["conv1d_fwd_varlen", "conv1d_update_decode", "sconv_paged_fused",
+           "SconvError", "library_path", "load_library", "exported_symbols",
+           "version", "status_string"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libsconv.so")
+_lib = None
+
+ACT_NONE, ACT_SILU = 0, 1
+
+
+class SconvError(RuntimeError):
+    """A libsconv call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library(path: str | None = None):
+    """Load libsconv.so (built by causal_depthwise_short_conv1d_amd.build).
+    Raises FileNotFoundError when it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(
+            f"libsconv not built: {p} is missing "
+            "(run python -m causal_depthwise_short_conv1d_amd.build)")
+    lib = ctypes.CDLL(p)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.sconv_status_string.argtypes = [ctypes.c_int]
+    lib.sconv_status_string.restype = ctypes.c_char_p
+    lib.sconv_version.argtypes = []
+    lib.sconv_version.restype = ctypes.c_int
+    lib.conv1d_fwd_varlen.argtypes = [
+        P, I64, I64, P, I64, P, P, I64, I64, I64, I64, P, P, P,
+        I32, I64, I32, I32, I32, I32, P, I64, I64, P]
+    lib.conv1d_update_decode.argtypes = [
+        P, I64, I64, I64, P, I64, P, P, I64, I64, I64, I64, P,
+        I32, I32, I32, I32, I32, I32, P, I64, I64, I64, P]
+    lib.sconv_paged_fused.argtypes = [
+        P, I64, P, I64, P, P, I64, I64, I64, I64, I32, I32, I32, I32, I32,
+        P, P, P, I32, P, I64, I32, I64, I32, I32, I32, P, I64, P]
+    for f in (lib.conv1d_fwd_varlen, lib.conv1d_update_decode, lib.sconv_paged_fused):
+        f.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def exported_symbols() -> list[str]:
+    return ["sconv_status_string", "sconv_version", "conv1d_fwd_varlen",
+            "conv1d_update_decode", "sconv_paged_fused"]
+
+
+def version() -> tuple[int, int]:
+    v = load_library().sconv_version()
+    return v >> 16, v & 0xFFFF
+
+
+def status_string(status: int) -> str:
+    try:
+        return load_library().sconv_status_string(int(status)).decode()
+    except FileNotFoundError:
+        return "unknown"
+
+
+# ------------------------------------------------------------ marshalling --
+
+def _dev(t: torch.Tensor | None, dtype: torch.dtype, name: str, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _index(t, dtype, name, device, n=None):
+    p = _dev(t, dtype, name, device)
+    if t is not None:
+        if t.dim() != 1 or (t.numel() > 1 and t.stride(0) != 1):
+            raise ValueError(f"{name} must be a contiguous 1-D tensor")
+        if n is not None and t.numel() < n:
+            raise ValueError(f"{name} needs at least {n} entries")
+    return p
+
+
+def _act(activation) -> int:
+    if activation is True or activation in ("silu", "swish"):
+        return ACT_SILU
+    if activation in (None, False):
+        return ACT_NONE
+    raise ValueError(f"unsupported activation {activation!r}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _call(fn: str, *args) -> None:
+    rc = getattr(load_library(), fn)(*args)
+    if rc != 0:
+        raise SconvError(fn, rc)
+
+
+def conv1d_fwd_varlen(x, weight, bias, conv_states, query_start_loc,
+                      cache_indices=None, has_initial_state=None,
+                      activation="silu", pad_slot_id: int = -1, out=None):
+    """Varlen prefill.  x: logical (dim, total_T) bf16, token-contiguous
+    (compact (dim, T)) or channel-contiguous ((T, dim) storage viewed as
+    (dim, T)); weight (dim, width); bias (dim,) or None; conv_states
+    (lines, dim, width-1) or None, updated in place; query_start_loc int32
+    (batch+1,); cache_indices int32 (batch,) or None; has_initial_state bool
+    (batch,) or None.  Returns out (a new tensor with x's strides unless
+    given)."""
+    dev = x.device
+    dim, total = x.shape
+    width = weight.shape[1]
+    batch = query_start_loc.numel() - 1
+    if weight.dim() != 2 or weight.shape[0] != dim or weight.stride(1) != 1:
+        raise ValueError("weight must be (dim, width) with unit width stride")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    if bias is not None and (bias.shape != (dim,) or bias.stride(0) != 1):
+        raise ValueError("bias must be a contiguous (dim,) tensor")
+    cs = conv_states
+    if cs is not None and (cs.dim() != 3 or cs.shape[1] != dim or cs.shape[2] != width - 1):
+        raise ValueError("conv_states must be (lines, dim, width-1)")
+    bf = torch.bfloat16
+    args = (
+        _dev(x, bf, "x", dev), x.stride(0), x.stride(1),
+        _dev(weight, bf, "weight", dev), weight.stride(0),
+        _dev(bias, bf, "bias", dev),
+        _dev(cs, bf, "conv_states", dev),
+        *(cs.stride() if cs is not None else (0, 0, 0)),
+        cs.shape[0] if cs is not None else 0,
+        _index(cache_indices, torch.int32, "cache_indices", dev, batch),
+        _index(has_initial_state, torch.bool, "has_initial_state", dev, batch),
+        _index(query_start_loc, torch.int32, "query_start_loc", dev),
+        batch, total, dim, width, _act(activation), pad_slot_id,
+        _dev(out, bf, "out", dev), out.stride(0), out.stride(1),
+    )
+    with torch.cuda.device(dev):
+        _call("conv1d_fwd_varlen", *args, _stream(dev))
+    return out
+
+
+def conv1d_update_decode(x, conv_state, weight, bias=None, activation=None,
+                         cache_indices=None, pad_slot_id: int = -1, out=None):
+    """Decode update.  x: (batch, dim) or (batch, dim, seqlen) bf16;
+    conv_state (lines, dim, width-1) updated in place; returns out, which
+    may be x itself (pass out=x to compute in place)."""
+    dev = x.device
+    squeeze = x.dim() == 2
+    xv = x.unsqueeze(-1) if squeeze else x
+    ov = None
+    if out is not None:
+        ov = out.unsqueeze(-1) if out.dim() == 2 else out
+    else:
+        ov = torch.empty_like(xv)
+    batch, dim, seqlen = xv.shape
+    width = weight.shape[1]
+    if weight.dim() != 2 or weight.shape[0] != dim or weight.stride(1) != 1:
+        raise ValueError("weight must be (dim, width) with unit width stride")
+    if conv_state.dim() != 3 or conv_state.shape[1] != dim or conv_state.shape[2] != width - 1:
+        raise ValueError("conv_state must be (lines, dim, width-1)")
+    if bias is not None and (bias.shape != (dim,) or bias.stride(0) != 1):
+        raise ValueError("bias must be a contiguous (dim,) tensor")
+    if ov.shape != xv.shape:
+        raise ValueError("out must have x's shape")
+    bf = torch.bfloat16
+    args = (
+        _dev(xv, bf, "x", dev), *xv.stride(),
+        _dev(weight, bf, "weight", dev), weight.stride(0),
+        _dev(bias, bf, "bias", dev),
+        _dev(conv_state, bf, "conv_state", dev), *conv_state.stride(), conv_state.shape[0],
+        _index(cache_indices, torch.int32, "cache_indices", dev, batch),
+        batch, dim, seqlen, width, _act(activation), pad_slot_id,
+        _dev(ov, bf, "out", dev), *ov.stride(),
+    )
+    with torch.cuda.device(dev):
+        _call("conv1d_update_decode", *args, _stream(dev))
+    if out is not None:
+        return out
+    return ov.squeeze(-1) if squeeze else ov
+
+
+def sconv_paged_fused(x, weight, cache, positions, slot_mapping, query_start_loc,
+                      block_table, off_s: int, ws: int, activation=None,
+                      use_residual: bool = True, bias=None, out=None):
+    """Paged insert + conv.  x (T, H*ws) bf16; weight (H*ws, width); cache
+    (num_blocks, H, N, D) bf16 with unit D stride, updated in place;
+    positions / slot_mapping int64 (T,); query_start_loc int32 (R+1,);
+    block_table int32 (R, max_blocks).  Returns out (T, H*ws)."""
+    dev = x.device
+    T, C = x.shape
+    num_blocks, H, N, D = cache.shape
+    width = weight.shape[1]
+    num_reqs = query_start_loc.numel() - 1
+    if C != H * ws:
+        raise ValueError("x's channel count must be cache heads * ws")
+    if x.stride(1) != 1 or cache.stride(3) != 1:
+        raise ValueError("x channels and cache D must have unit stride")
+    if weight.dim() != 2 or weight.shape[0] != C or weight.stride(1) != 1:
+        raise ValueError("weight must be (C, width) with unit width stride")
+    if bias is not None and (bias.shape != (C,) or bias.stride(0) != 1):
+        raise ValueError("bias must be a contiguous (C,) tensor")
+    if block_table.dim() != 2 or (block_table.numel() and block_table.stride(1) != 1):
+        raise ValueError("block_table must be 2-D with unit column stride")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.stride(1) != 1:
+        raise ValueError("out must be (T, C) with unit channel stride")
+    bf = torch.bfloat16
+    args = (
+        _dev(x, bf, "x", dev), x.stride(0),
+        _dev(weight, bf, "weight", dev), weight.stride(0),
+        _dev(bias, bf, "bias", dev),
+        _dev(cache, bf, "cache", dev), cache.stride(0), cache.stride(1), cache.stride(2),
+        num_blocks, H, N, D, off_s, ws,
+        _index(positions, torch.int64, "positions", dev, T),
+        _index(slot_mapping, torch.int64, "slot_mapping", dev, T),
+        _index(query_start_loc, torch.int32, "query_start_loc", dev),
+        num_reqs,
+        _dev(block_table, torch.int32, "block_table", dev), block_table.stride(0),
+        block_table.shape[1],
+        T, width, _act(activation), int(bool(use_residual)),
+        _dev(out, bf, "out", dev), out.stride(0),
+    )
+    with torch.cuda.device(dev):
+        _call("sconv_paged_fused", *args, _stream(dev))
+    return out

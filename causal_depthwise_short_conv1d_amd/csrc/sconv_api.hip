@@ -1,0 +1,318 @@
+// libsconv C ABI: host-side validation, layout dispatch and launch.
+// Nothing here touches device memory or synchronises; every successful call
+// enqueues exactly one kernel on the caller's stream.
+#include <stddef.h>
+#include <initializer_list>
+#include <stdint.h>
+
+#include "sconv.h"
+#include "sconv_params.h"
+
+using namespace sconv;
+
+namespace {
+
+constexpr int kVersionMajor = 1;
+constexpr int kVersionMinor = 0;
+
+// Byte range [lo, hi) covered by a strided bf16 tensor; empty when a size is 0.
+struct Span {
+    uintptr_t lo = 0, hi = 0;
+    bool empty() const { return hi <= lo; }
+};
+
+Span span_of(const void *p, std::initializer_list<int64_t> sizes,
+             std::initializer_list<int64_t> strides, int64_t elem = 2) {
+    Span s;
+    if (!p) return s;
+    int64_t last = 0;
+    auto st = strides.begin();
+    for (int64_t n : sizes) {
+        if (n <= 0) return s;
+        last += (n - 1) * *st++;
+    }
+    s.lo = reinterpret_cast<uintptr_t>(p);
+    s.hi = s.lo + uintptr_t((last + 1) * elem);
+    return s;
+}
+
+bool overlap(const Span &a, const Span &b) {
+    return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? SCONV_OK : SCONV_ERR_LAUNCH; }
+
+// Channel-contiguous storage: unit channel stride, 16-byte aligned rows.
+bool chanlast_ok(int64_t sd, int64_t st, int64_t dim, int64_t T) {
+    return sd == 1 && (T == 1 || (st >= dim && st % kVec == 0));
+}
+// Token-contiguous storage: a compact (dim, T) array.
+bool tokmajor_ok(int64_t sd, int64_t st, int64_t dim, int64_t T) {
+    return st == 1 && (dim == 1 || sd == T);
+}
+
+// Tokens per channel-contiguous wave tile: enough tiles for ~16 waves per
+// CU, never fewer than 32 tokens (halo re-reads stay under 10%).
+int32_t chanlast_tile(int64_t T, int32_t n_slabs) {
+    const int64_t target_waves = 256 * 16;
+    int64_t bt = (T * n_slabs + target_waves - 1) / target_waves;
+    bt = (bt + 15) / 16 * 16;
+    if (bt < 32) bt = 32;
+    if (bt > 256) bt = 256;
+    return int32_t(bt);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sconv_status_string(int status) {
+    switch (status) {
+        case SCONV_OK: return "ok";
+        case SCONV_ERR_NULL: return "required pointer is null";
+        case SCONV_ERR_SHAPE: return "invalid or inconsistent size";
+        case SCONV_ERR_STRIDE: return "unsupported stride / layout";
+        case SCONV_ERR_WIDTH: return "width outside 2..5";
+        case SCONV_ERR_ALIAS: return "output overlaps an input";
+        case SCONV_ERR_ALIGN: return "pointer or stride misaligned for 16-byte vectors";
+        case SCONV_ERR_ARG: return "invalid enumerated argument";
+        case SCONV_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int sconv_version(void) { return (kVersionMajor << 16) | kVersionMinor; }
+
+int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
+                      const void *weight, int64_t w_stride_dim, const void *bias,
+                      void *conv_states, int64_t cs_stride_line, int64_t cs_stride_dim,
+                      int64_t cs_stride_tok, int64_t num_cache_lines,
+                      const int32_t *cache_indices, const uint8_t *has_initial_state,
+                      const int32_t *query_start_loc, int32_t batch, int64_t total_tokens,
+                      int32_t dim, int32_t width, int32_t activation, int32_t pad_slot_id,
+                      void *out, int64_t o_stride_dim, int64_t o_stride_tok,
+                      hipStream_t stream) {
+    if (width < SCONV_MIN_WIDTH || width > SCONV_MAX_WIDTH) return SCONV_ERR_WIDTH;
+    if (activation != SCONV_ACT_NONE && activation != SCONV_ACT_SILU) return SCONV_ERR_ARG;
+    if (batch < 0 || total_tokens < 0 || dim < 0 || num_cache_lines < 0) return SCONV_ERR_SHAPE;
+    if (total_tokens > INT32_MAX) return SCONV_ERR_SHAPE;       // offsets are int32
+    if (batch == 0 || total_tokens == 0 || dim == 0) return SCONV_OK;
+    if (!x || !weight || !query_start_loc || !out) return SCONV_ERR_NULL;
+    if (has_initial_state && !conv_states) return SCONV_ERR_NULL;
+    if (x_stride_dim < 0 || x_stride_tok < 0 || o_stride_dim < 0 || o_stride_tok < 0 ||
+        cs_stride_line < 0 || cs_stride_dim < 0 || cs_stride_tok < 0)
+        return SCONV_ERR_STRIDE;
+    if (w_stride_dim < width) return SCONV_ERR_STRIDE;
+    if (conv_states) {
+        if (num_cache_lines < 1) return SCONV_ERR_SHAPE;
+        if (!cache_indices && num_cache_lines < batch) return SCONV_ERR_SHAPE;
+    }
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(weight, 2) || !aligned(bias, 2) ||
+        !aligned(conv_states, 2) || !aligned(cache_indices, 4) || !aligned(query_start_loc, 4))
+        return SCONV_ERR_ALIGN;
+
+    const int64_t T = total_tokens;
+    const Span sx = span_of(x, {dim, T}, {x_stride_dim, x_stride_tok});
+    const Span so = span_of(out, {dim, T}, {o_stride_dim, o_stride_tok});
+    const Span sw = span_of(weight, {dim, width}, {w_stride_dim, 1});
+    const Span sbias = span_of(bias, {dim}, {1});
+    const Span scs = span_of(conv_states, {num_cache_lines, dim, width - 1},
+                             {cs_stride_line, cs_stride_dim, cs_stride_tok});
+    if (overlap(so, sx) || overlap(so, scs) || overlap(so, sw) || overlap(so, sbias) ||
+        overlap(scs, sx) || overlap(scs, sw) || overlap(scs, sbias))
+        return SCONV_ERR_ALIAS;
+
+    SeqBatch sb;
+    sb.qsl = query_start_loc;
+    sb.cache_idx = cache_indices;
+    sb.has_init = has_initial_state;
+    sb.cs = static_cast<uint16_t *>(conv_states);
+    sb.cs_sl = cs_stride_line;
+    sb.cs_sd = cs_stride_dim;
+    sb.cs_st = cs_stride_tok;
+    sb.num_lines = conv_states ? num_cache_lines : 0;
+    sb.batch = batch;
+    sb.pad_slot_id = pad_slot_id;
+    sb.total_T = T;
+    const bool silu = activation == SCONV_ACT_SILU;
+
+    if (chanlast_ok(x_stride_dim, x_stride_tok, dim, T) &&
+        chanlast_ok(o_stride_dim, o_stride_tok, dim, T)) {
+        FwdClParams p;
+        p.x = static_cast<const uint16_t *>(x);
+        p.out = static_cast<uint16_t *>(out);
+        p.x_st = T == 1 ? 0 : x_stride_tok;
+        p.o_st = T == 1 ? 0 : o_stride_tok;
+        p.w = static_cast<const uint16_t *>(weight);
+        p.w_sd = w_stride_dim;
+        p.bias = static_cast<const uint16_t *>(bias);
+        p.sb = sb;
+        p.dim = dim;
+        p.n_slabs = (dim + kSlab - 1) / kSlab;
+        p.bt = chanlast_tile(T, p.n_slabs);
+        p.n_tiles = int32_t((T + p.bt - 1) / p.bt);
+        if (uint64_t(p.n_tiles) * uint64_t(p.n_slabs) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;
+        return launch_status(launch_fwd_chanlast(p, width, silu, stream));
+    }
+    if (tokmajor_ok(x_stride_dim, x_stride_tok, dim, T) &&
+        tokmajor_ok(o_stride_dim, o_stride_tok, dim, T)) {
+        const uint64_t n = uint64_t(dim) * uint64_t(T);
+        if (n >= (uint64_t(1) << 32)) return SCONV_ERR_SHAPE;
+        FwdTokParams p;
+        p.x = static_cast<const uint16_t *>(x);
+        p.out = static_cast<uint16_t *>(out);
+        p.w = static_cast<const uint16_t *>(weight);
+        p.w_sd = w_stride_dim;
+        p.bias = static_cast<const uint16_t *>(bias);
+        p.sb = sb;
+        p.T = uint32_t(T);
+        p.divT = FastDivU32::make(uint32_t(T));
+        p.n_elems = uint32_t(n);
+        p.n_chunks = uint32_t((n + kVec - 1) / kVec);
+        p.dim = dim;
+        return launch_status(launch_fwd_tokmajor(p, width, silu, stream));
+    }
+    return SCONV_ERR_STRIDE;
+}
+
+int conv1d_update_decode(const void *x, int64_t x_stride_seq, int64_t x_stride_dim,
+                         int64_t x_stride_tok, const void *weight, int64_t w_stride_dim,
+                         const void *bias, void *conv_state, int64_t cs_stride_line,
+                         int64_t cs_stride_dim, int64_t cs_stride_tok, int64_t num_cache_lines,
+                         const int32_t *cache_indices, int32_t batch, int32_t dim, int32_t seqlen,
+                         int32_t width, int32_t activation, int32_t pad_slot_id, void *out,
+                         int64_t o_stride_seq, int64_t o_stride_dim, int64_t o_stride_tok,
+                         hipStream_t stream) {
+    if (width < SCONV_MIN_WIDTH || width > SCONV_MAX_WIDTH) return SCONV_ERR_WIDTH;
+    if (activation != SCONV_ACT_NONE && activation != SCONV_ACT_SILU) return SCONV_ERR_ARG;
+    if (batch < 0 || dim < 0 || seqlen < 0 || num_cache_lines < 0) return SCONV_ERR_SHAPE;
+    if (batch == 0 || dim == 0 || seqlen == 0) return SCONV_OK;
+    if (!x || !weight || !conv_state || !out) return SCONV_ERR_NULL;
+    if (x_stride_seq < 0 || x_stride_dim < 0 || x_stride_tok < 0 || o_stride_seq < 0 ||
+        o_stride_dim < 0 || o_stride_tok < 0 || cs_stride_line < 0 || cs_stride_dim < 0 ||
+        cs_stride_tok < 0)
+        return SCONV_ERR_STRIDE;
+    if (w_stride_dim < width) return SCONV_ERR_STRIDE;
+    if (num_cache_lines < 1 || (!cache_indices && num_cache_lines < batch)) return SCONV_ERR_SHAPE;
+    if (!aligned(x, 2) || !aligned(out, 2) || !aligned(weight, 2) || !aligned(bias, 2) ||
+        !aligned(conv_state, 2) || !aligned(cache_indices, 4))
+        return SCONV_ERR_ALIGN;
+    const uint64_t cblocks = (uint64_t(dim) + 255) / 256;
+    if (cblocks * uint64_t(batch) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;
+
+    const Span sx = span_of(x, {batch, dim, seqlen}, {x_stride_seq, x_stride_dim, x_stride_tok});
+    const Span so = span_of(out, {batch, dim, seqlen}, {o_stride_seq, o_stride_dim, o_stride_tok});
+    const Span scs = span_of(conv_state, {num_cache_lines, dim, width - 1},
+                             {cs_stride_line, cs_stride_dim, cs_stride_tok});
+    const Span sw = span_of(weight, {dim, width}, {w_stride_dim, 1});
+    const Span sbias = span_of(bias, {dim}, {1});
+    const bool in_place = out == x && o_stride_seq == x_stride_seq &&
+                          o_stride_dim == x_stride_dim && o_stride_tok == x_stride_tok;
+    if ((!in_place && overlap(so, sx)) || overlap(so, scs) || overlap(so, sw) ||
+        overlap(so, sbias) || overlap(scs, sx) || overlap(scs, sw) || overlap(scs, sbias))
+        return SCONV_ERR_ALIAS;
+
+    UpdParams p;
+    p.x = static_cast<const uint16_t *>(x);
+    p.x_sb = x_stride_seq;
+    p.x_sd = x_stride_dim;
+    p.x_st = x_stride_tok;
+    p.out = static_cast<uint16_t *>(out);
+    p.o_sb = o_stride_seq;
+    p.o_sd = o_stride_dim;
+    p.o_st = o_stride_tok;
+    p.w = static_cast<const uint16_t *>(weight);
+    p.w_sd = w_stride_dim;
+    p.bias = static_cast<const uint16_t *>(bias);
+    p.cs = static_cast<uint16_t *>(conv_state);
+    p.cs_sl = cs_stride_line;
+    p.cs_sd = cs_stride_dim;
+    p.cs_st = cs_stride_tok;
+    p.num_lines = num_cache_lines;
+    p.cache_idx = cache_indices;
+    p.batch = batch;
+    p.dim = dim;
+    p.seqlen = seqlen;
+    p.pad_slot_id = pad_slot_id;
+    return launch_status(launch_update_decode(p, width, activation == SCONV_ACT_SILU, stream));
+}
+
+int sconv_paged_fused(const void *x, int64_t x_stride_tok, const void *weight,
+                      int64_t w_stride_dim, const void *bias, void *cache, int64_t c_stride_blk,
+                      int64_t c_stride_head, int64_t c_stride_slot, int64_t num_blocks,
+                      int32_t num_heads, int32_t block_size, int32_t head_dim, int32_t off_s,
+                      int32_t ws, const int64_t *positions, const int64_t *slot_mapping,
+                      const int32_t *query_start_loc, int32_t num_reqs,
+                      const int32_t *block_table, int64_t bt_stride_req, int32_t max_blocks,
+                      int64_t num_tokens, int32_t width, int32_t activation,
+                      int32_t use_residual, void *out, int64_t o_stride_tok,
+                      hipStream_t stream) {
+    if (width < SCONV_MIN_WIDTH || width > SCONV_MAX_WIDTH) return SCONV_ERR_WIDTH;
+    if (activation != SCONV_ACT_NONE && activation != SCONV_ACT_SILU) return SCONV_ERR_ARG;
+    if (use_residual != 0 && use_residual != 1) return SCONV_ERR_ARG;
+    if (num_tokens < 0 || num_reqs < 0 || max_blocks < 0 || num_blocks < 0) return SCONV_ERR_SHAPE;
+    if (num_heads < 1 || ws < 1 || block_size < 1 || head_dim < 1 || off_s < 0 ||
+        int64_t(off_s) + ws > head_dim)
+        return SCONV_ERR_SHAPE;
+    if (num_tokens == 0) return SCONV_OK;
+    if (num_tokens > INT32_MAX) return SCONV_ERR_SHAPE;
+    if (!x || !weight || !cache || !positions || !slot_mapping || !query_start_loc || !out ||
+        (num_reqs > 0 && max_blocks > 0 && !block_table))
+        return SCONV_ERR_NULL;
+    const int64_t C = int64_t(num_heads) * ws;
+    if (C > INT32_MAX) return SCONV_ERR_SHAPE;
+    if (x_stride_tok < C || o_stride_tok < C || w_stride_dim < width || bt_stride_req < 0 ||
+        c_stride_blk < 0 || c_stride_head < 0 || c_stride_slot < 0)
+        return SCONV_ERR_STRIDE;
+    if (ws % kVec || off_s % kVec || c_stride_blk % kVec || c_stride_head % kVec ||
+        c_stride_slot % kVec || x_stride_tok % kVec || o_stride_tok % kVec || !aligned(x, 16) ||
+        !aligned(out, 16) || !aligned(cache, 16) || !aligned(weight, 2) || !aligned(bias, 2) ||
+        !aligned(positions, 8) || !aligned(slot_mapping, 8) || !aligned(query_start_loc, 4) ||
+        !aligned(block_table, 4))
+        return SCONV_ERR_ALIGN;
+
+    const Span sx = span_of(x, {num_tokens, C}, {x_stride_tok, 1});
+    const Span so = span_of(out, {num_tokens, C}, {o_stride_tok, 1});
+    const Span sc = span_of(cache, {num_blocks, num_heads, block_size, head_dim},
+                            {c_stride_blk, c_stride_head, c_stride_slot, 1});
+    const Span sw = span_of(weight, {C, width}, {w_stride_dim, 1});
+    const Span sbias = span_of(bias, {C}, {1});
+    if (overlap(so, sx) || overlap(so, sc) || overlap(so, sw) || overlap(so, sbias) ||
+        overlap(sc, sx) || overlap(sc, sw) || overlap(sc, sbias))
+        return SCONV_ERR_ALIAS;
+
+    PagedParams p;
+    p.x = static_cast<const uint16_t *>(x);
+    p.x_st = x_stride_tok;
+    p.out = static_cast<uint16_t *>(out);
+    p.o_st = o_stride_tok;
+    p.w = static_cast<const uint16_t *>(weight);
+    p.w_sd = w_stride_dim;
+    p.bias = static_cast<const uint16_t *>(bias);
+    p.cache = static_cast<uint16_t *>(cache);
+    p.c_sb = c_stride_blk;
+    p.c_sh = c_stride_head;
+    p.c_sn = c_stride_slot;
+    p.num_blocks = num_blocks;
+    p.block_size = block_size;
+    p.off_s = off_s;
+    p.ws = ws;
+    p.C = int32_t(C);
+    p.pos = positions;
+    p.slot = slot_mapping;
+    p.qsl = query_start_loc;
+    p.num_reqs = num_reqs;
+    p.bt = block_table;
+    p.bt_sr = bt_stride_req;
+    p.max_blocks = block_table ? max_blocks : 0;
+    p.T = num_tokens;
+    p.n_slabs = int32_t((C + kSlab - 1) / kSlab);
+    p.n_tiles = int32_t((num_tokens + kPagedBT - 1) / kPagedBT);
+    if (uint64_t(p.n_tiles) * uint64_t(p.n_slabs) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;
+    return launch_status(launch_paged_fused(p, width, activation == SCONV_ACT_SILU,
+                                            use_residual != 0, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Device-side helpers for the gfx950 short-conv kernels: bf16 packing,
+// 16-byte vector memory access, SiLU, and the varlen sequence lookup.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "sconv_params.h"
+
+namespace sconv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ bf16 --
+// A bf16 is the upper half of a binary32, so widening is a shift or a mask.
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf_one(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// fp32 -> bf16 round-to-nearest-even; gfx950 converts a pair in one
+// instruction (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ uint16_t to_bf16(float v) {
+    return uint16_t(pack_bf16x2(v, 0.0f) & 0xffffu);
+}
+
+// Unpack 8 bf16 held in a 16-byte vector into floats.
+__device__ __forceinline__ void unpack8(const u32x4 &v, float f[8]) {
+    f[0] = bf_lo(v.x); f[1] = bf_hi(v.x);
+    f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+    f[4] = bf_lo(v.z); f[5] = bf_hi(v.z);
+    f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+}
+__device__ __forceinline__ u32x4 pack8(const float f[8]) {
+    u32x4 r;
+    r.x = pack_bf16x2(f[0], f[1]);
+    r.y = pack_bf16x2(f[2], f[3]);
+    r.z = pack_bf16x2(f[4], f[5]);
+    r.w = pack_bf16x2(f[6], f[7]);
+    return r;
+}
+
+// ------------------------------------------------------------------ SiLU --
+// silu(a) = a * sigmoid(a) = a / (1 + e^-a), with the hardware exp2 and
+// reciprocal (about 1 ulp each, far below the bf16 output rounding).
+template <bool SILU>
+__device__ __forceinline__ float act(float a) {
+    if constexpr (SILU) {
+        const float e = __builtin_amdgcn_exp2f(a * -1.4426950408889634f);
+        return a * __builtin_amdgcn_rcpf(1.0f + e);
+    } else {
+        return a;
+    }
+}
+
+// -------------------------------------------------------- vector memory --
+__device__ __forceinline__ u32x4 ld16(const uint16_t *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ void st16_stream(uint16_t *p, const u32x4 &v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+__device__ __forceinline__ void st16(uint16_t *p, const u32x4 &v) {
+    *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// 8 consecutive channels of which only the first n (0..8) exist: a full
+// vector access when n == 8, element accesses otherwise (zero filled).
+__device__ __forceinline__ u32x4 ld8_partial(const uint16_t *p, int n) {
+    if (n >= 8) return ld16(p);
+    uint16_t e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = (i < n) ? p[i] : uint16_t(0);
+    u32x4 r;
+    r.x = e[0] | (uint32_t(e[1]) << 16);
+    r.y = e[2] | (uint32_t(e[3]) << 16);
+    r.z = e[4] | (uint32_t(e[5]) << 16);
+    r.w = e[6] | (uint32_t(e[7]) << 16);
+    return r;
+}
+__device__ __forceinline__ void st8_partial(uint16_t *p, const u32x4 &v, int n, bool stream) {
+    if (n >= 8) {
+        if (stream) st16_stream(p, v); else st16(p, v);
+        return;
+    }
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < n) p[i] = uint16_t((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
+}
+__device__ __forceinline__ uint16_t lane_elem(const u32x4 &v, int i) {
+    const uint32_t w = (i >> 1) == 0 ? v.x : (i >> 1) == 1 ? v.y : (i >> 1) == 2 ? v.z : v.w;
+    return uint16_t((w >> ((i & 1) * 16)) & 0xffffu);
+}
+
+// -------------------------------------------------- varlen sequence lookup --
+// Largest j in [0, n) with qsl[j] <= t (the token -> sequence search of the
+// Inkling page's metadata kernel).  Works for any qsl contents: the result
+// is always a valid index.
+__device__ __forceinline__ int32_t seq_search(const int32_t *qsl, int32_t n, int64_t t) {
+    int32_t lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (int64_t(qsl[mid]) <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// What the forward kernels need to know about one sequence.
+struct SeqInfo {
+    int64_t start, end;   // token range, clamped into [0, total_T]
+    int64_t line;         // cache line
+    bool skip;            // padded, or its line is out of range
+    bool init;            // continue from the cached state
+};
+
+__device__ __forceinline__ SeqInfo seq_info(const SeqBatch &sb, const int32_t *qsl, int32_t s) {
+    SeqInfo si;
+    int64_t a = qsl[s], b = qsl[s + 1];
+    a = a < 0 ? 0 : (a > sb.total_T ? sb.total_T : a);
+    b = b < a ? a : (b > sb.total_T ? sb.total_T : b);
+    si.start = a;
+    si.end = b;
+    si.line = sb.cache_idx ? int64_t(sb.cache_idx[s]) : int64_t(s);
+    si.skip = (sb.cache_idx && si.line == sb.pad_slot_id) ||
+              (sb.cs && (si.line < 0 || si.line >= sb.num_lines));
+    si.init = sb.cs && sb.has_init && sb.has_init[s] != 0;
+    return si;
+}
+
+// Map a launch-order block id to a tile id so that each XCD (blocks are
+// dealt round-robin to the 8 XCDs) walks one contiguous range of tiles:
+// neighbouring tiles, whose halos overlap, then share an L2.
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t nblocks) {
+    constexpr uint32_t kXcds = 8;
+    const uint32_t xcd = bid % kXcds, idx = bid / kXcds;
+    const uint32_t q = nblocks / kXcds, r = nblocks % kXcds;
+    return xcd * q + (xcd < r ? xcd : r) + idx;
+}
+
+}  // namespace sconv

@@ -1,0 +1,137 @@
+// Kernel parameter blocks and launcher declarations shared by the C ABI
+// (sconv_api.hip) and the kernel translation units.  Host and device code
+// both see these structs: the host fills them, kernels take them by value.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace sconv {
+
+// Exact unsigned 32-bit division by a launch constant d >= 1: with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+// n / d == (umulhi(m, n) + n) >> l for every n < 2^32 (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994).
+struct FastDivU32 {
+    uint32_t d;
+    uint32_t m;
+    uint32_t l;
+
+    static FastDivU32 make(uint32_t d) {
+        FastDivU32 f;
+        f.d = d;
+        uint32_t l = 0;
+        while (l < 32 && (uint64_t(1) << l) < d) ++l;
+        f.l = l;
+        f.m = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+        return f;
+    }
+    __host__ __device__ uint32_t div(uint32_t n) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+        uint32_t hi = __umulhi(m, n);
+#else
+        uint32_t hi = uint32_t((uint64_t(m) * n) >> 32);
+#endif
+        return uint32_t((uint64_t(hi) + n) >> l);
+    }
+};
+
+// Everything about the varlen batch that the forward kernels share.
+struct SeqBatch {
+    const int32_t *qsl;          // [batch + 1]
+    const int32_t *cache_idx;    // [batch] or null (line = sequence id)
+    const uint8_t *has_init;     // [batch] or null (all false)
+    uint16_t *cs;                // conv states or null
+    int64_t cs_sl, cs_sd, cs_st; // state strides (line, channel, column)
+    int64_t num_lines;
+    int32_t batch;
+    int32_t pad_slot_id;
+    int64_t total_T;
+};
+
+struct FwdTokParams {          // token-contiguous (dim, T) storage
+    const uint16_t *x;
+    uint16_t *out;
+    const uint16_t *w;
+    int64_t w_sd;
+    const uint16_t *bias;      // or null
+    SeqBatch sb;
+    uint32_t T;                // total tokens (row length)
+    FastDivU32 divT;
+    uint32_t n_elems;          // dim * T
+    uint32_t n_chunks;         // ceil(n_elems / 8)
+    int32_t dim;
+};
+
+struct FwdClParams {           // channel-contiguous (T, dim) storage
+    const uint16_t *x;
+    uint16_t *out;
+    int64_t x_st, o_st;        // row strides (elements, multiples of 8)
+    const uint16_t *w;
+    int64_t w_sd;
+    const uint16_t *bias;
+    SeqBatch sb;
+    int32_t dim;
+    int32_t n_slabs;           // ceil(dim / 512)
+    int32_t bt;                // tokens per wave tile
+    int32_t n_tiles;           // ceil(T / bt)
+};
+
+struct UpdParams {
+    const uint16_t *x;
+    int64_t x_sb, x_sd, x_st;
+    uint16_t *out;
+    int64_t o_sb, o_sd, o_st;
+    const uint16_t *w;
+    int64_t w_sd;
+    const uint16_t *bias;
+    uint16_t *cs;
+    int64_t cs_sl, cs_sd, cs_st;
+    int64_t num_lines;
+    const int32_t *cache_idx;
+    int32_t batch, dim, seqlen, pad_slot_id;
+};
+
+struct PagedParams {
+    const uint16_t *x;
+    int64_t x_st;
+    uint16_t *out;
+    int64_t o_st;
+    const uint16_t *w;
+    int64_t w_sd;
+    const uint16_t *bias;
+    uint16_t *cache;
+    int64_t c_sb, c_sh, c_sn;
+    int64_t num_blocks;
+    int32_t block_size, off_s, ws, C;
+    const int64_t *pos;
+    const int64_t *slot;
+    const int32_t *qsl;
+    int32_t num_reqs;
+    const int32_t *bt;
+    int64_t bt_sr;
+    int32_t max_blocks;
+    int64_t T;
+    int32_t n_slabs;
+    int32_t n_tiles;
+};
+
+// Launchers: each enqueues one kernel and returns hipGetLastError().
+hipError_t launch_fwd_tokmajor(const FwdTokParams &p, int width, bool silu, hipStream_t s);
+hipError_t launch_fwd_chanlast(const FwdClParams &p, int width, bool silu, hipStream_t s);
+hipError_t launch_update_decode(const UpdParams &p, int width, bool silu, hipStream_t s);
+hipError_t launch_paged_fused(const PagedParams &p, int width, bool silu, bool residual,
+                              hipStream_t s);
+
+// Tile geometry used by both the host (grid sizes) and the kernels.
+constexpr int kWaveSize = 64;
+constexpr int kVec = 8;                          // bf16 per 16-byte vector
+constexpr int kSlab = kWaveSize * kVec;          // channels per wave (512)
+constexpr int kTokWavesPerBlock = 4;
+constexpr int kTokRounds = 4;                    // 64-chunk rounds per wave
+constexpr int kClWavesPerBlock = 4;
+constexpr int kPagedWavesPerBlock = 4;
+constexpr int kPagedBT = 16;                     // tokens per paged wave tile
+constexpr int kQslLdsMax = 2048;                 // qsl entries staged in LDS
+
+}  // namespace sconv

@@ -1,0 +1,231 @@
+/*
+ * sconv.h -- C ABI of libsconv, a gfx950 (MI355X) library for the causal
+ * depthwise short convolution (width 2..5) used by hybrid / linear-attention
+ * language models.
+ *
+ * The operation, in the notation of the pages it comes from:
+ *
+ *   For a sequence s with inputs x[c][t], t < L, a per-channel history
+ *   h[c][k], k < W-1 (the cached last W-1 inputs, oldest first), weights
+ *   w[c][j], j < W, and bias b[c]:
+ *     u[c] = h[c] ++ x[c]
+ *     y[c][t] = b[c] + sum_j w[c][j] * u[c][t+j]       (fp32 accumulation)
+ *     out[c][t] = bf16(silu(y))  or  bf16(y)            (one rounding, RNE)
+ *     new h[c][k] = u[c][L+k]                           (last W-1 of u)
+ *
+ *   -- atrex-bench operator #003 "causal_conv1d", section "Reference
+ *      Implementation" (prefix by state, depthwise conv1d, last T outputs,
+ *      SiLU); tokenspeed causal_conv1d.py, causal_conv1d_fn and
+ *      causal_conv1d_update (varlen batches, cache lines, pads, state
+ *      update); Inkling sconv.py, fused_sconv (paged sliding-window cache).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller.  The
+ *     library keeps no pointer after it returns, but the work it enqueues
+ *     reads and writes them asynchronously: they must stay valid until the
+ *     stream reaches that work.
+ *   - bf16 tensors are passed as void* (IEEE bfloat16 bit patterns).  Index
+ *     arrays are int32 (query_start_loc, cache_indices, block_table), int64
+ *     (positions, slot_mapping) or bytes (has_initial_state, 0 = false).
+ *   - Strides are in ELEMENTS and must be non-negative.
+ *   - The library allocates nothing, never reads device memory on the host
+ *     and never synchronises: each call validates its host arguments, then
+ *     enqueues exactly one kernel on `stream` (NULL = the default stream) and
+ *     returns.  Calls are therefore safe to capture in a HIP graph.
+ *   - Return value: SCONV_OK, or a negative sconv_status.  On any error
+ *     nothing is enqueued.  An empty problem (zero tokens, zero sequences)
+ *     returns SCONV_OK without enqueueing anything.
+ *   - Device data is not validated on the host (it is never read there).
+ *     Kernels guard every data-dependent index: a cache line outside
+ *     [0, num_cache_lines) skips its sequence, a block id outside
+ *     [0, num_blocks) reads as zero / drops the insert, and token offsets
+ *     are clamped into the tensor.  Results for such inputs are defined by
+ *     these rules only; the memory accessed always stays inside the tensors.
+ *   - Calls that write the same cache lines / blocks must be ordered by the
+ *     caller (same stream, or events); concurrent writers race.
+ */
+#ifndef SCONV_H
+#define SCONV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sconv_status {
+    SCONV_OK = 0,
+    SCONV_ERR_NULL = -1,    /* a required pointer is NULL                       */
+    SCONV_ERR_SHAPE = -2,   /* a size is negative, inconsistent or too large    */
+    SCONV_ERR_STRIDE = -3,  /* a layout the kernels do not take                 */
+    SCONV_ERR_WIDTH = -4,   /* width outside [SCONV_MIN_WIDTH, SCONV_MAX_WIDTH] */
+    SCONV_ERR_ALIAS = -5,   /* an output overlaps an input it must not overlap  */
+    SCONV_ERR_ALIGN = -6,   /* a pointer / stride breaks a vector alignment     */
+    SCONV_ERR_ARG = -7,     /* an enumerated argument (activation, ...) is bad  */
+    SCONV_ERR_LAUNCH = -8   /* the HIP runtime refused the launch               */
+} sconv_status;
+
+#define SCONV_MIN_WIDTH 2
+#define SCONV_MAX_WIDTH 5
+#define SCONV_ACT_NONE 0
+#define SCONV_ACT_SILU 1
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *sconv_status_string(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+int sconv_version(void);
+
+/*
+ * conv1d_fwd_varlen -- prefill over a packed batch of variable-length
+ * sequences, each continued from (and writing back) its conv state.
+ * Follows tokenspeed causal_conv1d.py, causal_conv1d_fn /
+ * _causal_conv1d_fwd_kernel, with the arithmetic of the atrex-bench #003
+ * reference forward.
+ *
+ * x            logical [dim][total_tokens] bf16; element (c, t) at
+ *              x[c*x_stride_dim + t*x_stride_tok].  Two storages are taken:
+ *                token-contiguous: x_stride_tok == 1 and
+ *                  x_stride_dim == total_tokens (a compact (dim, T) array,
+ *                  the benchmark page's layout; dim*total_tokens < 2^32);
+ *                channel-contiguous: x_stride_dim == 1, x_stride_tok >= dim
+ *                  and a multiple of 8 (the (T, dim) layout the tokenspeed
+ *                  launcher requires).  With total_tokens == 1 the token
+ *                  stride is ignored.
+ *              x and out must be 16-byte aligned.
+ * weight       logical [dim][width] bf16, element (c, j) at
+ *              weight[c*w_stride_dim + j] (unit width stride, as the page
+ *              asserts).  w_stride_dim >= width.
+ * bias         [dim] bf16, or NULL for no bias.
+ * conv_states  logical [num_cache_lines][dim][width-1] bf16, element
+ *              (l, c, k) at conv_states[l*cs_stride_line + c*cs_stride_dim
+ *              + k*cs_stride_tok]; column 0 is the oldest input.  Read as the
+ *              history of sequences with has_initial_state set, and
+ *              overwritten in place with the last width-1 inputs of every
+ *              processed sequence of non-zero length.  NULL: zero history,
+ *              no state written.
+ * cache_indices  [batch] int32: the cache line of each sequence; an entry
+ *              equal to pad_slot_id marks a padded sequence, which is skipped
+ *              entirely (no output, no state).  NULL: sequence s uses line s.
+ * has_initial_state  [batch] bytes, non-zero = continue from the cached
+ *              state; NULL = all false.  Requires conv_states.
+ * query_start_loc  [batch+1] int32 token offsets: 0, then the running sum of
+ *              the lengths; the last entry must equal total_tokens.
+ * activation   SCONV_ACT_NONE or SCONV_ACT_SILU ("silu" / "swish").
+ * out          logical [dim][total_tokens] bf16 in the same storage class as
+ *              x (strides o_stride_dim / o_stride_tok, same rules).  It must
+ *              not overlap x or conv_states.  Rows of skipped sequences are
+ *              left untouched.
+ * Errors: NULL x/weight/query_start_loc/out (when there is work), or
+ *   has_initial_state without conv_states -> SCONV_ERR_NULL; bad sizes,
+ *   conv_states narrower than the lines cache_indices may not check ->
+ *   SCONV_ERR_SHAPE; unsupported strides -> SCONV_ERR_STRIDE; alignment ->
+ *   SCONV_ERR_ALIGN; overlap -> SCONV_ERR_ALIAS.
+ */
+int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
+                      const void *weight, int64_t w_stride_dim,
+                      const void *bias,
+                      void *conv_states, int64_t cs_stride_line,
+                      int64_t cs_stride_dim, int64_t cs_stride_tok,
+                      int64_t num_cache_lines,
+                      const int32_t *cache_indices,
+                      const uint8_t *has_initial_state,
+                      const int32_t *query_start_loc,
+                      int32_t batch, int64_t total_tokens, int32_t dim,
+                      int32_t width, int32_t activation, int32_t pad_slot_id,
+                      void *out, int64_t o_stride_dim, int64_t o_stride_tok,
+                      hipStream_t stream);
+
+/*
+ * conv1d_update_decode -- decode-time update: each of `batch` entries feeds
+ * `seqlen` new tokens (seqlen == 1 for plain decode) continuing from its
+ * cached state, which is then shifted to hold the last width-1 inputs.
+ * Follows tokenspeed causal_conv1d.py, causal_conv1d_update /
+ * _causal_conv1d_update_kernel (without speculative decoding).
+ *
+ * x            logical [batch][dim][seqlen] bf16 at
+ *              x[b*x_stride_seq + c*x_stride_dim + t*x_stride_tok].
+ * weight, bias as for conv1d_fwd_varlen.
+ * conv_state   logical [num_cache_lines][dim][width-1] bf16 (any strides),
+ *              always read as the history and updated in place.
+ * cache_indices  [batch] int32 or NULL (entry b uses line b, and then
+ *              num_cache_lines must be >= batch); pad_slot_id skips an entry.
+ * out          logical [batch][dim][seqlen] bf16.  It may be exactly x
+ *              (same pointer and strides: the page computes in place);
+ *              any other overlap with x, and any overlap with conv_state, is
+ *              SCONV_ERR_ALIAS.
+ */
+int conv1d_update_decode(const void *x, int64_t x_stride_seq, int64_t x_stride_dim,
+                         int64_t x_stride_tok,
+                         const void *weight, int64_t w_stride_dim,
+                         const void *bias,
+                         void *conv_state, int64_t cs_stride_line,
+                         int64_t cs_stride_dim, int64_t cs_stride_tok,
+                         int64_t num_cache_lines,
+                         const int32_t *cache_indices,
+                         int32_t batch, int32_t dim, int32_t seqlen,
+                         int32_t width, int32_t activation, int32_t pad_slot_id,
+                         void *out, int64_t o_stride_seq, int64_t o_stride_dim,
+                         int64_t o_stride_tok,
+                         hipStream_t stream);
+
+/*
+ * sconv_paged_fused -- one launch that inserts every token's input into a
+ * paged sliding-window cache and convolves the width taps ending at its
+ * absolute position.  Follows Inkling sconv.py, fused_sconv /
+ * _fused_sconv_kernel; the token -> request lookup of its
+ * _seq_metadata_kernel is done inside the kernel from query_start_loc.
+ *
+ * x            [num_tokens][C] bf16, C = num_heads * ws, channel stride 1,
+ *              row stride x_stride_tok (multiple of 8, >= C); head-major
+ *              channels: channel c is head c / ws, cache D-index
+ *              off_s + c % ws.
+ * weight       [C][width] bf16 (unit width stride), bias [C] or NULL (the
+ *              page has none).
+ * cache        [num_blocks][num_heads][block_size][head_dim] bf16 with unit
+ *              D stride; strides c_stride_blk / c_stride_head /
+ *              c_stride_slot (multiples of 8).  It holds the conv input of
+ *              every absolute position: position p of request r lives in
+ *              block block_table[r*bt_stride_req + p / block_size], slot
+ *              p % block_size, D range [off_s, off_s + ws).
+ *              Requires ws % 8 == 0, off_s % 8 == 0, off_s + ws <= head_dim.
+ * positions    [num_tokens] int64 absolute position of each row.
+ * slot_mapping [num_tokens] int64 flat slot block*block_size + offset of
+ *              each row; < 0 marks a pad row.
+ * query_start_loc [num_reqs+1] int32 row offsets of the requests; rows at or
+ *              past query_start_loc[num_reqs] are pad rows.
+ * block_table  [num_reqs][>= max_blocks] int32.
+ * For a non-pad row t of request r (first row qs) at position p, tap j
+ * (0..width-1) covers position p-(width-1)+j: zero before position 0, the
+ * input row t-(width-1)+j when that row is >= qs (inside this forward),
+ * else the cached value.  y = bias + sum of taps; silu if asked; + x[t] if
+ * use_residual; one bf16 rounding.  Pad rows are neither convolved nor
+ * inserted: out = x (use_residual) or 0.  The cache is read as it was
+ * before the call (rows inside the forward are never read back from it),
+ * which requires the blocks written by one request not to be read as
+ * pre-forward taps by another.
+ * out          [num_tokens][C] bf16 with row stride o_stride_tok; must not
+ *              overlap x or the cache.
+ */
+int sconv_paged_fused(const void *x, int64_t x_stride_tok,
+                      const void *weight, int64_t w_stride_dim,
+                      const void *bias,
+                      void *cache, int64_t c_stride_blk, int64_t c_stride_head,
+                      int64_t c_stride_slot,
+                      int64_t num_blocks, int32_t num_heads, int32_t block_size,
+                      int32_t head_dim, int32_t off_s, int32_t ws,
+                      const int64_t *positions, const int64_t *slot_mapping,
+                      const int32_t *query_start_loc, int32_t num_reqs,
+                      const int32_t *block_table, int64_t bt_stride_req,
+                      int32_t max_blocks,
+                      int64_t num_tokens, int32_t width, int32_t activation,
+                      int32_t use_residual,
+                      void *out, int64_t o_stride_tok,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCONV_H */

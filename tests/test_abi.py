@@ -1,0 +1,193 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/sconv.h declares, and rejects bad host arguments with the documented
+status codes before touching the GPU (so nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import causal_depthwise_short_conv1d_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sconv.h")
+
+OK, ENULL, ESHAPE, ESTRIDE, EWIDTH, EALIAS, EALIGN, EARG = 0, -1, -2, -3, -4, -5, -6, -7
+
+# fake, well-aligned, non-overlapping "device" addresses: validation only
+# compares them, it never dereferences them.
+BASE = 0x7F0000000000
+GB = 1 << 30
+
+
+def addr(i):
+    return ctypes.c_void_p(BASE + i * GB)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(S.library_path()):
+        pytest.fail("libsconv.so is not built (run python -m causal_depthwise_short_conv1d_amd.build)")
+    return S.load_library()
+
+
+def test_header_declares_the_three_entry_points():
+    fns = declared_functions()
+    for name in ("conv1d_fwd_varlen", "conv1d_update_decode", "sconv_paged_fused",
+                 "sconv_status_string", "sconv_version"):
+        assert name in fns
+    assert sorted(S.exported_symbols()) == fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", S.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_strings(lib):
+    assert S.version() == (1, 0)
+    for code in range(-8, 1):
+        assert S.status_string(code) != "unknown status"
+    assert S.status_string(-99) == "unknown status"
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(FileNotFoundError):
+        S.load_library(str(tmp_path / "nope.so"))
+
+
+# ------------------------------------------------------------------ fwd --
+
+def fwd(lib, **kw):
+    a = dict(x=addr(1), xsd=1, xst=64, w=addr(2), wsd=4, b=addr(3), cs=addr(4), csl=192,
+             csd=3, cst=1, lines=4, ci=addr(5), hi=addr(6), qsl=addr(7), batch=2, T=10,
+             dim=64, width=4, act=1, pad=-1, out=addr(8), osd=1, ost=64)
+    a.update(kw)
+    return lib.conv1d_fwd_varlen(a["x"], a["xsd"], a["xst"], a["w"], a["wsd"], a["b"], a["cs"],
+                                 a["csl"], a["csd"], a["cst"], a["lines"], a["ci"], a["hi"],
+                                 a["qsl"], a["batch"], a["T"], a["dim"], a["width"], a["act"],
+                                 a["pad"], a["out"], a["osd"], a["ost"], None)
+
+
+@pytest.mark.parametrize("width", [0, 1, 6, 9])
+def test_fwd_width(lib, width):
+    assert fwd(lib, width=width) == EWIDTH
+
+
+def test_fwd_bad_enums_and_sizes(lib):
+    assert fwd(lib, act=2) == EARG
+    assert fwd(lib, batch=-1) == ESHAPE
+    assert fwd(lib, T=-3) == ESHAPE
+    assert fwd(lib, T=1 << 31) == ESHAPE
+    assert fwd(lib, dim=-1) == ESHAPE
+
+
+def test_fwd_empty_is_a_noop(lib):
+    # returns before any pointer is looked at or any kernel launched
+    assert fwd(lib, T=0, x=None, out=None) == OK
+    assert fwd(lib, batch=0, x=None) == OK
+    assert fwd(lib, dim=0, x=None) == OK
+
+
+def test_fwd_nulls(lib):
+    for k in ("x", "w", "qsl", "out"):
+        assert fwd(lib, **{k: None}) == ENULL, k
+    assert fwd(lib, cs=None) == ENULL          # has_initial_state needs conv_states
+
+
+def test_fwd_strides_and_layouts(lib):
+    assert fwd(lib, wsd=3) == ESTRIDE          # weight rows narrower than width
+    assert fwd(lib, xst=2, xsd=2) == ESTRIDE   # neither storage class
+    assert fwd(lib, xst=60) == ESTRIDE         # channel-contiguous rows shorter than dim
+    assert fwd(lib, xst=68) == ESTRIDE         # row pitch not a multiple of 8
+    assert fwd(lib, osd=10, ost=1) == ESTRIDE  # out in the other storage class
+    assert fwd(lib, xsd=-1) == ESTRIDE
+
+
+def test_fwd_state_shape(lib):
+    assert fwd(lib, ci=None, lines=1) == ESHAPE   # line = sequence id needs >= batch lines
+    assert fwd(lib, lines=0) == ESHAPE
+
+
+def test_fwd_alignment(lib):
+    assert fwd(lib, x=ctypes.c_void_p(BASE + GB + 8)) == EALIGN
+    assert fwd(lib, out=ctypes.c_void_p(BASE + 8 * GB + 2)) == EALIGN
+    assert fwd(lib, w=ctypes.c_void_p(BASE + 2 * GB + 1)) == EALIGN
+
+
+def test_fwd_aliasing(lib):
+    assert fwd(lib, out=addr(1)) == EALIAS                               # out is x
+    assert fwd(lib, out=ctypes.c_void_p(BASE + GB + 512)) == EALIAS      # partial overlap
+    assert fwd(lib, cs=ctypes.c_void_p(BASE + 8 * GB + 16)) == EALIAS   # state inside out
+    assert fwd(lib, cs=ctypes.c_void_p(BASE + GB)) == EALIAS             # state inside x
+
+
+# --------------------------------------------------------------- decode --
+
+def upd(lib, **kw):
+    a = dict(x=addr(1), xsb=64, xsd=1, xst=64, w=addr(2), wsd=4, b=addr(3), cs=addr(4),
+             csl=192, csd=3, cst=1, lines=4, ci=addr(5), batch=2, dim=64, seqlen=1,
+             width=4, act=1, pad=-1, out=addr(8), osb=64, osd=1, ost=64)
+    a.update(kw)
+    return lib.conv1d_update_decode(a["x"], a["xsb"], a["xsd"], a["xst"], a["w"], a["wsd"],
+                                    a["b"], a["cs"], a["csl"], a["csd"], a["cst"], a["lines"],
+                                    a["ci"], a["batch"], a["dim"], a["seqlen"], a["width"],
+                                    a["act"], a["pad"], a["out"], a["osb"], a["osd"], a["ost"],
+                                    None)
+
+
+def test_decode_validation(lib):
+    assert upd(lib, width=1) == EWIDTH
+    assert upd(lib, act=-1) == EARG
+    assert upd(lib, seqlen=0, x=None) == OK
+    assert upd(lib, batch=0, x=None) == OK
+    assert upd(lib, cs=None) == ENULL
+    assert upd(lib, ci=None, lines=1) == ESHAPE
+    assert upd(lib, wsd=2) == ESTRIDE
+    assert upd(lib, out=ctypes.c_void_p(BASE + GB + 2)) == EALIAS        # partial overlap
+    assert upd(lib, out=addr(1), osd=2) == EALIAS                        # same base, other strides
+    assert upd(lib, cs=ctypes.c_void_p(BASE + GB + 4)) == EALIAS
+    assert upd(lib, x=ctypes.c_void_p(BASE + GB + 1)) == EALIGN
+
+
+# ---------------------------------------------------------------- paged --
+
+def paged(lib, **kw):
+    a = dict(x=addr(1), xst=4096, w=addr(2), wsd=4, b=None, c=addr(3), csb=32 * 16 * 512,
+             csh=16 * 512, csn=512, nb=64, H=32, N=16, D=512, off=128, ws=128, pos=addr(4),
+             slot=addr(5), qsl=addr(6), R=3, bt=addr(7), btsr=64, mb=64, T=100, width=4,
+             act=1, res=1, out=addr(8), ost=4096)
+    a.update(kw)
+    return lib.sconv_paged_fused(a["x"], a["xst"], a["w"], a["wsd"], a["b"], a["c"], a["csb"],
+                                 a["csh"], a["csn"], a["nb"], a["H"], a["N"], a["D"], a["off"],
+                                 a["ws"], a["pos"], a["slot"], a["qsl"], a["R"], a["bt"],
+                                 a["btsr"], a["mb"], a["T"], a["width"], a["act"], a["res"],
+                                 a["out"], a["ost"], None)
+
+
+def test_paged_validation(lib):
+    assert paged(lib, width=6) == EWIDTH
+    assert paged(lib, res=2) == EARG
+    assert paged(lib, T=0, x=None) == OK
+    assert paged(lib, off=400) == ESHAPE          # stream past head_dim
+    assert paged(lib, H=0) == ESHAPE
+    assert paged(lib, bt=None) == ENULL
+    assert paged(lib, slot=None) == ENULL
+    assert paged(lib, xst=4000) == ESTRIDE        # row shorter than C
+    assert paged(lib, ws=100, xst=3200, ost=3200) == EALIGN   # ws not a multiple of 8
+    assert paged(lib, off=4) == EALIGN
+    assert paged(lib, csn=500) == EALIGN
+    assert paged(lib, x=ctypes.c_void_p(BASE + GB + 8)) == EALIGN
+    assert paged(lib, out=addr(1)) == EALIAS
+    assert paged(lib, out=ctypes.c_void_p(BASE + 3 * GB + 1024)) == EALIAS   # out inside cache

@@ -1,0 +1,261 @@
+"""GPU parity for conv1d_fwd_varlen (through the C ABI) against the oracle.
+
+Sizes: every named workload at full size (the long prefill and the varlen
+batch compare a channel sample against the oracle and check the state of
+every channel), plus many small seeded cases that span several tiles, the
+ragged tail and every edge case: widths 2..5, both storages, pads, zero and
+short sequences, missing optional tensors, strided states.
+"""
+import pytest
+import torch
+
+import causal_depthwise_short_conv1d_amd as S
+import oracle
+import workloads as W
+from tests.parity import assert_bits, assert_close, sample_channels, say
+
+pytestmark = pytest.mark.gpu
+BF = torch.bfloat16
+DEV = "cuda"
+
+
+def to_dev(d):
+    r = {}
+    for k, v in d.items():
+        if isinstance(v, torch.Tensor):
+            t = v.to(DEV)
+            assert t.stride() == v.stride() or v.numel() <= 1
+            r[k] = t
+        else:
+            r[k] = v
+    return r
+
+
+def run_gpu(d, activation="silu", pad_slot_id=-1, out_fill=None):
+    out = torch.empty_like(d["x"])
+    if out_fill is not None:
+        out.fill_(out_fill)
+    cs = d["conv_states"].clone() if d.get("conv_states") is not None else None
+    S.conv1d_fwd_varlen(d["x"], d["weight"], d.get("bias"), cs, d["query_start_loc"],
+                        cache_indices=d.get("cache_indices"),
+                        has_initial_state=d.get("has_initial_state"),
+                        activation=activation, pad_slot_id=pad_slot_id, out=out)
+    torch.cuda.synchronize()
+    return out, cs
+
+
+def run_oracle(d, activation="silu", pad_slot_id=-1, out_fill=None, channels=None):
+    """Oracle on CPU copies; with `channels`, only those channels (all tokens)."""
+    def cpu(t):
+        return None if t is None else t.cpu()
+    x, w, b, cs = cpu(d["x"]), cpu(d["weight"]), cpu(d.get("bias")), cpu(d.get("conv_states"))
+    if channels is not None:
+        x, w = x[channels], w[channels]
+        b = b[channels] if b is not None else None
+        cs = cs[:, channels] if cs is not None else None
+    cs = cs.clone() if cs is not None else None
+    out = torch.full(x.shape, 0.0 if out_fill is None else out_fill, dtype=BF)
+    oracle.fwd_varlen(x, w, b, cs, cpu(d["query_start_loc"]), out,
+                      cache_indices=cpu(d.get("cache_indices")),
+                      has_initial_state=cpu(d.get("has_initial_state")),
+                      activation=activation, pad_slot_id=pad_slot_id)
+    return out, cs
+
+
+def check_full(d, activation="silu", pad_slot_id=-1, exact=False, label=""):
+    say(f"[fwd] {label} x{tuple(d['x'].shape)} strides={d['x'].stride()} W={d['weight'].shape[1]}")
+    g_out, g_cs = run_gpu(d, activation, pad_slot_id, out_fill=-7.0)
+    r_out, r_cs = run_oracle(d, activation, pad_slot_id, out_fill=-7.0)
+    if exact:
+        assert_bits(g_out, r_out, f"{label} out")
+    else:
+        assert_close(g_out, r_out, f"{label} out")
+    if g_cs is not None:
+        assert_bits(g_cs, r_cs, f"{label} state")
+
+
+# ------------------------------------------------------- named workloads --
+
+def test_smallest_single_sequence():
+    d = to_dev(W.single_sequence(**W.SINGLE_SEQ_SMALL, seed=W.seed_for(1)))
+    check_full(d, label="dim256 T16")
+
+
+@pytest.mark.parametrize("T", W.PREFILL_SWEEP_DIM4096["Ts"])
+@pytest.mark.parametrize("layout", ["dim_tok", "tok_dim"])
+def test_prefill_sweep_dim4096(T, layout):
+    d = to_dev(W.single_sequence(dim=4096, T=T, width=4, seed=W.seed_for(2, T % 97),
+                                 layout=layout))
+    check_full(d, label=f"dim4096 T{T} {layout}")
+
+
+@pytest.mark.parametrize("T", W.LONG_PREFILL_DIM8192["Ts"])
+def test_long_prefill_dim8192(T):
+    """The benchmark launch: token-contiguous (dim, T), dim 8192, width 4."""
+    d = W.single_sequence(dim=8192, T=T, width=4, seed=W.seed_for(3, T % 97), device=DEV)
+    say(f"[fwd] dim8192 T{T} full-size launch")
+    g_out, g_cs = run_gpu(d)
+    ch = sample_channels(8192, 64, seed=T)
+    r_out, r_cs = run_oracle(d, channels=ch)
+    assert_close(g_out[ch.to(DEV)], r_out, f"T{T} sampled out")
+    assert_bits(g_cs[:, ch.to(DEV)], r_cs, f"T{T} sampled state")
+    # every channel: the new state is the last width-1 inputs
+    assert_bits(g_cs[0], d["x"][:, T - 3:], f"T{T} state (all channels)")
+
+
+def test_long_prefill_channel_contiguous():
+    T = 4195
+    d = W.single_sequence(dim=8192, T=T, width=4, seed=W.seed_for(3, 50), device=DEV,
+                          layout="tok_dim")
+    g_out, g_cs = run_gpu(d)
+    ch = sample_channels(8192, 64, seed=5)
+    r_out, r_cs = run_oracle(d, channels=ch)
+    assert_close(g_out[ch.to(DEV)], r_out, "T4195 (T,dim) sampled out")
+    assert_bits(g_cs[0], d["x"][:, T - 3:], "T4195 (T,dim) state")
+
+
+def varlen_state_property(d, g_cs, width):
+    """New state of every channel of every processed line: the last width-1
+    entries of (history ++ sequence); untouched lines unchanged."""
+    before = d["conv_states"]
+    qsl = d["query_start_loc"].tolist()
+    lines = d["cache_indices"].tolist()
+    init = d["has_initial_state"].tolist()
+    want = before.clone()
+    for s in range(len(lines)):
+        L = qsl[s + 1] - qsl[s]
+        if lines[s] == -1 or L == 0:
+            continue
+        h = before[lines[s]] if init[s] else torch.zeros_like(before[lines[s]])
+        u = torch.cat([h, d["x"][:, qsl[s]:qsl[s + 1]]], dim=1)
+        want[lines[s]] = u[:, L:L + width - 1]
+    assert_bits(g_cs, want, "varlen state (all channels)")
+
+
+@pytest.mark.parametrize("width", W.VARLEN_BATCH["widths"])
+@pytest.mark.parametrize("layout", ["tok_dim", "dim_tok"])
+def test_varlen_batch(width, layout):
+    if layout == "dim_tok" and width != 4:
+        pytest.skip("token-contiguous varlen run at width 4 only")
+    d = W.varlen_batch(dim=8192, width=width, seed=W.seed_for(4, width), layout=layout,
+                       device=DEV)
+    total = int(d["query_start_loc"][-1])
+    say(f"[fwd] varlen 64 seqs total_T={total} W={width} {layout}")
+    g_out, g_cs = run_gpu(d, out_fill=-7.0)
+    ch = sample_channels(8192, 40, seed=width)
+    r_out, r_cs = run_oracle(d, out_fill=-7.0, channels=ch)
+    assert_close(g_out[ch.to(DEV)], r_out, f"varlen W{width} sampled out")
+    assert_bits(g_cs[:, ch.to(DEV)], r_cs, f"varlen W{width} sampled state")
+    varlen_state_property(d, g_cs, width)
+    # pad sequences' rows untouched in every channel
+    qsl = d["query_start_loc"].tolist()
+    for s, line in enumerate(d["cache_indices"].tolist()):
+        if line == -1:
+            assert torch.all(g_out[:, qsl[s]:qsl[s + 1]] == -7.0)
+
+
+# ------------------------------------------------------------ small cases --
+
+SMALL_CASES = []
+_rng = torch.Generator().manual_seed(2024)
+for i in range(40):
+    width = 2 + i % 4
+    dim = [1, 3, 8, 13, 64, 520, 1030, 24][i % 8]
+    nseq = 1 + int(torch.randint(0, 9, (1,), generator=_rng))
+    lens = torch.randint(0, 70, (nseq,), generator=_rng).tolist()
+    if i % 5 == 0:
+        lens = [int(l) % 4 for l in lens]          # many sequences shorter than the window
+    if sum(lens) == 0:
+        lens[0] = 5
+    SMALL_CASES.append(dict(i=i, width=width, dim=dim, lens=lens,
+                            layout="dim_tok" if i % 2 else "tok_dim"))
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: f"c{c['i']}-W{c['width']}-d{c['dim']}-{c['layout']}")
+def test_small_varlen_cases(case):
+    i = case["i"]
+    d = W.varlen_batch(lengths=case["lens"], dim=case["dim"], width=case["width"],
+                       seed=300 + i, num_lines=len(case["lens"]) + 3,
+                       n_pad=1 if len(case["lens"]) > 2 else 0, layout=case["layout"],
+                       with_bias=(i % 3 != 0))
+    if i % 7 == 3:
+        d["has_initial_state"] = None
+    if i % 11 == 4:
+        d["cache_indices"] = None
+        d["conv_states"] = d["conv_states"][:len(case["lens"])].contiguous()
+    act = None if i % 4 == 1 else "silu"
+    x = d.pop("x")
+    g = to_dev(d)
+    if case["layout"] == "tok_dim":
+        # channel-contiguous rows must be 16-byte aligned: pad the row pitch
+        pitch = (case["dim"] + 7) // 8 * 8
+        buf = torch.zeros(x.shape[1], pitch, dtype=BF, device=DEV)
+        buf[:, :case["dim"]] = x.t().to(DEV)
+        g["x"] = buf[:, :case["dim"]].t()
+    else:
+        g["x"] = x.contiguous().to(DEV)
+    check_full(g, activation=act, label=f"small{i}")
+
+
+@pytest.mark.parametrize("width", [2, 3, 4, 5])
+@pytest.mark.parametrize("layout", ["dim_tok", "tok_dim"])
+def test_exact_values_bit_exact(width, layout):
+    """Exact-valued inputs (k/8): every sum is exact in fp32 and bf16, so the
+    GPU must reproduce the oracle bit for bit -- this pins tap placement."""
+    d = W.varlen_batch(lengths=[1, 2, 700, 3, 0, 1501, 5, 260], dim=520, width=width,
+                       seed=400 + width, num_lines=12, n_pad=1, layout=layout,
+                       values="exact")
+    check_full(to_dev(d), activation=None, exact=True, label=f"exact W{width} {layout}")
+
+
+@pytest.mark.parametrize("layout", ["dim_tok", "tok_dim"])
+def test_no_state_no_bias(layout):
+    d = W.varlen_batch(lengths=[33, 1, 64, 9], dim=40, width=4, seed=501, num_lines=8,
+                       n_pad=0, layout=layout, with_bias=False)
+    d["conv_states"] = None
+    d["has_initial_state"] = None
+    d["cache_indices"] = None
+    check_full(to_dev(d), label=f"nostate {layout}")
+
+
+def test_dim_contiguous_state_storage():
+    # the cache stored (lines, width-1, dim) and viewed as (lines, dim, width-1)
+    d = W.varlen_batch(lengths=[20, 3, 41], dim=96, width=4, seed=601, num_lines=6,
+                       n_pad=0, layout="tok_dim")
+    d["conv_states"] = d["conv_states"].transpose(1, 2).contiguous().transpose(1, 2)
+    assert d["conv_states"].stride(1) == 1
+    check_full(to_dev(d), label="dim-contiguous state")
+
+
+def test_custom_pad_id():
+    d = W.varlen_batch(lengths=[10, 10, 10], dim=16, width=3, seed=701, num_lines=5,
+                       n_pad=0, layout="dim_tok")
+    d["cache_indices"] = torch.tensor([2, 77, 0], dtype=torch.int32)
+    check_full(to_dev(d), pad_slot_id=77, label="pad id 77")
+
+
+@pytest.mark.parametrize("layout", ["dim_tok", "tok_dim"])
+def test_split_sequence_bit_identical(layout):
+    T, dim = 3000, 1024
+    d = to_dev(W.single_sequence(dim=dim, T=T, width=4, seed=801, layout=layout))
+    full, st_full = run_gpu(d)
+    for k in (1, 2, 3, 1000, 2999):
+        cs = d["conv_states"].clone()
+        parts = []
+        for lo, hi in ((0, k), (k, T)):
+            xs = W.to_layout(d["x"][:, lo:hi], layout)
+            o = S.conv1d_fwd_varlen(xs, d["weight"], d["bias"], cs,
+                                    torch.tensor([0, hi - lo], dtype=torch.int32, device=DEV),
+                                    has_initial_state=torch.ones(1, dtype=torch.bool, device=DEV))
+            parts.append(o)
+        torch.cuda.synchronize()
+        assert_bits(torch.cat(parts, dim=1), full, f"split at {k}")
+        assert_bits(cs, st_full, f"split state at {k}")
+
+
+def test_repeat_is_deterministic():
+    d = W.varlen_batch(dim=2048, nseq=16, max_len=600, width=4, seed=901, device=DEV)
+    a, sa = run_gpu(d)
+    b, sb = run_gpu(d)
+    assert_bits(a, b, "repeat out")
+    assert_bits(sa, sb, "repeat state")

@@ -1,0 +1,93 @@
+"""GPU parity for sconv_paged_fused (through the C ABI) against the oracle."""
+import pytest
+import torch
+
+import causal_depthwise_short_conv1d_amd as S
+import oracle
+import workloads as W
+from tests.parity import assert_bits, assert_close, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+BF = torch.bfloat16
+SMALL = dict(H=4, ws=16, N=4, D=48, off_s=16, num_blocks=96, n_decode=5,
+             n_prefill=3, chunk=37, max_pos=60)
+
+
+def run_both(d, activation="silu", residual=True, exact=False, cache_dev=None, label=""):
+    """d: CPU tensors except (optionally) the cache, given on the GPU."""
+    say(f"[paged] {label} T={d['x'].shape[0]} C={d['x'].shape[1]}")
+    cache_gpu = cache_dev if cache_dev is not None else d["cache"].to(DEV)
+    cache_ref = cache_gpu.cpu()
+    out_ref = torch.full(d["x"].shape, float("nan"), dtype=BF)
+    oracle.paged(d["x"], d["weight"], d["bias"], cache_ref, d["positions"], d["slot_mapping"],
+                 d["query_start_loc"], d["block_table"], d["off_s"], d["ws"], out_ref,
+                 activation=activation, use_residual=residual)
+    dv = lambda t: None if t is None else t.to(DEV)
+    out = S.sconv_paged_fused(dv(d["x"]), dv(d["weight"]), cache_gpu, dv(d["positions"]),
+                              dv(d["slot_mapping"]), dv(d["query_start_loc"]),
+                              dv(d["block_table"]), d["off_s"], d["ws"],
+                              activation=activation, use_residual=residual, bias=dv(d["bias"]))
+    torch.cuda.synchronize()
+    if exact:
+        assert_bits(out, out_ref, f"{label} out")
+    else:
+        assert_close(out, out_ref, f"{label} out")
+    assert_bits(cache_gpu, cache_ref, f"{label} cache")
+    return out, cache_gpu
+
+
+def test_paged_mixed_batch_full_size():
+    """32 decode tokens + 8 prefill chunks of 512, H 32, ws 128, cache
+    [4096, 32, 16, 512], 5% pad rows, residual + SiLU."""
+    cfg = W.PAGED_MIXED
+    # the 2 GiB cache (and x, weight) are drawn on the GPU
+    d2 = W.paged_batch(H=cfg["H"], ws=cfg["ws"], N=cfg["N"], D=cfg["D"], off_s=cfg["off_s"],
+                       num_blocks=cfg["num_blocks"], width=cfg["width"],
+                       n_decode=cfg["n_decode"], n_prefill=cfg["n_prefill"], chunk=cfg["chunk"],
+                       max_pos=cfg["max_pos"], pad_frac=cfg["pad_frac"], seed=W.seed_for(5),
+                       device=DEV)
+    host = {k: (v.cpu() if isinstance(v, torch.Tensor) and k != "cache" else v)
+            for k, v in d2.items()}
+    run_both(host, cache_dev=d2["cache"], label="mixed full size")
+
+
+@pytest.mark.parametrize("width", [2, 3, 4, 5])
+@pytest.mark.parametrize("residual", [True, False])
+def test_paged_small(width, residual):
+    d = W.paged_batch(**SMALL, width=width, pad_frac=0.1, trailing_pad=3,
+                      seed=100 + width, with_bias=(width % 2 == 0), min_pos=0)
+    run_both(d, residual=residual, label=f"small W{width}")
+
+
+@pytest.mark.parametrize("width", [2, 4, 5])
+def test_paged_exact_values(width):
+    d = W.paged_batch(**SMALL, width=width, pad_frac=0.2, trailing_pad=2,
+                      seed=200 + width, values="exact", with_bias=True, min_pos=0)
+    run_both(d, activation=None, residual=True, exact=True, label=f"exact W{width}")
+
+
+def test_paged_idempotent_on_gpu():
+    d = W.paged_batch(**SMALL, width=4, pad_frac=0.1, seed=300)
+    out1, cache1 = run_both(d, label="first")
+    before = cache1.clone()
+    dv = lambda t: t.to(DEV)
+    out2 = S.sconv_paged_fused(dv(d["x"]), dv(d["weight"]), cache1, dv(d["positions"]),
+                               dv(d["slot_mapping"]), dv(d["query_start_loc"]),
+                               dv(d["block_table"]), d["off_s"], d["ws"], activation="silu")
+    torch.cuda.synchronize()
+    assert_bits(out2, out1, "second step out")
+    assert_bits(cache1, before, "second step cache")
+
+
+def test_paged_partial_slab_and_many_heads():
+    # C = 20 heads * 24 = 480 channels: one partial 512-wide slab
+    cfg = dict(H=20, ws=24, N=8, D=64, off_s=32, num_blocks=200, n_decode=7, n_prefill=2,
+               chunk=45, max_pos=200)
+    d = W.paged_batch(**cfg, width=4, pad_frac=0.05, seed=400)
+    run_both(d, label="partial slab")
+
+
+def test_paged_only_decode_tokens():
+    d = W.paged_batch(**dict(SMALL, n_decode=40, n_prefill=0), width=4, pad_frac=0.1, seed=500)
+    run_both(d, label="decode only")
