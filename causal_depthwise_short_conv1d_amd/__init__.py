@@ -18,7 +18,7 @@ import os
 
 import torch
 
-__all__ = ["conv1d_fwd_varlen", "conv1d_update_decode", "sconv_paged_fused",
+__all__ = ["conv1d_fwd_varlen", "conv1d_update_decode", "sconv_paged_fused", "new_output",
            "SconvError", "library_path", "load_library", "exported_symbols",
            "version", "status_string"]
 
@@ -135,6 +135,17 @@ def _call(fn: str, *args) -> None:
         raise SconvError(fn, rc)
 
 
+def new_output(x: torch.Tensor) -> torch.Tensor:
+    """An uninitialised output in x's storage class: a compact (dim, T) array
+    for token-contiguous x, else (T, pitch) storage viewed as (dim, T) with a
+    row pitch rounded up to 8 elements (16-byte aligned rows)."""
+    dim, total = x.shape
+    if total > 1 and x.stride(1) == 1 and (dim == 1 or x.stride(0) == total):
+        return torch.empty((dim, total), dtype=x.dtype, device=x.device)
+    pitch = (dim + 7) // 8 * 8
+    return torch.empty((total, pitch), dtype=x.dtype, device=x.device)[:, :dim].t()
+
+
 def conv1d_fwd_varlen(x, weight, bias, conv_states, query_start_loc,
                       cache_indices=None, has_initial_state=None,
                       activation="silu", pad_slot_id: int = -1, out=None):
@@ -144,7 +155,7 @@ def conv1d_fwd_varlen(x, weight, bias, conv_states, query_start_loc,
     (lines, dim, width-1) or None, updated in place; query_start_loc int32
     (batch+1,); cache_indices int32 (batch,) or None; has_initial_state bool
     (batch,) or None.  Returns out (a new tensor with x's strides unless
-    given)."""
+    given; see new_output)."""
     dev = x.device
     dim, total = x.shape
     width = weight.shape[1]
@@ -152,7 +163,7 @@ def conv1d_fwd_varlen(x, weight, bias, conv_states, query_start_loc,
     if weight.dim() != 2 or weight.shape[0] != dim or weight.stride(1) != 1:
         raise ValueError("weight must be (dim, width) with unit width stride")
     if out is None:
-        out = torch.empty_like(x)
+        out = new_output(x)
     if out.shape != x.shape:
         raise ValueError("out must have x's shape")
     if bias is not None and (bias.shape != (dim,) or bias.stride(0) != 1):
