@@ -141,6 +141,15 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_per_step*1e3:.1f} us/step wall, "
         f"{kern_ms*1e3:.1f} us/launch (events) -> {achieved:.0f} GB/s")
 
+    # Calibration copy of a known byte count (256 MiB read + 256 MiB written),
+    # present in every run so that counter passes can scale HBM counters.
+    src = torch.empty(1 << 27, dtype=torch.bfloat16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
@@ -183,11 +192,13 @@ def main():
 
 
 def extras(torch, S, W, dev):
-    """Secondary measurements, each launch timed alone after a 1 GiB write that
-    evicts the caches (median of the repetitions)."""
+    """Secondary measurements, each launch timed alone after reading 1 GiB,
+    which evicts the caches and leaves no dirty lines to drain during the
+    timed launch (median of the repetitions)."""
     ex = {}
-    scratch = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
-    flush = lambda: scratch.fill_(1)
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    flush = lambda: torch.sum(scratch, dim=0, out=sink)
 
     sweep = {}
     for dim, Ts in ((4096, (1, 128, 256, 514, 1024)), (8192, (4195, 11027, 14807))):

@@ -8,25 +8,157 @@
 // kTokRounds rounds of 64 consecutive chunks, so each load instruction moves
 // 1 KiB of contiguous memory whatever T is (rows start misaligned whenever
 // T % 8 != 0).  The width-1 history of a chunk is the tail of the previous
-// chunk: it comes from the neighbouring lane with a cross-lane rotate, and
+// chunk: it comes from the neighbouring lane with a cross-lane permute, and
 // lane 0 takes lane 63's tail from the previous round (one 8-byte load per
 // wave for round 0).
 //
-// Fast path: the chunk lies inside one row and one sequence, at least
-// width-1 tokens past the sequence start -> all taps are in registers.
-// Slow path (rare: row or sequence boundaries, the first width-1 tokens of a
-// sequence, the ragged tail): element by element.  The element holding a
-// sequence's first token owns that sequence's history: it alone reads the
-// cached state, computes the first width-1 outputs (possibly spilling into
-// the next chunk) and writes the new state, so no other lane can read a
-// state that has already been overwritten.
+// The path is bound by memory only if the ALU work per 16-byte chunk stays
+// small (at 8 TB/s a CU has ~150 lane-instructions per chunk), so the fast
+// path is built to be lean:
+//   * when T >= 2048 a wave's 2048 elements span at most two channel rows:
+//     the channel, the row start and the weights are wave-uniform values and
+//     each lane only picks one of two (no per-lane division, no gathers);
+//   * the taps run on packed bf16 pairs with the gfx950 dot2 instruction
+//     (two products accumulated into fp32 per instruction, exact products),
+//     so x is never unpacked for the taps; an odd last tap uses one fma.
+// Chunks that touch a row or sequence boundary, the first width-1 tokens of
+// a sequence, or the ragged tail (about 0.1% of chunks at the benchmark's
+// sizes) are deferred and redone element by element after the fast rounds.
+// The element holding a sequence's first token owns that sequence's history:
+// it alone reads the cached state, computes the first width-1 outputs
+// (possibly spilling into the next chunk) and writes the new state, so no
+// other lane can read a state that has already been overwritten.
 #include "sconv_device.h"
 
 namespace sconv {
 
 namespace {
 
-// Weights and bias of one channel, widened to fp32.
+constexpr int kChunksPerWave = kWaveSize * kTokRounds;
+constexpr uint32_t kWaveElems = kChunksPerWave * kVec;
+
+// Weights of one channel for the dot2 path: taps as packed bf16 pairs
+// (w[2p], w[2p+1]), the odd last tap and the bias as fp32.
+template <int W>
+struct PairTaps {
+    uint32_t wp[W / 2];
+    float wl;
+    float b;
+};
+
+template <int W>
+__device__ __forceinline__ PairTaps<W> load_pair_taps(const FwdTokParams &p, uint32_t c) {
+    PairTaps<W> r;
+    const uint16_t *w = p.w + int64_t(c) * p.w_sd;
+#pragma unroll
+    for (int q = 0; q < W / 2; ++q) r.wp[q] = uint32_t(w[2 * q]) | (uint32_t(w[2 * q + 1]) << 16);
+    r.wl = (W & 1) ? bf_one(w[W - 1]) : 0.0f;
+    r.b = p.bias ? bf_one(p.bias[c]) : 0.0f;
+    return r;
+}
+
+template <int W>
+__device__ __forceinline__ PairTaps<W> uniform(PairTaps<W> t) {
+#pragma unroll
+    for (int q = 0; q < W / 2; ++q) t.wp[q] = __builtin_amdgcn_readfirstlane(t.wp[q]);
+    t.wl = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(t.wl)));
+    t.b = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(t.b)));
+    return t;
+}
+
+template <int W>
+__device__ __forceinline__ PairTaps<W> select(bool b, const PairTaps<W> &tb, const PairTaps<W> &ta) {
+    PairTaps<W> r;
+#pragma unroll
+    for (int q = 0; q < W / 2; ++q) r.wp[q] = b ? tb.wp[q] : ta.wp[q];
+    r.wl = b ? tb.wl : ta.wl;
+    r.b = b ? tb.b : ta.b;
+    return r;
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// The 12 elements e[0..11] before and in a chunk: e[0..3] are elements 4..7
+// of the previous chunk (dwords hz, hw), e[4..11] the chunk (v).  Pair m is
+// (e[m], e[m+1]); elem m is e[m] widened.
+struct Window {
+    uint32_t d[6];
+    __device__ __forceinline__ uint32_t pair(int m) const {
+        return (m & 1) ? __builtin_amdgcn_alignbit(d[(m + 1) >> 1], d[(m - 1) >> 1], 16)
+                       : d[m >> 1];
+    }
+    __device__ __forceinline__ float elem(int m) const {
+        return (m & 1) ? bf_hi(d[m >> 1]) : bf_lo(d[m >> 1]);
+    }
+};
+
+// 8 outputs of a chunk whose every tap lies in the window.
+template <int W, bool SILU>
+__device__ __forceinline__ u32x4 fast_chunk(const Window &win, const PairTaps<W> &tp) {
+    constexpr int H = W - 1;            // history length
+    constexpr int B = 4 - H;            // e index of u[0]
+    float o[kVec];
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        float acc = tp.b;
+#pragma unroll
+        for (int q = 0; q < W / 2; ++q) acc = dot2(win.pair(B + j + 2 * q), tp.wp[q], acc);
+        if constexpr (W & 1) acc = __builtin_fmaf(tp.wl, win.elem(B + j + W - 1), acc);
+        o[j] = act<SILU>(acc);
+    }
+    return pack8(o);
+}
+
+// Bits of the history entry h[H+l], l in [-H, -1], without dynamic indexing.
+template <int H>
+__device__ __forceinline__ uint32_t hist_bits(const uint32_t (&h)[H], int l) {
+    uint32_t v = h[0];
+#pragma unroll
+    for (int k = 1; k < H; ++k)
+        if (l == k - H) v = h[k];
+    return v;
+}
+
+// A chunk that holds part of the first width-1 tokens of a row whose head is
+// at flat index hp (the chunk may also end the previous row).  It is the fast
+// chunk twice: once on the window as loaded with the previous row's taps
+// (right for elements before hp), once on a copy whose positions in
+// [hp-H, hp) hold the cached history h, with the head row's taps (right for
+// elements from hp on); the two are merged element by element.
+template <int W, bool SILU>
+__device__ __forceinline__ u32x4 head_chunk(const Window &win, uint32_t i0, uint32_t hp,
+                                            const PairTaps<W> &t_prev, const PairTaps<W> &t_head,
+                                            const uint32_t (&h)[W - 1]) {
+    constexpr int H = W - 1;
+    Window wh = win;
+#pragma unroll
+    for (int d = 0; d < 6; ++d) {
+        uint32_t half[2] = {wh.d[d] & 0xffffu, wh.d[d] >> 16};
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int l = int(i0 - 4 + 2 * d + q) - int(hp);   // position relative to the head
+            if (l >= -H && l < 0) half[q] = hist_bits<H>(h, l);
+        }
+        wh.d[d] = half[0] | (half[1] << 16);
+    }
+    const u32x4 a = fast_chunk<W, SILU>(win, t_prev);
+    const u32x4 b = fast_chunk<W, SILU>(wh, t_head);
+    const uint32_t k = hp > i0 ? hp - i0 : 0;              // elements [0, k) end the previous row
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t lo = (2 * d < int(k) ? av[d] : bv[d]) & 0xffffu;
+        const uint32_t hi = (2 * d + 1 < int(k) ? av[d] : bv[d]) & 0xffff0000u;
+        r[d] = lo | hi;
+    }
+    return u32x4{r[0], r[1], r[2], r[3]};
+}
+
+// Scalar weights for the element-by-element path.
 template <int W>
 struct Taps {
     float w[W];
@@ -42,97 +174,246 @@ __device__ __forceinline__ Taps<W> load_taps(const FwdTokParams &p, uint32_t c) 
     return r;
 }
 
-// One element whose taps lie partly in the history h (bits, oldest first):
-// element with local index tl < width-1 reads h for negative offsets.
-template <int W, bool SILU>
-__device__ __forceinline__ uint16_t head_output(const Taps<W> &tp, const uint16_t *h,
-                                                const uint16_t *xseq, int tl) {
-    float acc = tp.b;
-#pragma unroll
-    for (int k = 0; k < W; ++k) {
-        const int idx = tl - (W - 1) + k;
-        const uint16_t v = idx >= 0 ? xseq[idx] : h[(W - 1) + idx];
-        acc = __builtin_fmaf(tp.w[k], bf_one(v), acc);
+// Sequence of token t, reusing the lane's previous answer when it still holds.
+struct SeqCache {
+    int32_t s = -1;
+    SeqInfo si;
+    __device__ __forceinline__ const SeqInfo &get(const SeqBatch &sb, const int32_t *qsl, int64_t t) {
+        if (s < 0 || t < si.start || t >= si.end) {
+            s = sb.batch == 1 ? 0 : seq_search(qsl, sb.batch, t);
+            si = seq_info(sb, qsl, s);
+        }
+        return si;
     }
-    return to_bf16(act<SILU>(acc));
-}
+};
 
-// Element-by-element processing of one chunk.  e[] holds the bits of flat
-// elements i0-(W-1) .. i0+7 (entries before element 0 of the tensor are
-// never used: such elements are the start of row 0 and read history).
+// Element-by-element processing of one chunk (all loads from memory).
 template <int W, bool SILU>
-__device__ void slow_chunk(const FwdTokParams &p, const int32_t *qsl, uint32_t i0,
-                           const uint16_t *e, uint32_t cA, const Taps<W> &tA,
-                           const Taps<W> &tB) {
+__device__ void slow_chunk(const FwdTokParams &p, const int32_t *qsl, uint32_t i0) {
+    constexpr int H = W - 1;
     const uint32_t T = p.T;
     uint32_t c = p.divT.div(i0);
     uint32_t t = i0 - c * T;
-    Taps<W> tp = (c == cA) ? tA : (c == cA + 1 ? tB : load_taps<W>(p, c));
-    int32_t s = -1;
-    SeqInfo si;
-    si.start = 0; si.end = 0; si.line = 0; si.skip = true; si.init = false;
-    for (int j = 0; j < 8; ++j) {
+    Taps<W> tp = load_taps<W>(p, c);
+    SeqCache sc;
+    for (int j = 0; j < kVec; ++j) {
         const uint32_t i = i0 + j;
         if (i >= p.n_elems) break;
         if (j > 0 && ++t == T) {           // crossed into the next channel row
             t = 0;
             ++c;
-            tp = (c == cA) ? tA : (c == cA + 1 ? tB : load_taps<W>(p, c));
+            tp = load_taps<W>(p, c);
         }
-        if (s < 0 || int64_t(t) < si.start || int64_t(t) >= si.end) {
-            s = p.sb.batch == 1 ? 0 : seq_search(qsl, p.sb.batch, t);
-            si = seq_info(p.sb, qsl, s);
-        }
+        const SeqInfo &si = sc.get(p.sb, qsl, t);
         if (si.skip || int64_t(t) < si.start || int64_t(t) >= si.end) continue;
         const int64_t tl = int64_t(t) - si.start;
-        if (tl >= 1 && tl <= W - 2) continue;      // owned by the sequence's first token
+        if (tl >= 1 && tl <= H - 1) continue;      // owned by the sequence's first token
+        const uint16_t *xrow = p.x + size_t(c) * T;
         uint16_t *orow = p.out + size_t(c) * T;
-        if (tl >= W - 1) {                          // every tap inside the row window
+        if (tl >= H) {                              // every tap inside the sequence
             float acc = tp.b;
 #pragma unroll
-            for (int k = 0; k < W; ++k) acc = __builtin_fmaf(tp.w[k], bf_one(e[j + k]), acc);
+            for (int k = 0; k < W; ++k) acc = __builtin_fmaf(tp.w[k], bf_one(xrow[t - H + k]), acc);
             orow[t] = to_bf16(act<SILU>(acc));
             continue;
         }
         // tl == 0: the history owner of (sequence, channel).
-        const uint16_t *xseq = p.x + size_t(c) * T + si.start;
-        uint16_t h[W - 1];
+        const uint16_t *xseq = xrow + si.start;
+        uint16_t h[H];
 #pragma unroll
-        for (int k = 0; k < W - 1; ++k)
-            h[k] = si.init ? p.sb.cs[si.line * p.sb.cs_sl + int64_t(c) * p.sb.cs_sd +
-                                     k * p.sb.cs_st]
+        for (int k = 0; k < H; ++k)
+            h[k] = si.init ? p.sb.cs[si.line * p.sb.cs_sl + int64_t(c) * p.sb.cs_sd + k * p.sb.cs_st]
                            : uint16_t(0);
         const int64_t L = si.end - si.start;
-        const int nq = L < (W - 1) ? int(L) : (W - 1);
-        for (int q = 0; q < nq; ++q) orow[si.start + q] = head_output<W, SILU>(tp, h, xseq, q);
-        if (p.sb.cs) {
-            uint16_t nh[W - 1];
+        const int nq = L < H ? int(L) : H;
 #pragma unroll
-            for (int k = 0; k < W - 1; ++k) {
+        for (int q = 0; q < H; ++q) {
+            if (q >= nq) break;
+            float acc = tp.b;
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int idx = q - H + k;          // compile-time after unrolling
+                const uint16_t v = idx >= 0 ? xseq[idx] : h[H + idx];
+                acc = __builtin_fmaf(tp.w[k], bf_one(v), acc);
+            }
+            orow[si.start + q] = to_bf16(act<SILU>(acc));
+        }
+        if (p.sb.cs) {
+            uint16_t nh[H];
+#pragma unroll
+            for (int k = 0; k < H; ++k) {
                 const int64_t m = L + k;            // index into h ++ x
-                nh[k] = m < (W - 1) ? h[m] : xseq[m - (W - 1)];
+                uint16_t hv = 0;
+#pragma unroll
+                for (int q = 0; q < H; ++q)
+                    if (m == q) hv = h[q];
+                nh[k] = m < H ? hv : xseq[m - H];
             }
 #pragma unroll
-            for (int k = 0; k < W - 1; ++k)
+            for (int k = 0; k < H; ++k)
                 p.sb.cs[si.line * p.sb.cs_sl + int64_t(c) * p.sb.cs_sd + k * p.sb.cs_st] = nh[k];
         }
     }
 }
 
+// One sequence whose rows are at least one wave long (T >= 2048): every
+// wave spans at most two rows and contains at most one row head.  The head's
+// history (state), the row's last width-1 inputs (the new state) and both
+// rows' taps are wave-uniform values loaded with the wave's x; the head
+// chunks are computed in registers and one lane writes the new state after
+// the wave's reads.  Only three rare cases fall back to the element path:
+// the ragged last chunk, and a head whose first width-1 tokens cross into the
+// next wave (its owner computes them element by element and the next wave's
+// first chunk skips them).
 template <int W, bool SILU>
-__global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tokmajor_kernel(FwdTokParams p) {
-    __shared__ int32_t s_qsl[kQslLdsMax];
-    const bool use_lds = p.sb.batch > 1 && p.sb.batch + 1 <= kQslLdsMax;
-    if (use_lds) {
-        for (int i = threadIdx.x; i <= p.sb.batch; i += blockDim.x) s_qsl[i] = p.sb.qsl[i];
-        __syncthreads();
+__global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tok_long_kernel(FwdTokParams p) {
+    constexpr int H = W - 1;
+    constexpr uint32_t kNone = 0xffffffffu;
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wave = threadIdx.x / kWaveSize;
+    const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const uint32_t wbase = (tile * kTokWavesPerBlock + wave) * uint32_t(kChunksPerWave);
+    if (wbase >= p.n_chunks) return;
+    const SeqInfo s0 = seq_info(p.sb, p.sb.qsl, 0);
+    if (s0.skip) return;                                    // padded sequence: nothing to do
+
+    const uint32_t T = p.T;
+    const uint32_t n_full = p.n_elems / kVec;
+    u32x4 v[kTokRounds];
+    if (wbase + kChunksPerWave <= n_full) {
+#pragma unroll
+        for (int r = 0; r < kTokRounds; ++r)
+            v[r] = ld16(p.x + size_t(wbase + r * kWaveSize + lane) * kVec);
+    } else {
+#pragma unroll
+        for (int r = 0; r < kTokRounds; ++r) {
+            const uint32_t ch = wbase + r * kWaveSize + lane;
+            v[r] = ch < n_full ? ld16(p.x + size_t(ch) * kVec) : u32x4{0u, 0u, 0u, 0u};
+        }
     }
-    const int32_t *qsl = use_lds ? s_qsl : p.sb.qsl;
+    uint32_t prev_z = 0, prev_w = 0;
+    if (lane == 0 && wbase > 0) {
+        const u32x2 t2 = *reinterpret_cast<const u32x2 *>(p.x + size_t(wbase) * kVec - 4);
+        prev_z = t2.x;
+        prev_w = t2.y;
+    }
+
+    // Wave-uniform rows, head and history.
+    const bool simple = s0.start == 0 && s0.end == int64_t(T);
+    const uint32_t e_first = wbase * kVec;
+    const uint32_t e_last = (e_first + kWaveElems <= p.n_elems ? e_first + kWaveElems : p.n_elems) - 1;
+    const uint32_t cA = p.divT.div(e_first);
+    const uint32_t row_a = cA * T, row_end = row_a + T;
+    uint32_t hp = kNone, R = 0;
+    if (e_first == row_a) { hp = e_first; R = cA; }
+    else if (row_end <= e_last) { hp = row_end; R = cA + 1; }
+    const bool cross = hp != kNone && uint64_t(hp) + (H - 1) > e_last;
+    const bool lead_owned = H >= 2 && e_first > row_a && e_first - row_a <= uint32_t(H - 1);
+    const PairTaps<W> tA = uniform(load_pair_taps<W>(p, cA));
+    const PairTaps<W> tB = (cA + 1 < uint32_t(p.dim)) ? uniform(load_pair_taps<W>(p, cA + 1)) : tA;
+    const bool own_head = simple && hp != kNone && !cross;
+
+    // Halo of every round first (each permute waits only for its own load).
+    const int src_lane = (lane + kWaveSize - 1) & (kWaveSize - 1);
+    uint32_t hz[kTokRounds], hw[kTokRounds];
+#pragma unroll
+    for (int r = 0; r < kTokRounds; ++r) {
+        const uint32_t rz = uint32_t(__shfl(int(v[r].z), src_lane));
+        const uint32_t rw = uint32_t(__shfl(int(v[r].w), src_lane));
+        hz[r] = lane == 0 ? prev_z : rz;
+        hw[r] = lane == 0 ? prev_w : rw;
+        prev_z = rz;
+        prev_w = rw;
+    }
+
+    // Interior chunks: computed and stored round by round.  Head chunks and
+    // element-path chunks are only marked here, which keeps this loop (and
+    // the register budget that sets the occupancy) small.
+    uint32_t head = 0, slow = 0;
+#pragma unroll
+    for (int r = 0; r < kTokRounds; ++r) {
+        const uint32_t chunk = wbase + r * kWaveSize + lane;
+        if (chunk >= p.n_chunks) continue;
+        const uint32_t i0 = chunk * kVec;
+        const bool at_head = hp != kNone && i0 + kVec > hp && i0 <= hp + (H - 1);
+        if (!simple || chunk >= n_full || (lead_owned && r == 0 && lane == 0) ||
+            (at_head && cross)) {
+            slow |= 1u << r;
+        } else if (at_head) {
+            head |= 1u << r;
+        } else {
+            Window win;
+            win.d[0] = hz[r];
+            win.d[1] = hw[r];
+            win.d[2] = v[r].x;
+            win.d[3] = v[r].y;
+            win.d[4] = v[r].z;
+            win.d[5] = v[r].w;
+            st16_stream(p.out + size_t(i0), fast_chunk<W, SILU>(win, select(i0 >= row_end, tB, tA)));
+        }
+    }
+
+    // The row head of this wave (at most two chunks, usually one lane): its
+    // history is the cached state, read once, uniformly, by this wave only;
+    // afterwards one lane replaces it with the row's last width-1 inputs.
+    if (own_head) {
+        uint32_t hb[H];
+        uint16_t nh[H];
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            const uint16_t b = s0.init
+                ? p.sb.cs[s0.line * p.sb.cs_sl + int64_t(R) * p.sb.cs_sd + k * p.sb.cs_st]
+                : uint16_t(0);
+            hb[k] = __builtin_amdgcn_readfirstlane(uint32_t(b));
+            nh[k] = uint16_t(__builtin_amdgcn_readfirstlane(p.x[size_t(R) * T + (T - H) + k]));
+        }
+        const PairTaps<W> &t_head = (R == cA) ? tA : tB;
+#pragma unroll 1
+        for (int r = 0; r < kTokRounds; ++r) {
+            if (!(head & (1u << r))) continue;
+            const uint32_t i0 = (wbase + r * kWaveSize + lane) * kVec;
+            Window win;
+            // elements 4..7 of the previous chunk (none before the tensor start,
+            // where every tap before the head comes from the history)
+            const u32x2 t2 = i0 >= kVec ? *reinterpret_cast<const u32x2 *>(p.x + size_t(i0) - 4)
+                                        : u32x2{0u, 0u};
+            const u32x4 cv = ld16(p.x + size_t(i0));
+            win.d[0] = t2.x;
+            win.d[1] = t2.y;
+            win.d[2] = cv.x;
+            win.d[3] = cv.y;
+            win.d[4] = cv.z;
+            win.d[5] = cv.w;
+            st16_stream(p.out + size_t(i0), head_chunk<W, SILU>(win, i0, hp, tA, t_head, hb));
+        }
+        if (p.sb.cs && lane == 0) {
+#pragma unroll
+            for (int k = 0; k < H; ++k)
+                p.sb.cs[s0.line * p.sb.cs_sl + int64_t(R) * p.sb.cs_sd + k * p.sb.cs_st] = nh[k];
+        }
+    }
+#pragma unroll 1
+    for (int r = 0; r < kTokRounds; ++r)
+        if (slow & (1u << r)) slow_chunk<W, SILU>(p, p.sb.qsl, (wbase + r * kWaveSize + lane) * kVec);
+}
+
+template <int W, bool SILU, bool VARLEN>
+__global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tokmajor_kernel(FwdTokParams p) {
+    constexpr int H = W - 1;
+    __shared__ int32_t s_qsl[VARLEN ? kQslLdsMax : 1];
+    const int32_t *qsl = p.sb.qsl;
+    if constexpr (VARLEN) {
+        if (p.sb.batch + 1 <= kQslLdsMax) {
+            for (int i = threadIdx.x; i <= p.sb.batch; i += blockDim.x) s_qsl[i] = p.sb.qsl[i];
+            __syncthreads();
+            qsl = s_qsl;
+        }
+    }
 
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wave = threadIdx.x / kWaveSize;
     const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const uint32_t wbase = (tile * kTokWavesPerBlock + wave) * uint32_t(kWaveSize * kTokRounds);
+    const uint32_t wbase = (tile * kTokWavesPerBlock + wave) * uint32_t(kChunksPerWave);
     if (wbase >= p.n_chunks) return;
 
     const uint32_t T = p.T;
@@ -140,15 +421,16 @@ __global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tokmajor_ke
 
     // Issue every load of the wave first.
     u32x4 v[kTokRounds];
+    if (wbase + kChunksPerWave <= n_full) {
 #pragma unroll
-    for (int r = 0; r < kTokRounds; ++r) {
-        const uint32_t ch = wbase + r * kWaveSize + lane;
-        if (ch < n_full) {
-            v[r] = ld16(p.x + size_t(ch) * kVec);
-        } else if (ch < p.n_chunks) {
-            v[r] = ld8_partial(p.x + size_t(ch) * kVec, int(p.n_elems - ch * kVec));
-        } else {
-            v[r] = u32x4{0u, 0u, 0u, 0u};
+        for (int r = 0; r < kTokRounds; ++r)
+            v[r] = ld16(p.x + size_t(wbase + r * kWaveSize + lane) * kVec);
+    } else {
+#pragma unroll
+        for (int r = 0; r < kTokRounds; ++r) {
+            const uint32_t ch = wbase + r * kWaveSize + lane;
+            if (ch < n_full) v[r] = ld16(p.x + size_t(ch) * kVec);
+            else v[r] = u32x4{0u, 0u, 0u, 0u};
         }
     }
     uint32_t prev_z = 0, prev_w = 0;     // lane 0: tail (elements 4..7) of the chunk before
@@ -158,73 +440,97 @@ __global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tokmajor_ke
         prev_w = t2.y;
     }
 
-    // The wave spans at most a few rows; the first two rows' taps are uniform.
-    const uint32_t cA = p.divT.div(wbase * kVec);
-    const Taps<W> tA = load_taps<W>(p, cA);
-    const Taps<W> tB = (cA + 1 < uint32_t(p.dim)) ? load_taps<W>(p, cA + 1) : tA;
+    // Wave-uniform row bookkeeping.
+    const uint32_t e_first = wbase * kVec;
+    const uint32_t cA = p.divT.div(e_first);
+    const uint32_t row_end = (cA + 1) * T;                 // first element of row cA+1
+    const uint32_t e_last = (e_first + kWaveElems <= p.n_elems ? e_first + kWaveElems : p.n_elems) - 1;
+    const bool two_rows = uint64_t(e_last) < uint64_t(row_end) + T;
+    PairTaps<W> tA, tB;
+    if (two_rows) {
+        tA = uniform(load_pair_taps<W>(p, cA));
+        tB = (cA + 1 < uint32_t(p.dim)) ? uniform(load_pair_taps<W>(p, cA + 1)) : tA;
+    }
     SeqInfo s0;
-    if (p.sb.batch == 1) s0 = seq_info(p.sb, qsl, 0);
+    if constexpr (!VARLEN) s0 = seq_info(p.sb, qsl, 0);
+    SeqCache sc;
 
+    // Halo of every round first (each permute waits only for its own load).
     const int src_lane = (lane + kWaveSize - 1) & (kWaveSize - 1);
+    uint32_t hz[kTokRounds], hw[kTokRounds];
 #pragma unroll
     for (int r = 0; r < kTokRounds; ++r) {
         const uint32_t rz = uint32_t(__shfl(int(v[r].z), src_lane));
         const uint32_t rw = uint32_t(__shfl(int(v[r].w), src_lane));
-        const uint32_t hz = lane == 0 ? prev_z : rz;
-        const uint32_t hw = lane == 0 ? prev_w : rw;
+        hz[r] = lane == 0 ? prev_z : rz;
+        hw[r] = lane == 0 ? prev_w : rw;
         prev_z = rz;
         prev_w = rw;
+    }
 
+    // Compute every fast chunk into registers, then store them back to back:
+    // a store inside the round loop would make the next round wait for it.
+    u32x4 o[kTokRounds];
+    uint32_t done = 0, slow = 0;
+#pragma unroll
+    for (int r = 0; r < kTokRounds; ++r) {
         const uint32_t chunk = wbase + r * kWaveSize + lane;
         if (chunk >= p.n_chunks) continue;
         const uint32_t i0 = chunk * kVec;
-        const uint32_t c = p.divT.div(i0);
-        const uint32_t t0 = i0 - c * T;
-
+        uint32_t t0;
+        PairTaps<W> tp;
+        if (two_rows) {
+            const bool in_b = i0 >= row_end;
+            t0 = i0 - (in_b ? row_end : row_end - T);
+            tp = select(in_b, tB, tA);
+        } else {
+            const uint32_t c = p.divT.div(i0);
+            t0 = i0 - c * T;
+            tp = load_pair_taps<W>(p, c);
+        }
         bool fast = chunk < n_full && t0 + kVec <= T;
         if (fast) {
-            SeqInfo si;
-            if (p.sb.batch == 1) si = s0;
-            else si = seq_info(p.sb, qsl, seq_search(qsl, p.sb.batch, t0));
-            fast = !si.skip && int64_t(t0) >= si.start + (W - 1) && int64_t(t0) + kVec <= si.end;
+            const SeqInfo &si = VARLEN ? sc.get(p.sb, qsl, t0) : s0;
+            fast = !si.skip && int64_t(t0) >= si.start + H && int64_t(t0) + kVec <= si.end;
         }
         if (fast) {
-            float e[kVec + W - 1];
-            const float hh[4] = {bf_lo(hz), bf_hi(hz), bf_lo(hw), bf_hi(hw)};
-#pragma unroll
-            for (int k = 0; k < W - 1; ++k) e[k] = hh[4 - (W - 1) + k];
-            unpack8(v[r], e + (W - 1));
-            const Taps<W> tp = (c == cA) ? tA : (c == cA + 1 ? tB : load_taps<W>(p, c));
-            float o[kVec];
-#pragma unroll
-            for (int j = 0; j < kVec; ++j) {
-                float acc = tp.b;
-#pragma unroll
-                for (int k = 0; k < W; ++k) acc = __builtin_fmaf(tp.w[k], e[j + k], acc);
-                o[j] = act<SILU>(acc);
-            }
-            st16_stream(p.out + size_t(i0), pack8(o));
+            Window win;
+            win.d[0] = hz[r];
+            win.d[1] = hw[r];
+            win.d[2] = v[r].x;
+            win.d[3] = v[r].y;
+            win.d[4] = v[r].z;
+            win.d[5] = v[r].w;
+            o[r] = fast_chunk<W, SILU>(win, tp);
+            done |= 1u << r;
         } else {
-            uint16_t eb[kVec + W - 1];
-            const uint16_t hb[4] = {uint16_t(hz & 0xffffu), uint16_t(hz >> 16),
-                                    uint16_t(hw & 0xffffu), uint16_t(hw >> 16)};
-#pragma unroll
-            for (int k = 0; k < W - 1; ++k) eb[k] = hb[4 - (W - 1) + k];
-#pragma unroll
-            for (int k = 0; k < kVec; ++k) eb[W - 1 + k] = lane_elem(v[r], k);
-            slow_chunk<W, SILU>(p, qsl, i0, eb, cA, tA, tB);
+            slow |= 1u << r;
         }
     }
+#pragma unroll
+    for (int r = 0; r < kTokRounds; ++r)
+        if (done & (1u << r))
+            st16_stream(p.out + size_t(wbase + r * kWaveSize + lane) * kVec, o[r]);
+    // Deferred boundary chunks (rare): element by element.
+#pragma unroll 1
+    for (int r = 0; r < kTokRounds; ++r)
+        if (slow & (1u << r)) slow_chunk<W, SILU>(p, qsl, (wbase + r * kWaveSize + lane) * kVec);
+}
+
+template <int W, bool SILU>
+hipError_t launch_ws(const FwdTokParams &p, hipStream_t s) {
+    const uint32_t blocks = (p.n_chunks + kTokWavesPerBlock * kChunksPerWave - 1) /
+                            (kTokWavesPerBlock * kChunksPerWave);
+    const dim3 grid(blocks), block(kTokWavesPerBlock * kWaveSize);
+    if (p.sb.batch > 1) fwd_tokmajor_kernel<W, SILU, true><<<grid, block, 0, s>>>(p);
+    else if (p.T >= kWaveElems) fwd_tok_long_kernel<W, SILU><<<grid, block, 0, s>>>(p);
+    else fwd_tokmajor_kernel<W, SILU, false><<<grid, block, 0, s>>>(p);
+    return hipGetLastError();
 }
 
 template <int W>
 hipError_t launch_w(const FwdTokParams &p, bool silu, hipStream_t s) {
-    const uint32_t per_block = kTokWavesPerBlock * kWaveSize * kTokRounds;
-    const uint32_t blocks = (p.n_chunks + per_block - 1) / per_block;
-    const dim3 grid(blocks), block(kTokWavesPerBlock * kWaveSize);
-    if (silu) fwd_tokmajor_kernel<W, true><<<grid, block, 0, s>>>(p);
-    else fwd_tokmajor_kernel<W, false><<<grid, block, 0, s>>>(p);
-    return hipGetLastError();
+    return silu ? launch_ws<W, true>(p, s) : launch_ws<W, false>(p, s);
 }
 
 }  // namespace

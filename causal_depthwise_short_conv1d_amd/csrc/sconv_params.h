@@ -127,7 +127,7 @@ hipError_t launch_paged_fused(const PagedParams &p, int width, bool silu, bool r
 constexpr int kWaveSize = 64;
 constexpr int kVec = 8;                          // bf16 per 16-byte vector
 constexpr int kSlab = kWaveSize * kVec;          // channels per wave (512)
-constexpr int kTokWavesPerBlock = 4;
+constexpr int kTokWavesPerBlock = 1;
 constexpr int kTokRounds = 4;                    // 64-chunk rounds per wave
 constexpr int kClWavesPerBlock = 4;
 constexpr int kPagedWavesPerBlock = 4;

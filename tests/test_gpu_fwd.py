@@ -91,16 +91,29 @@ def test_prefill_sweep_dim4096(T, layout):
 
 @pytest.mark.parametrize("T", W.LONG_PREFILL_DIM8192["Ts"])
 def test_long_prefill_dim8192(T):
-    """The benchmark launch: token-contiguous (dim, T), dim 8192, width 4."""
+    """The benchmark launch: token-contiguous (dim, T), dim 8192, width 4 --
+    every output and every state value compared with the oracle."""
     d = W.single_sequence(dim=8192, T=T, width=4, seed=W.seed_for(3, T % 97), device=DEV)
-    say(f"[fwd] dim8192 T{T} full-size launch")
+    say(f"[fwd] dim8192 T{T} full-size launch, full comparison")
     g_out, g_cs = run_gpu(d)
-    ch = sample_channels(8192, 64, seed=T)
-    r_out, r_cs = run_oracle(d, channels=ch)
-    assert_close(g_out[ch.to(DEV)], r_out, f"T{T} sampled out")
-    assert_bits(g_cs[:, ch.to(DEV)], r_cs, f"T{T} sampled state")
-    # every channel: the new state is the last width-1 inputs
-    assert_bits(g_cs[0], d["x"][:, T - 3:], f"T{T} state (all channels)")
+    r_out, r_cs = run_oracle(d)
+    assert_close(g_out, r_out, f"T{T} out")
+    assert_bits(g_cs, r_cs, f"T{T} state")
+
+
+@pytest.mark.parametrize("T", [2048, 2049, 2050, 3075, 4093, 4095, 4096])
+@pytest.mark.parametrize("width", [2, 3, 4, 5])
+@pytest.mark.parametrize("init", [True, False])
+def test_long_rows_every_head_position(T, width, init):
+    """Rows of at least one wave (2048 elements): row heads land at every
+    offset inside the waves, including heads whose first width-1 tokens cross
+    into the next wave and waves that start inside another wave's head."""
+    d = W.single_sequence(dim=72, T=T, width=width, seed=T * 10 + width, values="exact")
+    if not init:
+        d["has_initial_state"] = torch.zeros(1, dtype=torch.bool)
+    g = to_dev(d)
+    check_full(g, activation=None, exact=True, label=f"long rows T{T} W{width} init={init}")
+    check_full(g, activation="silu", label=f"long rows T{T} W{width} silu")
 
 
 def test_long_prefill_channel_contiguous():
