@@ -335,5 +335,83 @@ def cpu_baseline(torch, W, nbytes, base):
             "host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
 
 
+def summarize(argv):
+    """Turn rocprofv3 CSV output of headline runs into the committed summary:
+
+        python bench.py summarize TRACE_DIR FETCH_DIR WRITE_DIR OUT_PREFIX CMDLINE
+
+    TRACE_DIR holds --kernel-trace --stats output, FETCH_DIR / WRITE_DIR the
+    --pmc FETCH_SIZE / --pmc WRITE_SIZE passes of the same command.  The
+    counters are scaled by what they read for the run's calibration copies
+    (the last three 256 MiB device copies).  Writes OUT_PREFIX.txt and, for
+    the headline kernel, the traffic JSON that the benchmark reports."""
+    import csv
+    import glob
+    trace_dir, fetch_dir, write_dir, out_prefix, cmdline = argv[:5]
+    calib = float(1 << 28)
+
+    def one(d, pattern):
+        f = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+        if not f:
+            raise SystemExit(f"no {pattern} under {d}")
+        return f[0]
+
+    stats = list(csv.DictReader(open(one(trace_dir, "*kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(one(trace_dir, "*kernel_trace.csv"))))
+
+    def counters(d, name):
+        rows = [r for r in csv.DictReader(open(one(d, "*counter_collection.csv")))
+                if r["Counter_Name"] == name]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        cal = [float(r["Counter_Value"]) * 1024 for r in rows
+               if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) == 131072][-3:]
+        factor = calib / statistics.mean(cal)
+        ours = [float(r["Counter_Value"]) * 1024 for r in rows if "sconv::" in r["Kernel_Name"]]
+        return factor, statistics.mean(ours), len(ours)
+
+    fr, fetch, nf = counters(fetch_dir, "FETCH_SIZE")
+    fw, write, nw = counters(write_dir, "WRITE_SIZE")
+    headline = [r for r in stats if "sconv::" in r["Name"]]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in trace
+            if "sconv::" in r["Kernel_Name"]]
+    nbytes = fwd_bytes(HEADLINE["dim"], [HEADLINE["T"]], HEADLINE["width"])
+    traffic = fetch * fr + write * fw
+    lines = [
+        f"# rocprofv3 summary: token-contiguous forward, dim {HEADLINE['dim']}, "
+        f"T {HEADLINE['T']}, width {HEADLINE['width']}, SiLU, bias, initial state",
+        f"# command: {cmdline}",
+        f"# kernel source hash: {kernel_hash()}",
+        "",
+        "## kernel trace (--kernel-trace --stats), all kernels of the run",
+        "name | calls | avg us | min us | max us",
+    ]
+    for r in stats:
+        lines.append(f"{r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                     f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f}")
+    if durs:
+        med = statistics.median(durs) / 1e3
+        lines += ["", f"headline kernel: {len(durs)} dispatches, median {med:.2f} us, "
+                      f"mean {statistics.mean(durs)/1e3:.2f} us",
+                  f"algorithmic bytes per launch: {nbytes} -> "
+                  f"{nbytes / statistics.mean(durs):.1f} GB/s at the mean duration "
+                  f"({100 * nbytes / statistics.mean(durs) / HBM_PEAK_GBS:.1f}% of 8 TB/s)"]
+    lines += ["", "## HBM counters (--pmc FETCH_SIZE, --pmc WRITE_SIZE), per headline launch",
+              f"FETCH_SIZE raw {fetch:.0f} B x calibration {fr:.4f} = {fetch*fr:.0f} B ({nf} dispatches)",
+              f"WRITE_SIZE raw {write:.0f} B x calibration {fw:.4f} = {write*fw:.0f} B ({nw} dispatches)",
+              f"calibration: each counter divided into 268435456 B for the run's 256 MiB device copies",
+              f"HBM traffic {traffic:.0f} B vs algorithmic {nbytes} B "
+              f"({100 * (traffic / nbytes - 1):+.2f}%)"]
+    open(out_prefix + ".txt", "w").write("\n".join(lines) + "\n")
+    json.dump({"kernel_hash": kernel_hash(), "bytes_per_launch": round(traffic),
+               "fetch_bytes": round(fetch * fr), "write_bytes": round(write * fw),
+               "fetch_calibration": round(fr, 4), "write_calibration": round(fw, 4),
+               "algorithmic_bytes": nbytes, "command": cmdline},
+              open(TRAFFIC_FILE, "w"), indent=1)
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
-    main()
+    if len(sys.argv) > 1 and sys.argv[1] == "summarize":
+        summarize(sys.argv[2:])
+    else:
+        main()

@@ -2,11 +2,15 @@
 // tokenspeed causal_conv1d.py launcher (causal_conv1d_fn) requires for its
 // packed continuous-batching input.
 //
-// Decomposition: a wave owns a [bt tokens x 512 channels] tile; each lane
-// owns 8 adjacent channels (one 16-byte vector per token row, 1 KiB per wave
-// per row, fully coalesced) and walks the tile's tokens keeping the previous
-// width-1 inputs of its channels in registers.  All lanes of a wave share the
-// token, so the sequence bookkeeping is wave-uniform.
+// Decomposition: a wave owns a [bt tokens x 256 channels] tile; each lane
+// owns 4 adjacent channels (one 8-byte vector per token row, 512 B per wave
+// per row, fully coalesced), keeps 8 rows in flight, and walks the tile's
+// tokens keeping the previous width-1 input rows in registers, still packed.
+// The taps pair two rows' values of a channel with one byte permute and
+// accumulate them with the gfx950 dot2 instruction (exact products, fp32
+// sums); keeping rows and weights packed halves the registers, which is what
+// sets the occupancy of this streaming kernel.  All lanes of a wave share
+// the token, so the sequence bookkeeping is wave-uniform.
 //
 // Ownership of a sequence's history: the tile holding the sequence's first
 // token processes the first width-1 tokens of that sequence (spilling past
@@ -19,112 +23,234 @@ namespace sconv {
 
 namespace {
 
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;                     // token rows in flight per lane
 
+// A lane's taps for its 4 channels, packed for dot2: pair q of channel ch is
+// (w[ch][2q], w[ch][2q+1]); an odd last tap and the bias are fp32.
+template <int W>
+struct LaneTaps {
+    uint32_t wp[W / 2 > 0 ? W / 2 : 1][kCpl];
+    float wl[kCpl];
+    float b[kCpl];
+};
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// (channel ch of row a, channel ch of row b) as one bf16 pair.
+__device__ __forceinline__ uint32_t cross_pair(const u32x2 &ra, const u32x2 &rb, int ch) {
+    const uint32_t da = (ch >> 1) ? ra.y : ra.x, db = (ch >> 1) ? rb.y : rb.x;
+    return __builtin_amdgcn_perm(db, da, (ch & 1) ? 0x07060302u : 0x05040100u);
+}
+
+template <bool FULL>
+__device__ __forceinline__ u32x2 ld_row(const uint16_t *p, int nv) {
+    if constexpr (FULL) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));   // idle lanes read channel 0
+    } else {
+        uint32_t e[kCpl];
+#pragma unroll
+        for (int i = 0; i < kCpl; ++i) e[i] = i < nv ? p[i] : 0u;
+        return u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+    }
+}
+template <bool FULL>
+__device__ __forceinline__ void st_row(uint16_t *p, const u32x2 &v, int nv) {
+    if constexpr (FULL) {
+        if (nv > 0) __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
+    } else {
+        const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+        for (int i = 0; i < kCpl; ++i)
+            if (i < nv) p[i] = uint16_t((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
+    }
+}
+__device__ __forceinline__ uint16_t row_elem(const u32x2 &v, int i) {
+    return uint16_t((((i >> 1) ? v.y : v.x) >> ((i & 1) * 16)) & 0xffffu);
+}
+
+// Rows of a (T, pitch) bf16 tensor seen through a buffer descriptor based at
+// row `base`: a row's byte offset is a wave-uniform scalar, the lane's
+// channel offset the only vector operand, so the rows kept in flight cost no
+// address registers.  Offsets past `bytes` read 0 / drop the write.
+struct Rows {
+    __amdgpu_buffer_rsrc_t rsrc;
+    int64_t base;
+    int64_t pitch;   // bytes
+};
+__device__ __forceinline__ Rows make_rows(const uint16_t *t, int64_t base, int64_t stride,
+                                          int64_t rows_total, int32_t dim) {
+    Rows r;
+    r.base = base;
+    r.pitch = stride * 2;
+    // last row's channels end the extent (the row stride may be 0 when T == 1)
+    const int64_t bytes = (rows_total - base - 1) * r.pitch + int64_t(dim) * 2;
+    r.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(t + base * stride), short(0),
+                                               int(bytes < 0x7fffffff ? bytes : 0x7fffffff),
+                                               0x00020000);
+    return r;
+}
+constexpr int kNt = 2;   // non-temporal cache policy bit of buffer accesses
+__device__ __forceinline__ u32x2 ld_rows(const Rows &r, int64_t row, uint32_t voff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                         r.rsrc, voff, int((row - r.base) * r.pitch), kNt));
+}
+__device__ __forceinline__ void st_rows(const Rows &r, int64_t row, uint32_t voff, const u32x2 &v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v),
+                                          r.rsrc, voff, int((row - r.base) * r.pitch), kNt);
+}
+
+// Outputs of one token row: the taps' inputs are the H window rows (oldest
+// first) and the row itself.
 template <int W, bool SILU>
+__device__ __forceinline__ u32x2 conv_row(const LaneTaps<W> &tp, const u32x2 (&win)[W - 1],
+                                          const u32x2 &x) {
+    constexpr int H = W - 1;
+    float o[kCpl];
+#pragma unroll
+    for (int ch = 0; ch < kCpl; ++ch) {
+        float acc = tp.b[ch];
+#pragma unroll
+        for (int q = 0; q < W / 2; ++q) {
+            const u32x2 &ra = win[2 * q];
+            const u32x2 &rb = (2 * q + 1 < H) ? win[(2 * q + 1) < H ? 2 * q + 1 : 0] : x;
+            acc = dot2(cross_pair(ra, rb, ch), tp.wp[q][ch], acc);
+        }
+        if constexpr (W & 1) {
+            const uint32_t d = (ch >> 1) ? x.y : x.x;
+            acc = __builtin_fmaf(tp.wl[ch], (ch & 1) ? bf_hi(d) : bf_lo(d), acc);
+        }
+        o[ch] = act<SILU>(acc);
+    }
+    return u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+}
+
+template <int W, bool SILU, bool FULL>
 __device__ __forceinline__ void run_segment(const FwdClParams &p, const SeqInfo &si,
                                             int64_t b, int64_t e, bool head, int32_t c0,
-                                            int nv, const float (&wf)[W][kVec],
-                                            const float (&bf)[kVec]) {
-    float win[W - 1][kVec];
+                                            int nv, const LaneTaps<W> &tp) {
+    constexpr int H = W - 1;
+    // Row addresses are wave-uniform (scalar registers); only the lane's
+    // channel offset c0 lives in a vector register.
+    u32x2 win[H];
     if (head) {
-        uint16_t h[W - 1][kVec];
+        // One state line through a buffer descriptor: element (c, k) at byte
+        // 2*(c*cs_sd + k*cs_st) from the line start (the host bounds a line's
+        // extent below 2 GiB); only the lane's channel offsets are vectors.
+        // (no state: a zero-length descriptor, never dereferenced)
+        const __amdgpu_buffer_rsrc_t cs = __builtin_amdgcn_make_buffer_rsrc(
+            p.sb.cs ? p.sb.cs + si.line * p.sb.cs_sl : p.sb.cs, short(0),
+            p.sb.cs ? 0x7fffffff : 0, 0x00020000);
+        uint32_t coff[kCpl];
 #pragma unroll
-        for (int k = 0; k < W - 1; ++k)
+        for (int ch = 0; ch < kCpl; ++ch) coff[ch] = uint32_t(int64_t(c0 + ch) * p.sb.cs_sd * 2);
+        // the cached history, packed as it arrives
 #pragma unroll
-            for (int ch = 0; ch < kVec; ++ch)
-                h[k][ch] = (si.init && ch < nv)
-                               ? p.sb.cs[si.line * p.sb.cs_sl + int64_t(c0 + ch) * p.sb.cs_sd +
-                                         k * p.sb.cs_st]
-                               : uint16_t(0);
+        for (int k = 0; k < H; ++k) {
+            uint32_t d[2] = {0u, 0u};
+            if (si.init) {
 #pragma unroll
-        for (int k = 0; k < W - 1; ++k)
-#pragma unroll
-            for (int ch = 0; ch < kVec; ++ch) win[k][ch] = bf_one(h[k][ch]);
+                for (int ch = 0; ch < kCpl; ++ch)
+                    if (ch < nv)
+                        d[ch >> 1] |= uint32_t(__builtin_amdgcn_raw_buffer_load_b16(
+                                          cs, coff[ch], int(k * p.sb.cs_st * 2), 0))
+                                      << (16 * (ch & 1));
+            }
+            win[k] = u32x2{d[0], d[1]};
+        }
         if (p.sb.cs) {
             // new state = the last width-1 entries of (history ++ sequence)
             const int64_t L = si.end - si.start;
-            uint16_t nh[W - 1][kVec];
+            u32x2 nh[H];
 #pragma unroll
-            for (int k = 0; k < W - 1; ++k) {
+            for (int k = 0; k < H; ++k) {
                 const int64_t m = L + k;
-                if (m < W - 1) {
+                u32x2 hv = win[0];
 #pragma unroll
-                    for (int ch = 0; ch < kVec; ++ch) nh[k][ch] = h[m][ch];
+                for (int q = 1; q < H; ++q)
+                    if (m == q) hv = win[q];
+                if (m < H) {
+                    nh[k] = hv;
                 } else {
-                    const u32x4 v = ld8_partial(p.x + (si.start + m - (W - 1)) * p.x_st + c0, nv);
-#pragma unroll
-                    for (int ch = 0; ch < kVec; ++ch) nh[k][ch] = lane_elem(v, ch);
+                    const int64_t row = si.start + m - H;
+                    nh[k] = FULL ? ld_rows(make_rows(p.x, row, p.x_st, p.sb.total_T, p.dim), row,
+                                           uint32_t(c0) * 2)
+                                 : ld_row<FULL>(p.x + row * p.x_st + c0, nv);
                 }
             }
 #pragma unroll
-            for (int k = 0; k < W - 1; ++k)
+            for (int k = 0; k < H; ++k)
 #pragma unroll
-                for (int ch = 0; ch < kVec; ++ch)
+                for (int ch = 0; ch < kCpl; ++ch)
                     if (ch < nv)
-                        p.sb.cs[si.line * p.sb.cs_sl + int64_t(c0 + ch) * p.sb.cs_sd +
-                                k * p.sb.cs_st] = nh[k][ch];
+                        __builtin_amdgcn_raw_buffer_store_b16(row_elem(nh[k], ch), cs, coff[ch],
+                                                              int(k * p.sb.cs_st * 2), 0);
         }
-    } else {
+    }
+    const int64_t T = p.sb.total_T;
+    const int64_t base = head ? b : b - H;
+    const Rows xr = make_rows(p.x, base, p.x_st, T, p.dim);
+    const Rows orr = make_rows(p.out, base, p.o_st, T, p.dim);
+    const uint32_t voff = uint32_t(c0) * 2;
+    if (!head) {
         // interior: the previous width-1 rows belong to the same sequence
 #pragma unroll
-        for (int k = 0; k < W - 1; ++k) {
-            const u32x4 v = ld8_partial(p.x + (b - (W - 1) + k) * p.x_st + c0, nv);
-            unpack8(v, win[k]);
-        }
+        for (int k = 0; k < H; ++k)
+            win[k] = FULL ? ld_rows(xr, b - H + k, voff)
+                          : ld_row<FULL>(p.x + (b - H + k) * p.x_st + c0, nv);
     }
 
     for (int64_t t = b; t < e; t += kUnroll) {
         const int n = (e - t) < kUnroll ? int(e - t) : kUnroll;
-        u32x4 xv[kUnroll];
+        u32x2 xv[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            if (u < n) xv[u] = ld8_partial(p.x + (t + u) * p.x_st + c0, nv);
+            if (u < n)
+                xv[u] = FULL ? ld_rows(xr, t + u, voff) : ld_row<FULL>(p.x + (t + u) * p.x_st + c0, nv);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             if (u < n) {
-                float xf[kVec], o[kVec];
-                unpack8(xv[u], xf);
-#pragma unroll
-                for (int ch = 0; ch < kVec; ++ch) {
-                    float acc = bf[ch];
-#pragma unroll
-                    for (int k = 0; k < W - 1; ++k) acc = __builtin_fmaf(wf[k][ch], win[k][ch], acc);
-                    acc = __builtin_fmaf(wf[W - 1][ch], xf[ch], acc);
-                    o[ch] = act<SILU>(acc);
+                const u32x2 o = conv_row<W, SILU>(tp, win, xv[u]);
+                if constexpr (FULL) {
+                    if (nv > 0) st_rows(orr, t + u, voff, o);
+                } else {
+                    st_row<FULL>(p.out + (t + u) * p.o_st + c0, o, nv);
                 }
-                st8_partial(p.out + (t + u) * p.o_st + c0, pack8(o), nv, true);
 #pragma unroll
-                for (int k = 0; k + 1 < W - 1; ++k)
-#pragma unroll
-                    for (int ch = 0; ch < kVec; ++ch) win[k][ch] = win[k + 1][ch];
-#pragma unroll
-                for (int ch = 0; ch < kVec; ++ch) win[W - 2][ch] = xf[ch];
+                for (int k = 0; k + 1 < H; ++k) win[k] = win[k + 1];
+                win[H - 1] = xv[u];
             }
         }
     }
 }
 
-template <int W, bool SILU>
+template <int W, bool SILU, bool FULL>
 __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_chanlast_kernel(FwdClParams p) {
     const int lane = threadIdx.x & (kWaveSize - 1);
-    const int wave = threadIdx.x / kWaveSize;
-    const uint32_t wt = xcd_tile(blockIdx.x, gridDim.x) * kClWavesPerBlock + wave;
+    // wave index within the block: uniform, and marked so for the compiler
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+    const uint32_t wt = blockIdx.x * kClWavesPerBlock + wave;
     const int32_t slab = int32_t(wt % uint32_t(p.n_slabs));
     const int32_t tt = int32_t(wt / uint32_t(p.n_slabs));
     if (tt >= p.n_tiles) return;
 
-    const int32_t c0 = slab * kSlab + lane * kVec;
+    int32_t c0 = slab * kClSlab + lane * kCpl;
     int nv = p.dim - c0;
-    nv = nv < 0 ? 0 : (nv > kVec ? kVec : nv);
+    nv = nv < 0 ? 0 : (nv > kCpl ? kCpl : nv);
+    if (nv == 0) c0 = 0;                   // idle lane: in-range reads, no writes
 
-    float wf[W][kVec], bf[kVec];
+    LaneTaps<W> tp;
 #pragma unroll
-    for (int ch = 0; ch < kVec; ++ch) {
+    for (int ch = 0; ch < kCpl; ++ch) {
         const bool ok = ch < nv;
+        const uint16_t *w = p.w + int64_t(ok ? c0 + ch : 0) * p.w_sd;
 #pragma unroll
-        for (int k = 0; k < W; ++k) wf[k][ch] = ok ? bf_one(p.w[int64_t(c0 + ch) * p.w_sd + k]) : 0.0f;
-        bf[ch] = (ok && p.bias) ? bf_one(p.bias[c0 + ch]) : 0.0f;
+        for (int q = 0; q < W / 2; ++q)
+            tp.wp[q][ch] = ok ? (uint32_t(w[2 * q]) | (uint32_t(w[2 * q + 1]) << 16)) : 0u;
+        tp.wl[ch] = (ok && (W & 1)) ? bf_one(w[W - 1]) : 0.0f;
+        tp.b[ch] = (ok && p.bias) ? bf_one(p.bias[c0 + ch]) : 0.0f;
     }
 
     const int64_t T = p.sb.total_T;
@@ -154,7 +280,10 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_chanlast_ker
             const int64_t hend = si.start + (W - 1) < si.end ? si.start + (W - 1) : si.end;
             e = e > hend ? e : hend;
         }
-        if (!si.skip && b < e && nv > 0) run_segment<W, SILU>(p, si, b, e, head, c0, nv, wf, bf);
+        // Every lane runs the segment (the control flow stays wave-uniform, so
+        // row addresses stay scalar); lanes past the last channel read channel
+        // 0 and store nothing.
+        if (!si.skip && b < e) run_segment<W, SILU, FULL>(p, si, b, e, head, c0, nv, tp);
         t = b > e ? b : e;
         if (t >= si.end && ++s >= p.sb.batch) break;
     }
@@ -165,8 +294,11 @@ hipError_t launch_w(const FwdClParams &p, bool silu, hipStream_t s) {
     const uint64_t waves = uint64_t(p.n_tiles) * uint64_t(p.n_slabs);
     const uint32_t blocks = uint32_t((waves + kClWavesPerBlock - 1) / kClWavesPerBlock);
     const dim3 grid(blocks), block(kClWavesPerBlock * kWaveSize);
-    if (silu) fwd_chanlast_kernel<W, true><<<grid, block, 0, s>>>(p);
-    else fwd_chanlast_kernel<W, false><<<grid, block, 0, s>>>(p);
+    const bool full = p.dim % kCpl == 0;
+    if (silu && full) fwd_chanlast_kernel<W, true, true><<<grid, block, 0, s>>>(p);
+    else if (silu) fwd_chanlast_kernel<W, true, false><<<grid, block, 0, s>>>(p);
+    else if (full) fwd_chanlast_kernel<W, false, true><<<grid, block, 0, s>>>(p);
+    else fwd_chanlast_kernel<W, false, false><<<grid, block, 0, s>>>(p);
     return hipGetLastError();
 }
 

@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tok_long_ke
     constexpr uint32_t kNone = 0xffffffffu;
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wave = threadIdx.x / kWaveSize;
-    const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const uint32_t tile = blockIdx.x;
     const uint32_t wbase = (tile * kTokWavesPerBlock + wave) * uint32_t(kChunksPerWave);
     if (wbase >= p.n_chunks) return;
     const SeqInfo s0 = seq_info(p.sb, p.sb.qsl, 0);
@@ -283,12 +283,12 @@ __global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tok_long_ke
     if (wbase + kChunksPerWave <= n_full) {
 #pragma unroll
         for (int r = 0; r < kTokRounds; ++r)
-            v[r] = ld16(p.x + size_t(wbase + r * kWaveSize + lane) * kVec);
+            v[r] = ld16_stream(p.x + size_t(wbase + r * kWaveSize + lane) * kVec);
     } else {
 #pragma unroll
         for (int r = 0; r < kTokRounds; ++r) {
             const uint32_t ch = wbase + r * kWaveSize + lane;
-            v[r] = ch < n_full ? ld16(p.x + size_t(ch) * kVec) : u32x4{0u, 0u, 0u, 0u};
+            v[r] = ch < n_full ? ld16_stream(p.x + size_t(ch) * kVec) : u32x4{0u, 0u, 0u, 0u};
         }
     }
     uint32_t prev_z = 0, prev_w = 0;
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tokmajor_ke
 
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wave = threadIdx.x / kWaveSize;
-    const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const uint32_t tile = blockIdx.x;
     const uint32_t wbase = (tile * kTokWavesPerBlock + wave) * uint32_t(kChunksPerWave);
     if (wbase >= p.n_chunks) return;
 

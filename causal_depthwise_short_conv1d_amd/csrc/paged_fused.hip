@@ -42,8 +42,9 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     const int32_t *qsl = use_lds ? s_qsl : p.qsl;
 
     const int lane = threadIdx.x & (kWaveSize - 1);
-    const int wave = threadIdx.x / kWaveSize;
-    const uint32_t wt = xcd_tile(blockIdx.x, gridDim.x) * kPagedWavesPerBlock + wave;
+    // wave index within the block: uniform, and marked so for the compiler
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+    const uint32_t wt = blockIdx.x * kPagedWavesPerBlock + wave;
     const int32_t slab = int32_t(wt % uint32_t(p.n_slabs));
     const int32_t tt = int32_t(wt / uint32_t(p.n_slabs));
     if (tt >= p.n_tiles) return;

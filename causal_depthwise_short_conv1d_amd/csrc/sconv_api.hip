@@ -150,7 +150,7 @@ int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
         p.bias = static_cast<const uint16_t *>(bias);
         p.sb = sb;
         p.dim = dim;
-        p.n_slabs = (dim + kSlab - 1) / kSlab;
+        p.n_slabs = (dim + kClSlab - 1) / kClSlab;
         p.bt = chanlast_tile(T, p.n_slabs);
         p.n_tiles = int32_t((T + p.bt - 1) / p.bt);
         if (uint64_t(p.n_tiles) * uint64_t(p.n_slabs) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;

@@ -63,6 +63,10 @@ __device__ __forceinline__ float act(float a) {
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
+// Streaming (non-temporal) load for data read exactly once.
+__device__ __forceinline__ u32x4 ld16_stream(const uint16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 __device__ __forceinline__ void st16_stream(uint16_t *p, const u32x4 &v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
@@ -132,16 +136,6 @@ __device__ __forceinline__ SeqInfo seq_info(const SeqBatch &sb, const int32_t *q
               (sb.cs && (si.line < 0 || si.line >= sb.num_lines));
     si.init = sb.cs && sb.has_init && sb.has_init[s] != 0;
     return si;
-}
-
-// Map a launch-order block id to a tile id so that each XCD (blocks are
-// dealt round-robin to the 8 XCDs) walks one contiguous range of tiles:
-// neighbouring tiles, whose halos overlap, then share an L2.
-__device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t nblocks) {
-    constexpr uint32_t kXcds = 8;
-    const uint32_t xcd = bid % kXcds, idx = bid / kXcds;
-    const uint32_t q = nblocks / kXcds, r = nblocks % kXcds;
-    return xcd * q + (xcd < r ? xcd : r) + idx;
 }
 
 }  // namespace sconv

@@ -130,6 +130,8 @@ constexpr int kSlab = kWaveSize * kVec;          // channels per wave (512)
 constexpr int kTokWavesPerBlock = 1;
 constexpr int kTokRounds = 4;                    // 64-chunk rounds per wave
 constexpr int kClWavesPerBlock = 4;
+constexpr int kCpl = 4;                          // channels per lane, channel-contiguous
+constexpr int kClSlab = kWaveSize * kCpl;        // channels per wave there (256)
 constexpr int kPagedWavesPerBlock = 4;
 constexpr int kPagedBT = 16;                     // tokens per paged wave tile
 constexpr int kQslLdsMax = 2048;                 // qsl entries staged in LDS
