@@ -2,28 +2,36 @@
 // Inkling sconv.py, fused_sconv / _fused_sconv_kernel, with the
 // token -> request search of its _seq_metadata_kernel done in-kernel.
 //
-// Decomposition: a wave owns [kPagedBT tokens x 512 channels]; each lane owns
-// 8 adjacent channels, which lie in one head (ws % 8 == 0), so every cache
-// access of a lane is one 16-byte vector at D offset off_s + c % ws.
+// Decomposition: a wave owns [kPagedBT tokens x 256 channels]; each lane owns
+// 4 adjacent channels, which lie in one head (ws % 8 == 0), so every cache
+// access of a lane is one 8-byte vector at D offset off_s + c % ws.
 // Latency, not bandwidth, is the hazard here (decode rows are pure gathers
 // through block_table): the per-token metadata of the tile -- slot,
 // position, request, and for every tap whether it is zero, a row of x, or a
 // cached slot -- is resolved first, one token per lane, all loads in
 // parallel; the token loop then broadcasts it with readlane and keeps
-// kUnroll tokens' loads in flight.
+// kPagedUnroll tokens' loads (rows and gathers) in flight.
 //
-// Taps inside the forward read the immutable x (the previous width-1 rows
-// are kept in registers); only pre-forward positions are read from the
-// cache, so the inserts of this launch are never read back by it.
+// Every access goes through a buffer descriptor whose base is wave-uniform
+// (the tile's rows of x / out, or the physical block of a cached position),
+// so the in-flight rows cost no address registers and the descriptors are
+// built on the scalar unit.  Taps inside the forward read the immutable x
+// (the previous width-1 rows are kept in registers); only pre-forward
+// positions are read from the cache, so the inserts of this launch are never
+// read back by it.
 #include "sconv_device.h"
 
 namespace sconv {
 
 namespace {
 
-constexpr int kUnroll = 4;
-constexpr int kTapZero = -2;    // position before 0, pad row, or unmapped block
-constexpr int kTapIntra = -1;   // a row of x inside this forward
+constexpr int kPCpl = 4;                        // channels per lane
+constexpr int kPSlab = kPagedSlab;              // channels per wave (256)
+static_assert(kPSlab == kWaveSize * kPCpl, "paged slab = 64 lanes x 4 channels");
+constexpr int kPagedUnroll = 4;                 // tokens in flight per lane
+constexpr int kTapZero = -2;                    // position before 0, pad row, unmapped block
+constexpr int kTapIntra = -1;                   // a row of x inside this forward
+constexpr int kNt = 2;                          // non-temporal cache policy bit
 
 __device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
     const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), lane));
@@ -31,8 +39,39 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
     return int64_t((uint64_t(hi) << 32) | lo);
 }
 
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// (channel ch of row a, channel ch of row b) as one bf16 pair.
+__device__ __forceinline__ uint32_t cross_pair(const u32x2 &ra, const u32x2 &rb, int ch) {
+    const uint32_t da = (ch >> 1) ? ra.y : ra.x, db = (ch >> 1) ? rb.y : rb.x;
+    return __builtin_amdgcn_perm(db, da, (ch & 1) ? 0x07060302u : 0x05040100u);
+}
+
+typedef unsigned int ui32x2 __attribute__((ext_vector_type(2)));
+
+// A buffer descriptor over `bytes` bytes from `base` (offsets past the end
+// read 0 / drop the write).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0),
+                                             int(bytes < 0x7fffffff ? bytes : 0x7fffffff),
+                                             0x00020000);
+}
+template <int AUX>
+__device__ __forceinline__ u32x2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff, int64_t soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, int(soff), AUX));
+}
+template <int AUX>
+__device__ __forceinline__ void st8(__amdgpu_buffer_rsrc_t r, uint32_t voff, int64_t soff,
+                                    const u32x2 &v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(ui32x2, v), r, voff, int(soff), AUX);
+}
+
 template <int W, bool SILU, bool RESID>
 __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_kernel(PagedParams p) {
+    constexpr int H = W - 1;
     __shared__ int32_t s_qsl[kQslLdsMax];
     const bool use_lds = p.num_reqs + 1 <= kQslLdsMax;
     if (use_lds) {
@@ -49,19 +88,23 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     const int32_t tt = int32_t(wt / uint32_t(p.n_slabs));
     if (tt >= p.n_tiles) return;
 
-    const int32_t c0 = slab * kSlab + lane * kVec;
-    int nv = p.C - c0;
-    nv = nv < 0 ? 0 : (nv > kVec ? kVec : nv);
-    const int32_t cc = nv > 0 ? c0 : 0;                 // keeps idle lanes' addresses in range
-    const int64_t lane_off = int64_t(cc / p.ws) * p.c_sh + (p.off_s + cc % p.ws);
+    int32_t c0 = slab * kPSlab + lane * kPCpl;
+    const bool active = c0 < p.C;
+    if (!active) c0 = 0;                 // idle lane: in-range reads, no writes
+    // byte offsets of the lane's 4 channels inside a block and inside a row
+    const uint32_t coff = uint32_t((int64_t(c0 / p.ws) * p.c_sh + (p.off_s + c0 % p.ws)) * 2);
+    const uint32_t xoff = uint32_t(c0) * 2;
 
-    float wf[W][kVec], bf[kVec];
+    // taps: pair q of channel ch is (w[ch][2q], w[ch][2q+1]); odd last tap fp32
+    uint32_t wp[W / 2 > 0 ? W / 2 : 1][kPCpl];
+    float wl[kPCpl], bf[kPCpl];
 #pragma unroll
-    for (int ch = 0; ch < kVec; ++ch) {
-        const bool ok = ch < nv;
+    for (int ch = 0; ch < kPCpl; ++ch) {
+        const uint16_t *w = p.w + int64_t(c0 + ch) * p.w_sd;
 #pragma unroll
-        for (int k = 0; k < W; ++k) wf[k][ch] = ok ? bf_one(p.w[int64_t(c0 + ch) * p.w_sd + k]) : 0.0f;
-        bf[ch] = (ok && p.bias) ? bf_one(p.bias[c0 + ch]) : 0.0f;
+        for (int q = 0; q < W / 2; ++q) wp[q][ch] = uint32_t(w[2 * q]) | (uint32_t(w[2 * q + 1]) << 16);
+        wl[ch] = (W & 1) ? bf_one(w[W - 1]) : 0.0f;
+        bf[ch] = p.bias ? bf_one(p.bias[c0 + ch]) : 0.0f;
     }
 
     const int64_t tile_start = int64_t(tt) * kPagedBT;
@@ -69,120 +112,138 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     int64_t actual = p.num_reqs > 0 ? int64_t(qsl[p.num_reqs]) : 0;
     actual = actual < 0 ? 0 : (actual > p.T ? p.T : actual);
 
-    // Per-token metadata, token tile_start + lane in lane `lane`.
-    int64_t m_slot = -1;
+    // Per-token metadata, token tile_start + lane in lane `lane`, as 32-bit
+    // values (the token loop broadcasts them with readlane, so every cache
+    // address below is built on the scalar unit):
+    //   m_sblk / m_sn : physical block / slot of the insert (m_sblk < 0: none)
+    //   m_tblk / m_tn : per tap, the block / slot of a cached position, or
+    //                   kTapIntra (a row of x) or kTapZero.
+    int32_t m_sblk = -1, m_sn = 0;
     int32_t m_pad = 1;
     int64_t m_qs = 0;
-    int64_t m_tap[W - 1];
+    int32_t m_tblk[H], m_tn[H];
 #pragma unroll
-    for (int j = 0; j < W - 1; ++j) m_tap[j] = kTapZero;
+    for (int j = 0; j < H; ++j) {
+        m_tblk[j] = kTapZero;
+        m_tn[j] = 0;
+    }
     if (lane < n_tok) {
         const int64_t t = tile_start + lane;
-        m_slot = p.slot[t];
+        const int64_t slot = p.slot[t];
         const int64_t pos = p.pos[t];
-        m_pad = (m_slot < 0 || t >= actual) ? 1 : 0;
+        m_pad = (slot < 0 || t >= actual) ? 1 : 0;
         if (!m_pad) {
+            const int64_t sb = slot / p.block_size;
+            if (sb < p.num_blocks) {
+                m_sblk = int32_t(sb);
+                m_sn = int32_t(slot % p.block_size);
+            }
             const int32_t r = seq_search(qsl, p.num_reqs, t);
             m_qs = qsl[r];
 #pragma unroll
-            for (int j = 0; j < W - 1; ++j) {
-                const int64_t src = pos - (W - 1) + j;
-                const int64_t row = t - (W - 1) + j;
+            for (int j = 0; j < H; ++j) {
+                const int64_t src = pos - H + j;
+                const int64_t row = t - H + j;
                 if (src < 0) continue;
-                if (row >= m_qs) { m_tap[j] = kTapIntra; continue; }
+                if (row >= m_qs) { m_tblk[j] = kTapIntra; continue; }
                 const int64_t lblk = src / p.block_size;
                 if (lblk >= p.max_blocks) continue;
                 const int64_t blk = p.bt[int64_t(r) * p.bt_sr + lblk];
                 if (blk < 0 || blk >= p.num_blocks) continue;
-                m_tap[j] = blk * p.block_size + src % p.block_size;
+                m_tblk[j] = int32_t(blk);
+                m_tn[j] = int32_t(src % p.block_size);
             }
         }
     }
 
+    // x rows of the tile (and its width-1 predecessors), out rows of the tile
+    const int64_t xbase = tile_start >= H ? tile_start - H : 0;
+    const __amdgpu_buffer_rsrc_t xr =
+        rsrc(p.x + xbase * p.x_st, (p.T - xbase - 1) * p.x_st * 2 + int64_t(p.C) * 2);
+    const __amdgpu_buffer_rsrc_t orr =
+        rsrc(p.out + tile_start * p.o_st, (p.T - tile_start - 1) * p.o_st * 2 + int64_t(p.C) * 2);
+
     // Previous width-1 rows of x for the tile's first tokens; rows before
     // the first token's request are never an intra tap of this tile.
     const int64_t qs0 = readlane64(m_qs, 0);
-    float win[W - 1][kVec];
+    u32x2 win[H];
 #pragma unroll
-    for (int k = 0; k < W - 1; ++k) {
-        const int64_t row = tile_start - (W - 1) + k;
-        if (row >= 0 && row >= qs0) {
-            const u32x4 v = ld8_partial(p.x + row * p.x_st + cc, nv);
-            unpack8(v, win[k]);
-        } else {
-#pragma unroll
-            for (int ch = 0; ch < kVec; ++ch) win[k][ch] = 0.0f;
-        }
+    for (int k = 0; k < H; ++k) {
+        const int64_t row = tile_start - H + k;
+        win[k] = (row >= 0 && row >= qs0) ? ld8<kNt>(xr, xoff, (row - xbase) * p.x_st * 2)
+                                          : u32x2{0u, 0u};
     }
-    // Lanes past the last channel (nv == 0) stay active: they may hold token
-    // metadata that the loop below reads with readlane.  Their memory
-    // accesses are empty (nv == 0).
-    for (int u0 = 0; u0 < n_tok; u0 += kUnroll) {
-        u32x4 xv[kUnroll];
-        u32x4 g[kUnroll][W - 1];
-        int64_t taps[kUnroll][W - 1];
+
+    for (int u0 = 0; u0 < n_tok; u0 += kPagedUnroll) {
+        u32x2 xv[kPagedUnroll];
+        u32x2 g[kPagedUnroll][H];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kPagedUnroll; ++u) {
             if (u0 + u < n_tok) {
                 const int64_t t = tile_start + u0 + u;
-                xv[u] = ld8_partial(p.x + t * p.x_st + cc, nv);
+                xv[u] = ld8<kNt>(xr, xoff, (t - xbase) * p.x_st * 2);
 #pragma unroll
-                for (int j = 0; j < W - 1; ++j) {
-                    taps[u][j] = readlane64(m_tap[j], u0 + u);
-                    if (taps[u][j] >= 0) {
-                        const int64_t blk = taps[u][j] / p.block_size;
-                        const int64_t n = taps[u][j] % p.block_size;
-                        g[u][j] = ld8_partial(p.cache + blk * p.c_sb + n * p.c_sn + lane_off, nv);
+                for (int j = 0; j < H; ++j) {
+                    const int32_t blk = __builtin_amdgcn_readlane(m_tblk[j], u0 + u);
+                    g[u][j] = u32x2{0u, 0u};
+                    if (blk >= 0) {
+                        const int32_t n = __builtin_amdgcn_readlane(m_tn[j], u0 + u);
+                        const __amdgpu_buffer_rsrc_t cr = rsrc(p.cache + int64_t(blk) * p.c_sb, p.c_sb * 2);
+                        g[u][j] = ld8<0>(cr, coff, int64_t(n) * p.c_sn * 2);
                     }
                 }
             }
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kPagedUnroll; ++u) {
             if (u0 + u < n_tok) {
                 const int uu = u0 + u;
                 const int64_t t = tile_start + uu;
-                const int64_t slot = readlane64(m_slot, uu);
                 const bool pad = __builtin_amdgcn_readlane(m_pad, uu) != 0;
-                float xf[kVec], o[kVec];
-                unpack8(xv[u], xf);
+                float o[kPCpl];
                 if (!pad) {
-                    const int64_t blk = slot / p.block_size;
-                    if (blk < p.num_blocks)
-                        st8_partial(p.cache + blk * p.c_sb + (slot % p.block_size) * p.c_sn + lane_off,
-                                    xv[u], nv, false);
-#pragma unroll
-                    for (int ch = 0; ch < kVec; ++ch) o[ch] = bf[ch];
-#pragma unroll
-                    for (int j = 0; j < W - 1; ++j) {
-                        if (taps[u][j] == kTapIntra) {
-#pragma unroll
-                            for (int ch = 0; ch < kVec; ++ch) o[ch] = __builtin_fmaf(wf[j][ch], win[j][ch], o[ch]);
-                        } else if (taps[u][j] >= 0) {
-                            float gf[kVec];
-                            unpack8(g[u][j], gf);
-#pragma unroll
-                            for (int ch = 0; ch < kVec; ++ch) o[ch] = __builtin_fmaf(wf[j][ch], gf[ch], o[ch]);
-                        }
+                    const int32_t sblk = __builtin_amdgcn_readlane(m_sblk, uu);
+                    if (sblk >= 0 && active) {
+                        const int32_t sn = __builtin_amdgcn_readlane(m_sn, uu);
+                        const __amdgpu_buffer_rsrc_t cr = rsrc(p.cache + int64_t(sblk) * p.c_sb, p.c_sb * 2);
+                        st8<0>(cr, coff, int64_t(sn) * p.c_sn * 2, xv[u]);
                     }
+                    // the taps' input rows: a window row, a cached row or zero
+                    u32x2 in[W];
 #pragma unroll
-                    for (int ch = 0; ch < kVec; ++ch) o[ch] = __builtin_fmaf(wf[W - 1][ch], xf[ch], o[ch]);
+                    for (int j = 0; j < H; ++j)
+                        in[j] = __builtin_amdgcn_readlane(m_tblk[j], uu) == kTapIntra ? win[j] : g[u][j];
+                    in[H] = xv[u];
+#pragma unroll
+                    for (int ch = 0; ch < kPCpl; ++ch) {
+                        float acc = bf[ch];
+#pragma unroll
+                        for (int q = 0; q < W / 2; ++q)
+                            acc = dot2(cross_pair(in[2 * q], in[2 * q + 1], ch), wp[q][ch], acc);
+                        if constexpr (W & 1) {
+                            const uint32_t d = (ch >> 1) ? xv[u].y : xv[u].x;
+                            acc = __builtin_fmaf(wl[ch], (ch & 1) ? bf_hi(d) : bf_lo(d), acc);
+                        }
+                        o[ch] = acc;
+                    }
                 } else {
 #pragma unroll
-                    for (int ch = 0; ch < kVec; ++ch) o[ch] = 0.0f;
+                    for (int ch = 0; ch < kPCpl; ++ch) o[ch] = 0.0f;
                 }
 #pragma unroll
-                for (int ch = 0; ch < kVec; ++ch) {
+                for (int ch = 0; ch < kPCpl; ++ch) {
                     o[ch] = act<SILU>(o[ch]);
-                    if constexpr (RESID) o[ch] += xf[ch];
+                    if constexpr (RESID) {
+                        const uint32_t d = (ch >> 1) ? xv[u].y : xv[u].x;
+                        o[ch] += (ch & 1) ? bf_hi(d) : bf_lo(d);
+                    }
                 }
-                st8_partial(p.out + t * p.o_st + cc, pack8(o), nv, true);
+                if (active)
+                    st8<kNt>(orr, xoff, (t - tile_start) * p.o_st * 2,
+                             u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
 #pragma unroll
-                for (int k = 0; k + 1 < W - 1; ++k)
-#pragma unroll
-                    for (int ch = 0; ch < kVec; ++ch) win[k][ch] = win[k + 1][ch];
-#pragma unroll
-                for (int ch = 0; ch < kVec; ++ch) win[W - 2][ch] = xf[ch];
+                for (int k = 0; k + 1 < H; ++k) win[k] = win[k + 1];
+                win[H - 1] = xv[u];
             }
         }
     }

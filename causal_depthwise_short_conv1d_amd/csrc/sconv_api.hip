@@ -13,6 +13,7 @@ using namespace sconv;
 namespace {
 
 constexpr int kVersionMajor = 1;
+constexpr int kMaxWidthHistory = SCONV_MAX_WIDTH - 1;
 constexpr int kVersionMinor = 0;
 
 // Byte range [lo, hi) covered by a strided bf16 tensor; empty when a size is 0.
@@ -53,10 +54,11 @@ bool tokmajor_ok(int64_t sd, int64_t st, int64_t dim, int64_t T) {
     return st == 1 && (dim == 1 || sd == T);
 }
 
-// Tokens per channel-contiguous wave tile: enough tiles for ~16 waves per
-// CU, never fewer than 32 tokens (halo re-reads stay under 10%).
+// Tokens per channel-contiguous wave tile: enough tiles for ~32 waves per
+// CU (a full occupancy of the 256 CUs), never fewer than 32 tokens (halo
+// re-reads stay under 10%), never more than 256.
 int32_t chanlast_tile(int64_t T, int32_t n_slabs) {
-    const int64_t target_waves = 256 * 16;
+    const int64_t target_waves = 256 * 32;
     int64_t bt = (T * n_slabs + target_waves - 1) / target_waves;
     bt = (bt + 15) / 16 * 16;
     if (bt < 32) bt = 32;
@@ -152,6 +154,15 @@ int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
         p.dim = dim;
         p.n_slabs = (dim + kClSlab - 1) / kClSlab;
         p.bt = chanlast_tile(T, p.n_slabs);
+        // one descriptor spans a tile's rows (plus the spilled head) and one
+        // state line
+        const int64_t row_span = int64_t(p.bt + 2 * kMaxWidthHistory) *
+                                     (x_stride_tok > o_stride_tok ? x_stride_tok : o_stride_tok) * 2 +
+                                 int64_t(dim) * 2;
+        const int64_t line_span =
+            conv_states ? ((int64_t(dim) - 1) * cs_stride_dim + int64_t(width - 2) * cs_stride_tok + 1) * 2
+                        : 0;
+        if (row_span >= kMaxDescriptorSpan || line_span >= kMaxDescriptorSpan) return SCONV_ERR_SHAPE;
         p.n_tiles = int32_t((T + p.bt - 1) / p.bt);
         if (uint64_t(p.n_tiles) * uint64_t(p.n_slabs) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;
         return launch_status(launch_fwd_chanlast(p, width, silu, stream));
@@ -308,7 +319,12 @@ int sconv_paged_fused(const void *x, int64_t x_stride_tok, const void *weight,
     p.bt_sr = bt_stride_req;
     p.max_blocks = block_table ? max_blocks : 0;
     p.T = num_tokens;
-    p.n_slabs = int32_t((C + kSlab - 1) / kSlab);
+    p.n_slabs = int32_t((C + kPagedSlab - 1) / kPagedSlab);
+    // one descriptor spans a tile's rows, another one cache block
+    const int64_t row_span = int64_t(kPagedBT + SCONV_MAX_WIDTH) *
+                                 (x_stride_tok > o_stride_tok ? x_stride_tok : o_stride_tok) * 2 + C * 2;
+    if (row_span >= kMaxDescriptorSpan || c_stride_blk * 2 >= kMaxDescriptorSpan)
+        return SCONV_ERR_SHAPE;
     p.n_tiles = int32_t((num_tokens + kPagedBT - 1) / kPagedBT);
     if (uint64_t(p.n_tiles) * uint64_t(p.n_slabs) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;
     return launch_status(launch_paged_fused(p, width, activation == SCONV_ACT_SILU,

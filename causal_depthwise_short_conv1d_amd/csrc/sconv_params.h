@@ -134,6 +134,10 @@ constexpr int kCpl = 4;                          // channels per lane, channel-c
 constexpr int kClSlab = kWaveSize * kCpl;        // channels per wave there (256)
 constexpr int kPagedWavesPerBlock = 4;
 constexpr int kPagedBT = 16;                     // tokens per paged wave tile
+constexpr int kPagedSlab = 256;                  // channels per paged wave (4 per lane)
+// Buffer-descriptor offsets are 32-bit: rows, state lines and cache blocks
+// reached through one descriptor must span less than this many bytes.
+constexpr int64_t kMaxDescriptorSpan = int64_t(1) << 31;
 constexpr int kQslLdsMax = 2048;                 // qsl entries staged in LDS
 
 }  // namespace sconv
