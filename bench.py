@@ -34,7 +34,7 @@ HEADLINE = dict(dim=8192, T=14807, width=4)
 KERNEL_SOURCES = ["causal_depthwise_short_conv1d_amd/csrc/fwd_tokmajor.hip",
                   "causal_depthwise_short_conv1d_amd/csrc/sconv_device.h",
                   "causal_depthwise_short_conv1d_amd/csrc/sconv_params.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_tokmajor_dim8192_T14807_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_tok_long_dim8192_T14807_traffic.json")
 
 
 def log(*a):
@@ -178,7 +178,7 @@ def main():
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "fwd_tokmajor_kernel<4,true>",
+                     "traffic": traffic, "kernel": "fwd_tok_long_kernel<4,true>",
                      "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_us": round(kern_ms * 1e3, 2)},
     }
