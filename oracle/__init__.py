@@ -24,7 +24,7 @@ _SRC = os.path.join(_HERE, "sconv_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-__all__ = ["build", "fwd_varlen", "update_decode", "paged", "seq_metadata",
+__all__ = ["build", "fwd_varlen", "update_decode", "update_general", "paged", "seq_metadata",
            "bf16_from_f64", "f64_from_bf16", "silu"]
 
 
@@ -60,11 +60,16 @@ def _load():
     lib.oracle_update_decode.argtypes = [
         P, I64, I64, I64, P, I64, I64, P, P, I64, I64, I64, I64, P,
         I32, I32, I32, I32, I32, I32, P, I64, I64, I64]
+    lib.oracle_update_general.argtypes = [
+        P, I64, I64, I64, P, I64, I64, P, P, I64, I64, I64, I64, I32, P, P, P,
+        P, I64, I64, I64, I64, P, I64, I64, I32, I32, I32, I32, I32, I32,
+        P, I64, I64, I64]
     lib.oracle_paged.argtypes = [
         P, I64, P, I64, I64, P, P, I64, I64, I64, I64, I32, I32, I32, I32,
         P, P, P, I32, P, I64, I32, I64, I32, I32, I32, P, I64]
     lib.oracle_seq_metadata.argtypes = [P, I32, I64, I64, P, P]
-    for f in (lib.oracle_fwd_varlen, lib.oracle_update_decode, lib.oracle_paged,
+    for f in (lib.oracle_fwd_varlen, lib.oracle_update_decode, lib.oracle_update_general,
+              lib.oracle_paged,
               lib.oracle_seq_metadata):
         f.restype = ctypes.c_int
     _lib = lib
@@ -157,6 +162,39 @@ def update_decode(x, conv_state, weight, bias, out, cache_indices=None,
         _act(activation), pad_slot_id,
         _ptr(out, bf), *out.stride())
     _check(rc, "update_decode")
+
+
+def update_general(x, conv_state, weight, bias, out, cache_indices=None,
+                   cache_seqlens=None, num_accepted_tokens=None,
+                   intermediate=None, output_state_indices=None,
+                   activation=None, pad_slot_id: int = -1) -> None:
+    """Decode update with the speculative (num_accepted_tokens,
+    intermediate, output_state_indices) or ring-buffer (cache_seqlens)
+    options.  x / out: (batch, dim, seqlen) bf16 (out may be x);
+    conv_state: (lines, dim, state_len) bf16; intermediate:
+    (batch, steps, dim, width-1) bf16; output_state_indices: (batch, seqlen)
+    int32.  Everything is updated in place."""
+    lib = _load()
+    batch, dim, seqlen = x.shape
+    width = weight.shape[1]
+    bf = torch.bfloat16
+    inter = intermediate
+    osi = output_state_indices
+    if osi is not None and (osi.dtype != torch.int32 or osi.dim() != 2):
+        raise TypeError("output_state_indices must be a 2-D int32 tensor")
+    rc = lib.oracle_update_general(
+        _ptr(x, bf), *x.stride(),
+        _ptr(weight, bf), weight.stride(0), weight.stride(1),
+        _ptr(bias, bf),
+        _ptr(conv_state, bf), *conv_state.stride(), conv_state.shape[0],
+        conv_state.shape[2],
+        _ptr1d(cache_indices, torch.int32), _ptr1d(cache_seqlens, torch.int32),
+        _ptr1d(num_accepted_tokens, torch.int32),
+        _ptr(inter, bf), *(inter.stride() if inter is not None else (0, 0, 0, 0)),
+        _ptr(osi, torch.int32), *(osi.stride() if osi is not None else (0, 0)),
+        batch, dim, seqlen, width, _act(activation), pad_slot_id,
+        _ptr(out, bf), *out.stride())
+    _check(rc, "update_general")
 
 
 def paged(x, weight, bias, cache, positions, slot_mapping, query_start_loc,

@@ -219,6 +219,146 @@ int oracle_update_decode(const uint16_t *x, int64_t x_sb, int64_t x_sd, int64_t 
     return 0;
 }
 
+/*
+ * General decode update with the speculative-decoding and circular-buffer
+ * options of the same page [P1 causal_conv1d_update /
+ * _causal_conv1d_update_kernel: num_accepted_tokens, intermediate_conv_window,
+ * output_state_indices; cache_seqlens as its docstring describes it].
+ *
+ * x           : logical [batch][dim][seqlen]
+ * conv_state  : logical [num_lines][dim][state_len], state_len >= width-1
+ * cache_seqlens : [batch] or NULL.  Given: the line is a ring of state_len
+ *          inputs; input number n of the stream sits at slot n mod state_len
+ *          and cache_seqlens[b] inputs have been seen so far.
+ * num_accepted : [batch] or NULL.  Given (speculative decoding): the history
+ *          window starts at column num_accepted[b] - 1 of the line.
+ * inter   : logical [batch][steps >= seqlen][dim][width-1] or NULL; element
+ *          (b, t, c, k) at inter[b*i_sb + t*i_st + c*i_sd + k*i_sk].
+ * out_idx : logical [batch][seqlen] line numbers or NULL, element (b, t) at
+ *          out_idx[b*oi_sb + t*oi_st].
+ *
+ * For entry b and channel c, with W = width:
+ *   h[k] (k < W-1), the history:
+ *     ring:  state[(cache_seqlens[b] - (W-1) + k) mod state_len]
+ *     else:  state[off + k], off = num_accepted ? num_accepted[b] - 1 : 0
+ *   u = h ++ x[b][c][0..seqlen), out[t] = act(bias + sum_j w[j] u[t+j])
+ *   win_t = u[t+1 .. t+W-1], the W-1 inputs that end with x[t]
+ *   inter given:    inter[b][t][c][k] = win_t[k]
+ *   out_idx given:  state[out_idx[b][t]][c][k] = win_t[k] for every t whose
+ *                   index lies in [0, num_lines)
+ *   state update in place, only when neither inter nor out_idx is given:
+ *     ring:  x[t] goes to slot (cache_seqlens[b] + t) mod state_len (for the
+ *            last min(seqlen, state_len) tokens: later tokens overwrite)
+ *     speculative:  state[k] = u[1 + k] for k < W-2+seqlen, i.e. the history
+ *            minus its oldest input, then all of x (the page's comment: the
+ *            state becomes history2..historyM, draft1..draftN, and the next
+ *            call's num_accepted picks the window that ends with the last
+ *            accepted draft)
+ *     plain: state[k] = u[seqlen + k] for k < W-1 (the decode rule above)
+ * Readings (all defensive, the page leaves them open): an entry whose line is
+ * pad_slot_id or out of range, whose num_accepted[b] - 1 + W-1 exceeds
+ * state_len or is below W-1 (num_accepted < 1), or whose cache_seqlens[b] is
+ * negative, is skipped entirely; the ring option excludes the three
+ * speculative ones; without inter/out_idx a speculative call needs
+ * state_len >= W-2+seqlen.  Every read of an entry happens before its writes,
+ * so out may be x and out_idx may name the entry's own line.
+ */
+int oracle_update_general(const uint16_t *x, int64_t x_sb, int64_t x_sd, int64_t x_st,
+                          const uint16_t *weight, int64_t w_sd, int64_t w_sw,
+                          const uint16_t *bias,
+                          uint16_t *conv_state, int64_t cs_sl, int64_t cs_sd,
+                          int64_t cs_st, int64_t num_lines, int32_t state_len,
+                          const int32_t *cache_indices, const int32_t *cache_seqlens,
+                          const int32_t *num_accepted,
+                          uint16_t *inter, int64_t i_sb, int64_t i_st, int64_t i_sd,
+                          int64_t i_sk,
+                          const int32_t *out_idx, int64_t oi_sb, int64_t oi_st,
+                          int32_t batch, int32_t dim, int32_t seqlen, int32_t width,
+                          int32_t silu, int32_t pad_slot_id,
+                          uint16_t *out, int64_t o_sb, int64_t o_sd, int64_t o_st)
+{
+    if (width < 1 || width > ORACLE_MAX_WIDTH || dim < 0 || batch < 0 || seqlen < 0 ||
+        state_len < width - 1)
+        return -1;
+    const int ring = cache_seqlens != NULL;
+    const int spec = num_accepted != NULL;
+    const int scatter = inter != NULL || out_idx != NULL;
+    if (ring && (spec || scatter || state_len < 1))
+        return -1;
+    if (spec && !scatter && state_len < width - 2 + seqlen)
+        return -1;
+    const int hist = width - 1;
+    uint16_t *u = (uint16_t *)malloc((size_t)(hist + seqlen + 1) * sizeof(uint16_t));
+    if (!u)
+        return -1;
+    for (int32_t b = 0; b < batch; ++b) {
+        const int64_t line = cache_indices ? (int64_t)cache_indices[b] : (int64_t)b;
+        if (cache_indices && line == pad_slot_id)
+            continue;
+        if (line < 0 || line >= num_lines)
+            continue;
+        int64_t off = 0;
+        if (spec) {
+            off = (int64_t)num_accepted[b] - 1;
+            if (off < 0 || off + hist > state_len)
+                continue;
+        }
+        if (ring && cache_seqlens[b] < 0)
+            continue;
+        for (int32_t c = 0; c < dim; ++c) {
+            uint16_t *row = conv_state + line * cs_sl + c * cs_sd;
+            for (int k = 0; k < hist; ++k) {
+                int64_t col = off + k;
+                if (ring) {
+                    col = ((int64_t)cache_seqlens[b] - hist + k) % state_len;
+                    if (col < 0)
+                        col += state_len;
+                }
+                u[k] = row[col * cs_st];
+            }
+            for (int32_t t = 0; t < seqlen; ++t)
+                u[hist + t] = x[b * x_sb + c * x_sd + t * x_st];
+            for (int32_t t = 0; t < seqlen; ++t) {
+                double acc = bias ? oracle_bf16_to_f64(bias[c]) : 0.0;
+                for (int j = 0; j < width; ++j)
+                    acc += oracle_bf16_to_f64(weight[c * w_sd + j * w_sw]) *
+                           oracle_bf16_to_f64(u[t + j]);
+                if (silu)
+                    acc = oracle_silu(acc);
+                out[b * o_sb + c * o_sd + t * o_st] = oracle_f64_to_bf16(acc);
+            }
+            for (int32_t t = 0; t < seqlen; ++t) {
+                if (inter)
+                    for (int k = 0; k < hist; ++k)
+                        inter[b * i_sb + t * i_st + c * i_sd + k * i_sk] = u[t + 1 + k];
+                if (out_idx) {
+                    const int64_t dst = out_idx[b * oi_sb + t * oi_st];
+                    if (dst >= 0 && dst < num_lines)
+                        for (int k = 0; k < hist; ++k)
+                            conv_state[dst * cs_sl + c * cs_sd + k * cs_st] = u[t + 1 + k];
+                }
+            }
+            if (scatter)
+                continue;
+            if (ring) {
+                const int32_t first = seqlen > state_len ? seqlen - state_len : 0;
+                for (int32_t t = first; t < seqlen; ++t) {
+                    const int64_t col = ((int64_t)cache_seqlens[b] + t) % state_len;
+                    row[col * cs_st] = u[hist + t];
+                }
+            } else if (spec) {
+                for (int k = 0; k < hist - 1 + seqlen; ++k)
+                    row[k * cs_st] = u[1 + k];
+            } else {
+                for (int k = 0; k < hist; ++k)
+                    row[k * cs_st] = u[seqlen + k];
+            }
+        }
+    }
+    free(u);
+    return 0;
+}
+
 /* ---------------------------------------------------- paged fused step -- */
 
 /* Request owning token row t: the largest j in [0, num_reqs) with

@@ -33,6 +33,7 @@ PREFILL_SWEEP_DIM4096 = dict(dim=4096, Ts=(1, 128, 256, 514, 1024), width=4)
 LONG_PREFILL_DIM8192 = dict(dim=8192, Ts=(4195, 11027, 14807), width=4)
 VARLEN_BATCH = dict(dim=8192, nseq=64, max_len=2048, num_lines=256, n_pad=4,
                     widths=(2, 3, 4, 5))
+SPEC_DECODE = dict(batch=64, dim=8192, width=4, seqlen=4, num_lines=256, n_pad=4)
 PAGED_MIXED = dict(H=32, ws=128, N=16, D=512, off_s=128, num_blocks=4096,
                    width=4, n_decode=32, n_prefill=8, chunk=512, max_pos=8191,
                    pad_frac=0.05)
@@ -157,6 +158,87 @@ def decode_batch(batch: int = 1, dim: int = 4096, width: int = 4,
     state = _draw((num_lines, dim, width - 1), g, device, values)
     return dict(x=x, weight=weight, bias=bias, conv_state=state,
                 cache_indices=lines.to(device))
+
+
+def spec_decode_batch(batch: int = 64, dim: int = 8192, width: int = 4,
+                      seqlen: int = 4, state_len: int | None = None, seed: int = 0,
+                      num_lines: int = 256, n_pad: int = 0, mode: str = "roll",
+                      device="cpu", values: str = "normal",
+                      with_bias: bool = True, state_layout: str = "dim_contig") -> dict:
+    """A speculative-decoding verify step (tokenspeed causal_conv1d.py,
+    causal_conv1d_update with num_accepted_tokens): every entry feeds seqlen
+    tokens whose history window starts at column num_accepted - 1 of its
+    state line.  num_accepted is uniform over the values that keep the window
+    inside the line.  mode "roll": the state line (default length
+    width-2+seqlen) is rewritten in place; mode "scatter": the state lines
+    are width-1 long and the call saves per-step windows into `intermediate`
+    (batch, seqlen, dim, width-1) and into the lines named by
+    `output_state_indices` (batch, seqlen), distinct lines outside the ones
+    being read, about a quarter of them -1 (no write).  x is
+    channel-contiguous per token and, by default, so is the state
+    ("dim_contig", unit stride along dim, as the page asks of it)."""
+    if mode not in ("roll", "scatter"):
+        raise ValueError(f"unknown mode {mode!r}")
+    hist = width - 1
+    if state_len is None:
+        state_len = hist - 1 + seqlen if mode == "roll" else hist
+    state_len = max(state_len, hist)
+    g_host = _gen(seed, "cpu")
+    perm = torch.randperm(num_lines, generator=g_host).to(torch.int32)
+    lines = perm[:batch].clone()
+    if n_pad:
+        lines[torch.randperm(batch, generator=g_host)[:n_pad]] = PAD_SLOT_ID
+    hi = state_len - hist + 1
+    num_acc = torch.randint(1, hi + 1, (batch,), generator=g_host).to(torch.int32)
+    osi = None
+    if mode == "scatter":
+        free = perm[batch:]
+        if free.numel() < batch * seqlen:
+            raise ValueError("need num_lines >= batch * (seqlen + 1) for scatter mode")
+        osi = free[:batch * seqlen].reshape(batch, seqlen).clone()
+        osi[torch.rand(batch, seqlen, generator=g_host) < 0.25] = -1
+
+    g = _gen(seed + 1, device)
+    x = _draw((batch, seqlen, dim), g, device, values).permute(0, 2, 1)
+    weight = _draw((dim, width), g, device, values)
+    bias = _draw((dim,), g, device, values) if with_bias else None
+    if state_layout == "dim_contig":
+        state = _draw((num_lines, state_len, dim), g, device, values).permute(0, 2, 1)
+    elif state_layout == "tok_contig":
+        state = _draw((num_lines, dim, state_len), g, device, values)
+    else:
+        raise ValueError(f"unknown state layout {state_layout!r}")
+    out = dict(x=x, weight=weight, bias=bias, conv_state=state,
+               cache_indices=lines.to(device), num_accepted_tokens=num_acc.to(device),
+               state_len=state_len)
+    if mode == "scatter":
+        out["intermediate"] = torch.zeros(batch, seqlen, dim, hist, dtype=BF16, device=device)
+        out["output_state_indices"] = osi.to(device)
+    return out
+
+
+def ring_decode_batch(batch: int = 64, dim: int = 8192, width: int = 4,
+                      seqlen: int = 1, state_len: int = 8, seed: int = 0,
+                      num_lines: int = 256, n_pad: int = 0, max_seen: int = 64,
+                      device="cpu", values: str = "normal",
+                      with_bias: bool = True) -> dict:
+    """A decode step on ring-buffer states (the cache_seqlens option of
+    tokenspeed causal_conv1d_update's docstring): each line holds state_len
+    inputs, input n of a stream at column n mod state_len, and
+    cache_seqlens counts the inputs seen so far (uniform in [0, max_seen])."""
+    g_host = _gen(seed, "cpu")
+    lines = torch.randperm(num_lines, generator=g_host)[:batch].to(torch.int32)
+    if n_pad:
+        lines[torch.randperm(batch, generator=g_host)[:n_pad]] = PAD_SLOT_ID
+    seen = torch.randint(0, max_seen + 1, (batch,), generator=g_host).to(torch.int32)
+    g = _gen(seed + 1, device)
+    x = _draw((batch, seqlen, dim), g, device, values).permute(0, 2, 1)
+    weight = _draw((dim, width), g, device, values)
+    bias = _draw((dim,), g, device, values) if with_bias else None
+    state = _draw((num_lines, dim, state_len), g, device, values)
+    return dict(x=x, weight=weight, bias=bias, conv_state=state,
+                cache_indices=lines.to(device), cache_seqlens=seen.to(device),
+                state_len=state_len)
 
 
 def paged_batch(H: int = 32, ws: int = 128, N: int = 16, D: int = 512,
