@@ -9,6 +9,8 @@ binding raises.
 Entry points (same names as the C ABI):
   conv1d_fwd_varlen    -- varlen prefill with per-sequence conv state
   conv1d_update_decode -- decode update (state shift), in place allowed
+  conv1d_update        -- decode update with speculative-decoding and
+                          ring-buffer options
   sconv_paged_fused    -- paged sliding-window cache insert + conv
 """
 from __future__ import annotations
@@ -18,7 +20,8 @@ import os
 
 import torch
 
-__all__ = ["conv1d_fwd_varlen", "conv1d_update_decode", "sconv_paged_fused", "new_output",
+__all__ = ["conv1d_fwd_varlen", "conv1d_update_decode", "conv1d_update", "sconv_paged_fused",
+           "new_output",
            "SconvError", "library_path", "load_library", "exported_symbols",
            "version", "status_string"]
 
@@ -64,10 +67,15 @@ def load_library(path: str | None = None):
     lib.conv1d_update_decode.argtypes = [
         P, I64, I64, I64, P, I64, P, P, I64, I64, I64, I64, P,
         I32, I32, I32, I32, I32, I32, P, I64, I64, I64, P]
+    lib.conv1d_update.argtypes = [
+        P, I64, I64, I64, P, I64, P, P, I64, I64, I64, I64, I32, P, P, P,
+        P, I64, I64, I64, I64, P, I64, I64,
+        I32, I32, I32, I32, I32, I32, P, I64, I64, I64, P]
     lib.sconv_paged_fused.argtypes = [
         P, I64, P, I64, P, P, I64, I64, I64, I64, I32, I32, I32, I32, I32,
         P, P, P, I32, P, I64, I32, I64, I32, I32, I32, P, I64, P]
-    for f in (lib.conv1d_fwd_varlen, lib.conv1d_update_decode, lib.sconv_paged_fused):
+    for f in (lib.conv1d_fwd_varlen, lib.conv1d_update_decode, lib.conv1d_update,
+              lib.sconv_paged_fused):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -76,7 +84,7 @@ def load_library(path: str | None = None):
 
 def exported_symbols() -> list[str]:
     return ["sconv_status_string", "sconv_version", "conv1d_fwd_varlen",
-            "conv1d_update_decode", "sconv_paged_fused"]
+            "conv1d_update_decode", "conv1d_update", "sconv_paged_fused"]
 
 
 def version() -> tuple[int, int]:
@@ -225,6 +233,65 @@ def conv1d_update_decode(x, conv_state, weight, bias=None, activation=None,
     )
     with torch.cuda.device(dev):
         _call("conv1d_update_decode", *args, _stream(dev))
+    if out is not None:
+        return out
+    return ov.squeeze(-1) if squeeze else ov
+
+
+def conv1d_update(x, conv_state, weight, bias=None, activation=None, cache_indices=None,
+                  cache_seqlens=None, num_accepted_tokens=None, intermediate=None,
+                  output_state_indices=None, pad_slot_id: int = -1, out=None):
+    """Decode update with the speculative-decoding options
+    (num_accepted_tokens (batch,) int32; intermediate (batch, steps, dim,
+    width-1) bf16; output_state_indices (batch, seqlen) int32) or ring-buffer
+    states (cache_seqlens (batch,) int32).  x: (batch, dim) or
+    (batch, dim, seqlen) bf16; conv_state (lines, dim, state_len) bf16,
+    state_len >= width-1.  Returns out, which may be x itself."""
+    dev = x.device
+    squeeze = x.dim() == 2
+    xv = x.unsqueeze(-1) if squeeze else x
+    if out is not None:
+        ov = out.unsqueeze(-1) if out.dim() == 2 else out
+    else:
+        ov = torch.empty_like(xv)
+    batch, dim, seqlen = xv.shape
+    width = weight.shape[1]
+    if weight.dim() != 2 or weight.shape[0] != dim or weight.stride(1) != 1:
+        raise ValueError("weight must be (dim, width) with unit width stride")
+    if conv_state.dim() != 3 or conv_state.shape[1] != dim:
+        raise ValueError("conv_state must be (lines, dim, state_len)")
+    if bias is not None and (bias.shape != (dim,) or bias.stride(0) != 1):
+        raise ValueError("bias must be a contiguous (dim,) tensor")
+    if ov.shape != xv.shape:
+        raise ValueError("out must have x's shape")
+    inter = intermediate
+    if inter is not None and (inter.dim() != 4 or inter.shape[0] < batch or
+                              inter.shape[1] < seqlen or inter.shape[2] != dim or
+                              inter.shape[3] != width - 1):
+        raise ValueError("intermediate must be (batch, >= seqlen, dim, width-1)")
+    osi = output_state_indices
+    if osi is not None:
+        if osi.dim() != 2 or osi.shape[0] < batch or osi.shape[1] < seqlen:
+            raise ValueError("output_state_indices must be (batch, >= seqlen)")
+        _dev(osi, torch.int32, "output_state_indices", dev)
+    bf = torch.bfloat16
+    args = (
+        _dev(xv, bf, "x", dev), *xv.stride(),
+        _dev(weight, bf, "weight", dev), weight.stride(0),
+        _dev(bias, bf, "bias", dev),
+        _dev(conv_state, bf, "conv_state", dev), *conv_state.stride(), conv_state.shape[0],
+        conv_state.shape[2],
+        _index(cache_indices, torch.int32, "cache_indices", dev, batch),
+        _index(cache_seqlens, torch.int32, "cache_seqlens", dev, batch),
+        _index(num_accepted_tokens, torch.int32, "num_accepted_tokens", dev, batch),
+        _dev(inter, bf, "intermediate", dev), *(inter.stride() if inter is not None else (0,) * 4),
+        _dev(osi, torch.int32, "output_state_indices", dev),
+        *(osi.stride() if osi is not None else (0, 0)),
+        batch, dim, seqlen, width, _act(activation), pad_slot_id,
+        _dev(ov, bf, "out", dev), *ov.stride(),
+    )
+    with torch.cuda.device(dev):
+        _call("conv1d_update", *args, _stream(dev))
     if out is not None:
         return out
     return ov.squeeze(-1) if squeeze else ov

@@ -14,7 +14,7 @@ namespace {
 
 constexpr int kVersionMajor = 1;
 constexpr int kMaxWidthHistory = SCONV_MAX_WIDTH - 1;
-constexpr int kVersionMinor = 0;
+constexpr int kVersionMinor = 1;
 
 // Byte range [lo, hi) covered by a strided bf16 tensor; empty when a size is 0.
 struct Span {
@@ -188,41 +188,58 @@ int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
     return SCONV_ERR_STRIDE;
 }
 
-int conv1d_update_decode(const void *x, int64_t x_stride_seq, int64_t x_stride_dim,
-                         int64_t x_stride_tok, const void *weight, int64_t w_stride_dim,
-                         const void *bias, void *conv_state, int64_t cs_stride_line,
-                         int64_t cs_stride_dim, int64_t cs_stride_tok, int64_t num_cache_lines,
-                         const int32_t *cache_indices, int32_t batch, int32_t dim, int32_t seqlen,
-                         int32_t width, int32_t activation, int32_t pad_slot_id, void *out,
-                         int64_t o_stride_seq, int64_t o_stride_dim, int64_t o_stride_tok,
-                         hipStream_t stream) {
+int conv1d_update(const void *x, int64_t x_stride_seq, int64_t x_stride_dim,
+                  int64_t x_stride_tok, const void *weight, int64_t w_stride_dim,
+                  const void *bias, void *conv_state, int64_t cs_stride_line,
+                  int64_t cs_stride_dim, int64_t cs_stride_tok, int64_t num_cache_lines,
+                  int32_t state_len, const int32_t *cache_indices,
+                  const int32_t *cache_seqlens, const int32_t *num_accepted_tokens,
+                  void *intermediate, int64_t it_stride_seq, int64_t it_stride_step,
+                  int64_t it_stride_dim, int64_t it_stride_win,
+                  const int32_t *output_state_indices, int64_t osi_stride_seq,
+                  int64_t osi_stride_step, int32_t batch, int32_t dim, int32_t seqlen,
+                  int32_t width, int32_t activation, int32_t pad_slot_id, void *out,
+                  int64_t o_stride_seq, int64_t o_stride_dim, int64_t o_stride_tok,
+                  hipStream_t stream) {
     if (width < SCONV_MIN_WIDTH || width > SCONV_MAX_WIDTH) return SCONV_ERR_WIDTH;
     if (activation != SCONV_ACT_NONE && activation != SCONV_ACT_SILU) return SCONV_ERR_ARG;
+    const bool saved = intermediate || output_state_indices;
+    if (cache_seqlens && (num_accepted_tokens || saved)) return SCONV_ERR_ARG;
     if (batch < 0 || dim < 0 || seqlen < 0 || num_cache_lines < 0) return SCONV_ERR_SHAPE;
+    if (state_len < width - 1) return SCONV_ERR_SHAPE;
+    if (num_accepted_tokens && !saved && int64_t(state_len) < int64_t(width) - 2 + seqlen)
+        return SCONV_ERR_SHAPE;
     if (batch == 0 || dim == 0 || seqlen == 0) return SCONV_OK;
     if (!x || !weight || !conv_state || !out) return SCONV_ERR_NULL;
     if (x_stride_seq < 0 || x_stride_dim < 0 || x_stride_tok < 0 || o_stride_seq < 0 ||
         o_stride_dim < 0 || o_stride_tok < 0 || cs_stride_line < 0 || cs_stride_dim < 0 ||
-        cs_stride_tok < 0)
+        cs_stride_tok < 0 || it_stride_seq < 0 || it_stride_step < 0 || it_stride_dim < 0 ||
+        it_stride_win < 0 || osi_stride_seq < 0 || osi_stride_step < 0)
         return SCONV_ERR_STRIDE;
     if (w_stride_dim < width) return SCONV_ERR_STRIDE;
     if (num_cache_lines < 1 || (!cache_indices && num_cache_lines < batch)) return SCONV_ERR_SHAPE;
     if (!aligned(x, 2) || !aligned(out, 2) || !aligned(weight, 2) || !aligned(bias, 2) ||
-        !aligned(conv_state, 2) || !aligned(cache_indices, 4))
+        !aligned(conv_state, 2) || !aligned(intermediate, 2) || !aligned(cache_indices, 4) ||
+        !aligned(cache_seqlens, 4) || !aligned(num_accepted_tokens, 4) ||
+        !aligned(output_state_indices, 4))
         return SCONV_ERR_ALIGN;
     const uint64_t cblocks = (uint64_t(dim) + 255) / 256;
     if (cblocks * uint64_t(batch) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;
 
     const Span sx = span_of(x, {batch, dim, seqlen}, {x_stride_seq, x_stride_dim, x_stride_tok});
     const Span so = span_of(out, {batch, dim, seqlen}, {o_stride_seq, o_stride_dim, o_stride_tok});
-    const Span scs = span_of(conv_state, {num_cache_lines, dim, width - 1},
+    const Span scs = span_of(conv_state, {num_cache_lines, dim, state_len},
                              {cs_stride_line, cs_stride_dim, cs_stride_tok});
     const Span sw = span_of(weight, {dim, width}, {w_stride_dim, 1});
     const Span sbias = span_of(bias, {dim}, {1});
+    const Span sit = span_of(intermediate, {batch, seqlen, dim, width - 1},
+                             {it_stride_seq, it_stride_step, it_stride_dim, it_stride_win});
     const bool in_place = out == x && o_stride_seq == x_stride_seq &&
                           o_stride_dim == x_stride_dim && o_stride_tok == x_stride_tok;
     if ((!in_place && overlap(so, sx)) || overlap(so, scs) || overlap(so, sw) ||
-        overlap(so, sbias) || overlap(scs, sx) || overlap(scs, sw) || overlap(scs, sbias))
+        overlap(so, sbias) || overlap(scs, sx) || overlap(scs, sw) || overlap(scs, sbias) ||
+        overlap(sit, sx) || overlap(sit, so) || overlap(sit, scs) || overlap(sit, sw) ||
+        overlap(sit, sbias))
         return SCONV_ERR_ALIAS;
 
     UpdParams p;
@@ -243,11 +260,38 @@ int conv1d_update_decode(const void *x, int64_t x_stride_seq, int64_t x_stride_d
     p.cs_st = cs_stride_tok;
     p.num_lines = num_cache_lines;
     p.cache_idx = cache_indices;
+    p.ring_seen = cache_seqlens;
+    p.num_acc = num_accepted_tokens;
+    p.inter = static_cast<uint16_t *>(intermediate);
+    p.i_sb = it_stride_seq;
+    p.i_st = it_stride_step;
+    p.i_sd = it_stride_dim;
+    p.i_sk = it_stride_win;
+    p.out_idx = output_state_indices;
+    p.oi_sb = osi_stride_seq;
+    p.oi_st = osi_stride_step;
+    p.state_len = state_len;
     p.batch = batch;
     p.dim = dim;
     p.seqlen = seqlen;
     p.pad_slot_id = pad_slot_id;
-    return launch_status(launch_update_decode(p, width, activation == SCONV_ACT_SILU, stream));
+    return launch_status(launch_update(p, width, activation == SCONV_ACT_SILU, stream));
+}
+
+int conv1d_update_decode(const void *x, int64_t x_stride_seq, int64_t x_stride_dim,
+                         int64_t x_stride_tok, const void *weight, int64_t w_stride_dim,
+                         const void *bias, void *conv_state, int64_t cs_stride_line,
+                         int64_t cs_stride_dim, int64_t cs_stride_tok, int64_t num_cache_lines,
+                         const int32_t *cache_indices, int32_t batch, int32_t dim, int32_t seqlen,
+                         int32_t width, int32_t activation, int32_t pad_slot_id, void *out,
+                         int64_t o_stride_seq, int64_t o_stride_dim, int64_t o_stride_tok,
+                         hipStream_t stream) {
+    if (width < SCONV_MIN_WIDTH || width > SCONV_MAX_WIDTH) return SCONV_ERR_WIDTH;
+    return conv1d_update(x, x_stride_seq, x_stride_dim, x_stride_tok, weight, w_stride_dim, bias,
+                         conv_state, cs_stride_line, cs_stride_dim, cs_stride_tok,
+                         num_cache_lines, width - 1, cache_indices, nullptr, nullptr, nullptr,
+                         0, 0, 0, 0, nullptr, 0, 0, batch, dim, seqlen, width, activation,
+                         pad_slot_id, out, o_stride_seq, o_stride_dim, o_stride_tok, stream);
 }
 
 int sconv_paged_fused(const void *x, int64_t x_stride_tok, const void *weight,

@@ -89,6 +89,13 @@ struct UpdParams {
     int64_t cs_sl, cs_sd, cs_st;
     int64_t num_lines;
     const int32_t *cache_idx;
+    const int32_t *ring_seen;     // cache_seqlens: inputs seen per entry (ring states)
+    const int32_t *num_acc;       // num_accepted_tokens (speculative decoding)
+    uint16_t *inter;              // per-step windows [batch][steps][dim][width-1]
+    int64_t i_sb, i_st, i_sd, i_sk;
+    const int32_t *out_idx;       // per-step destination lines [batch][seqlen]
+    int64_t oi_sb, oi_st;
+    int32_t state_len;
     int32_t batch, dim, seqlen, pad_slot_id;
 };
 
@@ -119,7 +126,7 @@ struct PagedParams {
 // Launchers: each enqueues one kernel and returns hipGetLastError().
 hipError_t launch_fwd_tokmajor(const FwdTokParams &p, int width, bool silu, hipStream_t s);
 hipError_t launch_fwd_chanlast(const FwdClParams &p, int width, bool silu, hipStream_t s);
-hipError_t launch_update_decode(const UpdParams &p, int width, bool silu, hipStream_t s);
+hipError_t launch_update(const UpdParams &p, int width, bool silu, hipStream_t s);
 hipError_t launch_paged_fused(const PagedParams &p, int width, bool silu, bool residual,
                               hipStream_t s);
 

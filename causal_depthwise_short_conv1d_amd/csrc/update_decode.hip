@@ -1,13 +1,26 @@
 // Decode-time update: every batch entry feeds seqlen (usually 1) new tokens
-// that continue from its cached state, then the state is shifted to hold the
-// last width-1 inputs -- tokenspeed causal_conv1d.py, causal_conv1d_update /
-// _causal_conv1d_update_kernel (non-speculative path).
+// that continue from its cached state -- tokenspeed causal_conv1d.py,
+// causal_conv1d_update / _causal_conv1d_update_kernel, including the options
+// of that kernel and its docstring:
+//   * speculative decoding: num_accepted_tokens moves the start of the
+//     history window to column num_accepted - 1 of the state line; without
+//     saved windows the line is rewritten as the history minus its oldest
+//     input followed by every new input, so that the next call's acceptance
+//     count selects the window that ends with the last accepted token;
+//   * saved windows: the width-1 inputs that end with token t go to
+//     intermediate[b][t] and/or to the line output_state_indices[b][t]
+//     (then the state is not updated in place);
+//   * ring-buffer states (cache_seqlens): input n of a stream lives at column
+//     n mod state_len.
+// Without options the state becomes the last width-1 inputs of
+// history ++ x.
 //
 // The work is tiny (about 100 KiB at dim 4096) and latency-bound: one lane
-// per (entry, channel), all loads of a lane independent of each other, so a
-// launch costs one memory round trip plus the stores.  Each lane reads its
-// inputs before writing its outputs, which makes out == x (in place, as the
-// page computes) safe.
+// per (entry, channel); the per-entry option values are wave-uniform loads.
+// Each lane reads its history before writing any state and loads a group of
+// up to four inputs before storing their outputs, which makes out == x (in
+// place, as the page computes) and a saved window aimed at the entry's own
+// line safe.
 #include "sconv_device.h"
 
 namespace sconv {
@@ -15,53 +28,119 @@ namespace sconv {
 namespace {
 
 constexpr int kUpdBlock = 256;
+constexpr int kUpdGroup = 4;   // inputs loaded ahead of their outputs
 
 template <int W, bool SILU>
-__global__ __launch_bounds__(kUpdBlock) void update_decode_kernel(UpdParams p, uint32_t cblocks) {
+__global__ __launch_bounds__(kUpdBlock) void update_kernel(UpdParams p, uint32_t cblocks) {
+    constexpr int H = W - 1;
     const uint32_t b = blockIdx.x / cblocks;
     const int32_t c = int32_t((blockIdx.x % cblocks) * kUpdBlock + threadIdx.x);
     if (int32_t(b) >= p.batch || c >= p.dim) return;
     const int64_t line = p.cache_idx ? int64_t(p.cache_idx[b]) : int64_t(b);
     if ((p.cache_idx && line == p.pad_slot_id) || line < 0 || line >= p.num_lines) return;
 
-    uint16_t *st = p.cs + line * p.cs_sl + int64_t(c) * p.cs_sd;
-    uint16_t win[W - 1];
+    const int32_t L = p.state_len;
+    int32_t off = 0;     // first history column (speculative decoding)
+    int32_t rcol = 0;    // ring: column of the next input
+    if (p.num_acc) {
+        off = p.num_acc[b] - 1;
+        if (off < 0 || off > L - H) return;
+    }
+    if (p.ring_seen) {
+        const int32_t seen = p.ring_seen[b];
+        if (seen < 0) return;
+        rcol = seen % L;
+    }
+    const bool spec = p.num_acc != nullptr;
+    const bool ring = p.ring_seen != nullptr;
+    const bool saved = p.inter != nullptr || p.out_idx != nullptr;
+
+    uint16_t *row = p.cs + line * p.cs_sl + int64_t(c) * p.cs_sd;
+    uint16_t win[H];
 #pragma unroll
-    for (int k = 0; k < W - 1; ++k) win[k] = st[k * p.cs_st];
+    for (int k = 0; k < H; ++k) {
+        int32_t col = off + k;
+        if (ring) {
+            col = rcol - H + k;
+            if (col < 0) col += L;          // H <= L, so one wrap suffices
+        }
+        win[k] = row[int64_t(col) * p.cs_st];
+    }
     float wf[W];
 #pragma unroll
     for (int k = 0; k < W; ++k) wf[k] = bf_one(p.w[int64_t(c) * p.w_sd + k]);
     const float b0 = p.bias ? bf_one(p.bias[c]) : 0.0f;
 
+    // Speculative roll: the line restarts with the history minus its oldest
+    // input (the new inputs follow at columns H-1 onward).
+    if (spec && !saved) {
+#pragma unroll
+        for (int k = 0; k + 1 < H; ++k) row[int64_t(k) * p.cs_st] = win[k + 1];
+    }
+
     const uint16_t *xp = p.x + int64_t(b) * p.x_sb + int64_t(c) * p.x_sd;
     uint16_t *op = p.out + int64_t(b) * p.o_sb + int64_t(c) * p.o_sd;
-    for (int32_t t = 0; t < p.seqlen; ++t) {
-        const uint16_t xb = xp[int64_t(t) * p.x_st];
-        float acc = b0;
+    const int32_t ring_from = p.seqlen - L;    // ring: earlier inputs are overwritten anyway
+    for (int32_t t0 = 0; t0 < p.seqlen; t0 += kUpdGroup) {
+        uint16_t xv[kUpdGroup];
 #pragma unroll
-        for (int k = 0; k < W - 1; ++k) acc = __builtin_fmaf(wf[k], bf_one(win[k]), acc);
-        acc = __builtin_fmaf(wf[W - 1], bf_one(xb), acc);
-        op[int64_t(t) * p.o_st] = to_bf16(act<SILU>(acc));
+        for (int i = 0; i < kUpdGroup; ++i)
+            xv[i] = t0 + i < p.seqlen ? xp[int64_t(t0 + i) * p.x_st] : uint16_t(0);
 #pragma unroll
-        for (int k = 0; k + 1 < W - 1; ++k) win[k] = win[k + 1];
-        win[W - 2] = xb;
+        for (int i = 0; i < kUpdGroup; ++i) {
+            const int32_t t = t0 + i;
+            if (t >= p.seqlen) break;
+            float acc = b0;
+#pragma unroll
+            for (int k = 0; k < H; ++k) acc = __builtin_fmaf(wf[k], bf_one(win[k]), acc);
+            acc = __builtin_fmaf(wf[H], bf_one(xv[i]), acc);
+            op[int64_t(t) * p.o_st] = to_bf16(act<SILU>(acc));
+#pragma unroll
+            for (int k = 0; k + 1 < H; ++k) win[k] = win[k + 1];
+            win[H - 1] = xv[i];
+
+            if (p.inter) {
+                uint16_t *ip = p.inter + int64_t(b) * p.i_sb + int64_t(t) * p.i_st +
+                               int64_t(c) * p.i_sd;
+#pragma unroll
+                for (int k = 0; k < H; ++k) ip[int64_t(k) * p.i_sk] = win[k];
+            }
+            if (p.out_idx) {
+                const int64_t dst = p.out_idx[int64_t(b) * p.oi_sb + int64_t(t) * p.oi_st];
+                if (dst >= 0 && dst < p.num_lines) {
+                    uint16_t *dp = p.cs + dst * p.cs_sl + int64_t(c) * p.cs_sd;
+#pragma unroll
+                    for (int k = 0; k < H; ++k) dp[int64_t(k) * p.cs_st] = win[k];
+                }
+            }
+            if (!saved) {
+                if (ring) {
+                    if (t >= ring_from) row[int64_t(rcol) * p.cs_st] = xv[i];
+                    rcol = rcol + 1 == L ? 0 : rcol + 1;
+                } else if (spec) {
+                    row[int64_t(H - 1 + t) * p.cs_st] = xv[i];
+                }
+            }
+        }
     }
+    if (!saved && !ring && !spec) {
 #pragma unroll
-    for (int k = 0; k < W - 1; ++k) st[k * p.cs_st] = win[k];
+        for (int k = 0; k < H; ++k) row[int64_t(k) * p.cs_st] = win[k];
+    }
 }
 
 template <int W>
 hipError_t launch_w(const UpdParams &p, bool silu, hipStream_t s) {
     const uint32_t cblocks = uint32_t((p.dim + kUpdBlock - 1) / kUpdBlock);
     const dim3 grid(cblocks * uint32_t(p.batch)), block(kUpdBlock);
-    if (silu) update_decode_kernel<W, true><<<grid, block, 0, s>>>(p, cblocks);
-    else update_decode_kernel<W, false><<<grid, block, 0, s>>>(p, cblocks);
+    if (silu) update_kernel<W, true><<<grid, block, 0, s>>>(p, cblocks);
+    else update_kernel<W, false><<<grid, block, 0, s>>>(p, cblocks);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_update_decode(const UpdParams &p, int width, bool silu, hipStream_t s) {
+hipError_t launch_update(const UpdParams &p, int width, bool silu, hipStream_t s) {
     switch (width) {
         case 2: return launch_w<2>(p, silu, s);
         case 3: return launch_w<3>(p, silu, s);

@@ -142,7 +142,8 @@ int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
  * `seqlen` new tokens (seqlen == 1 for plain decode) continuing from its
  * cached state, which is then shifted to hold the last width-1 inputs.
  * Follows tokenspeed causal_conv1d.py, causal_conv1d_update /
- * _causal_conv1d_update_kernel (without speculative decoding).
+ * _causal_conv1d_update_kernel (without speculative decoding; conv1d_update
+ * below adds the page's options).
  *
  * x            logical [batch][dim][seqlen] bf16 at
  *              x[b*x_stride_seq + c*x_stride_dim + t*x_stride_tok].
@@ -169,6 +170,79 @@ int conv1d_update_decode(const void *x, int64_t x_stride_seq, int64_t x_stride_d
                          void *out, int64_t o_stride_seq, int64_t o_stride_dim,
                          int64_t o_stride_tok,
                          hipStream_t stream);
+
+/*
+ * conv1d_update -- the decode update with the options of the same page
+ * (tokenspeed causal_conv1d.py, causal_conv1d_update /
+ * _causal_conv1d_update_kernel and its docstring): speculative decoding
+ * (num_accepted_tokens, intermediate windows, output_state_indices) and
+ * ring-buffer states (cache_seqlens).  conv1d_update_decode is this call with
+ * state_len = width-1 and every option NULL.
+ *
+ * x, weight, bias, out, cache_indices, pad_slot_id: as for
+ *              conv1d_update_decode (out may be exactly x).
+ * conv_state   logical [num_cache_lines][dim][state_len] bf16 (any strides),
+ *              state_len >= width-1.  The page asks for a unit dim stride;
+ *              any stride works here.
+ * Per entry b, the history (the width-1 inputs before x[b][.][0]) is
+ *   cache_seqlens given: columns (cache_seqlens[b] - (width-1) + k) mod
+ *              state_len, k = 0..width-2 (input n of the stream lives at
+ *              column n mod state_len, and cache_seqlens[b] inputs have been
+ *              seen);
+ *   num_accepted_tokens given: columns num_accepted_tokens[b] - 1 + k;
+ *   otherwise: columns k.
+ * Outputs are act(bias + sum_j w[j] u[t+j]) over u = history ++ x[b], as for
+ * every other call.  The window after step t is u[t+1 .. t+width-1], the
+ * width-1 inputs that end with x[b][.][t].
+ * intermediate [batch][>= seqlen][dim][width-1] bf16 or NULL, element
+ *              (b, t, c, k) at intermediate[b*it_stride_seq + t*it_stride_step
+ *              + c*it_stride_dim + k*it_stride_win]: receives the window after
+ *              every step t.  Indexed by batch position, not by cache line.
+ * output_state_indices  [batch][seqlen] int32 or NULL, element (b, t) at
+ *              [b*osi_stride_seq + t*osi_stride_step]: a line in
+ *              [0, num_cache_lines) receives the window after step t in its
+ *              columns 0..width-2; other values write nothing.  A destination
+ *              line must not be one that another entry of the same call reads
+ *              (the entry's own line is fine: an entry reads before it writes).
+ * State update in place, only when neither intermediate nor
+ *   output_state_indices is given:
+ *   cache_seqlens: x[b][.][t] goes to column (cache_seqlens[b] + t) mod
+ *              state_len (when seqlen > state_len only the last state_len
+ *              inputs remain);
+ *   num_accepted_tokens: columns 0 .. width-3+seqlen receive u[1 ..], the
+ *              history minus its oldest input followed by all of x[b]; the
+ *              next call's num_accepted_tokens = a then reads the window that
+ *              ends with the a-th input of this call.  Needs state_len >=
+ *              width-2+seqlen (else SCONV_ERR_SHAPE);
+ *   otherwise: columns 0..width-2 receive the last width-1 inputs of u.
+ * An entry is skipped entirely (no output, no state, no window) when its line
+ * is pad_slot_id or outside [0, num_cache_lines), when num_accepted_tokens[b]
+ * is below 1 or above state_len - width + 2, or when cache_seqlens[b] is
+ * negative.
+ * Errors: as for conv1d_update_decode; cache_seqlens together with any of
+ *   the three speculative options -> SCONV_ERR_ARG; state_len < width-1 ->
+ *   SCONV_ERR_SHAPE; intermediate overlapping x, out, conv_state, weight or
+ *   bias -> SCONV_ERR_ALIAS; index arrays must be 4-byte aligned.
+ */
+int conv1d_update(const void *x, int64_t x_stride_seq, int64_t x_stride_dim,
+                  int64_t x_stride_tok,
+                  const void *weight, int64_t w_stride_dim,
+                  const void *bias,
+                  void *conv_state, int64_t cs_stride_line,
+                  int64_t cs_stride_dim, int64_t cs_stride_tok,
+                  int64_t num_cache_lines, int32_t state_len,
+                  const int32_t *cache_indices,
+                  const int32_t *cache_seqlens,
+                  const int32_t *num_accepted_tokens,
+                  void *intermediate, int64_t it_stride_seq, int64_t it_stride_step,
+                  int64_t it_stride_dim, int64_t it_stride_win,
+                  const int32_t *output_state_indices, int64_t osi_stride_seq,
+                  int64_t osi_stride_step,
+                  int32_t batch, int32_t dim, int32_t seqlen,
+                  int32_t width, int32_t activation, int32_t pad_slot_id,
+                  void *out, int64_t o_stride_seq, int64_t o_stride_dim,
+                  int64_t o_stride_tok,
+                  hipStream_t stream);
 
 /*
  * sconv_paged_fused -- one launch that inserts every token's input into a

@@ -25,6 +25,15 @@ def addr(i):
     return ctypes.c_void_p(BASE + i * GB)
 
 
+def no_gpu():
+    """The validation calls below pass fake addresses.  Where a GPU is
+    visible, a check that wrongly let one through would launch a kernel on
+    them, so those tests only run where no GPU is."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-address validation runs only where no GPU is visible")
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -38,10 +47,10 @@ def lib():
     return S.load_library()
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     fns = declared_functions()
-    for name in ("conv1d_fwd_varlen", "conv1d_update_decode", "sconv_paged_fused",
-                 "sconv_status_string", "sconv_version"):
+    for name in ("conv1d_fwd_varlen", "conv1d_update_decode", "conv1d_update",
+                 "sconv_paged_fused", "sconv_status_string", "sconv_version"):
         assert name in fns
     assert sorted(S.exported_symbols()) == fns
 
@@ -56,7 +65,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert S.version() == (1, 0)
+    assert S.version() == (1, 1)
     for code in range(-8, 1):
         assert S.status_string(code) != "unknown status"
     assert S.status_string(-99) == "unknown status"
@@ -70,6 +79,7 @@ def test_missing_library_fails_loudly(tmp_path):
 # ------------------------------------------------------------------ fwd --
 
 def fwd(lib, **kw):
+    no_gpu()
     a = dict(x=addr(1), xsd=1, xst=64, w=addr(2), wsd=4, b=addr(3), cs=addr(4), csl=192,
              csd=3, cst=1, lines=4, ci=addr(5), hi=addr(6), qsl=addr(7), batch=2, T=10,
              dim=64, width=4, act=1, pad=-1, out=addr(8), osd=1, ost=64)
@@ -136,6 +146,7 @@ def test_fwd_aliasing(lib):
 # --------------------------------------------------------------- decode --
 
 def upd(lib, **kw):
+    no_gpu()
     a = dict(x=addr(1), xsb=64, xsd=1, xst=64, w=addr(2), wsd=4, b=addr(3), cs=addr(4),
              csl=192, csd=3, cst=1, lines=4, ci=addr(5), batch=2, dim=64, seqlen=1,
              width=4, act=1, pad=-1, out=addr(8), osb=64, osd=1, ost=64)
@@ -161,9 +172,49 @@ def test_decode_validation(lib):
     assert upd(lib, x=ctypes.c_void_p(BASE + GB + 1)) == EALIGN
 
 
+def updx(lib, **kw):
+    no_gpu()
+    a = dict(x=addr(1), xsb=64 * 4, xsd=1, xst=64, w=addr(2), wsd=4, b=addr(3), cs=addr(4),
+             csl=64 * 6, csd=1, cst=64, lines=16, L=6, ci=addr(5), ring=None, nacc=addr(6),
+             it=None, isb=0, ist=0, isd=0, isk=0, osi=None, osb_=0, ost_=0, batch=2, dim=64,
+             seqlen=4, width=4, act=1, pad=-1, out=addr(8), osb=64 * 4, osd=1, ost=64)
+    a.update(kw)
+    return lib.conv1d_update(a["x"], a["xsb"], a["xsd"], a["xst"], a["w"], a["wsd"], a["b"],
+                             a["cs"], a["csl"], a["csd"], a["cst"], a["lines"], a["L"], a["ci"],
+                             a["ring"], a["nacc"], a["it"], a["isb"], a["ist"], a["isd"],
+                             a["isk"], a["osi"], a["osb_"], a["ost_"], a["batch"], a["dim"],
+                             a["seqlen"], a["width"], a["act"], a["pad"], a["out"], a["osb"],
+                             a["osd"], a["ost"], None)
+
+
+def test_update_options_validation(lib):
+    inter = dict(it=addr(9), isb=4 * 64 * 3, ist=64 * 3, isd=3, isk=1)
+    assert updx(lib, width=6) == EWIDTH
+    assert updx(lib, ring=addr(7)) == EARG                 # ring with speculative options
+    assert updx(lib, ring=addr(7), nacc=None, osi=addr(10)) == EARG
+    assert updx(lib, ring=addr(7), nacc=None, **inter) == EARG
+    # accepted combinations, checked with batch 0 so that nothing is launched
+    assert updx(lib, ring=addr(7), nacc=None, L=3, batch=0) == OK
+    assert updx(lib, L=2) == ESHAPE                        # shorter than width-1
+    assert updx(lib, L=5) == ESHAPE                        # roll needs width-2+seqlen
+    assert updx(lib, L=3, osi=addr(10), osb_=4, ost_=1, batch=0) == OK   # saved windows: no roll
+    assert updx(lib, L=3, batch=0, **inter) == OK
+    assert updx(lib, L=5, batch=0) == ESHAPE
+    assert updx(lib, seqlen=0, x=None) == OK
+    assert updx(lib, cs=None) == ENULL
+    assert updx(lib, isd=-1, **{k: v for k, v in inter.items() if k != "isd"}) == ESTRIDE
+    assert updx(lib, nacc=ctypes.c_void_p(BASE + 6 * GB + 2)) == EALIGN
+    assert updx(lib, osi=ctypes.c_void_p(BASE + 10 * GB + 2)) == EALIGN
+    assert updx(lib, it=ctypes.c_void_p(BASE + 1 * GB + 64), isb=768, ist=192, isd=3,
+                isk=1) == EALIAS                          # windows inside x
+    assert updx(lib, it=ctypes.c_void_p(BASE + 4 * GB), isb=768, ist=192, isd=3,
+                isk=1) == EALIAS                          # windows inside the state
+
+
 # ---------------------------------------------------------------- paged --
 
 def paged(lib, **kw):
+    no_gpu()
     a = dict(x=addr(1), xst=4096, w=addr(2), wsd=4, b=None, c=addr(3), csb=32 * 16 * 512,
              csh=16 * 512, csn=512, nb=64, H=32, N=16, D=512, off=128, ws=128, pos=addr(4),
              slot=addr(5), qsl=addr(6), R=3, bt=addr(7), btsr=64, mb=64, T=100, width=4,
