@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   conv1d_update        -- decode update with speculative-decoding and
                           ring-buffer options
   sconv_paged_fused    -- paged sliding-window cache insert + conv
+  sconv_seq_metadata   -- per-token (request, first row) buffers
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ import os
 import torch
 
 __all__ = ["conv1d_fwd_varlen", "conv1d_update_decode", "conv1d_update", "sconv_paged_fused",
-           "new_output",
+           "sconv_seq_metadata", "new_output",
            "SconvError", "library_path", "load_library", "exported_symbols",
            "version", "status_string"]
 
@@ -74,8 +75,9 @@ def load_library(path: str | None = None):
     lib.sconv_paged_fused.argtypes = [
         P, I64, P, I64, P, P, I64, I64, I64, I64, I32, I32, I32, I32, I32,
         P, P, P, I32, P, I64, I32, I64, I32, I32, I32, P, I64, P]
+    lib.sconv_seq_metadata.argtypes = [P, I32, I64, I64, P, I64, P, I64, P]
     for f in (lib.conv1d_fwd_varlen, lib.conv1d_update_decode, lib.conv1d_update,
-              lib.sconv_paged_fused):
+              lib.sconv_paged_fused, lib.sconv_seq_metadata):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -84,7 +86,8 @@ def load_library(path: str | None = None):
 
 def exported_symbols() -> list[str]:
     return ["sconv_status_string", "sconv_version", "conv1d_fwd_varlen",
-            "conv1d_update_decode", "conv1d_update", "sconv_paged_fused"]
+            "conv1d_update_decode", "conv1d_update", "sconv_paged_fused",
+            "sconv_seq_metadata"]
 
 
 def version() -> tuple[int, int]:
@@ -342,3 +345,23 @@ def sconv_paged_fused(x, weight, cache, positions, slot_mapping, query_start_loc
     with torch.cuda.device(dev):
         _call("sconv_paged_fused", *args, _stream(dev))
     return out
+
+
+def sconv_seq_metadata(query_start_loc, num_reqs: int, num_actual_tokens: int,
+                       seq_idx_out, query_start_out, num_padded_tokens: int | None = None):
+    """Fill seq_idx_out / query_start_out (int32 device tensors) for the
+    first num_padded_tokens rows (default num_actual_tokens): owning request
+    and its first row for actual rows, 0 / 0 for padded ones."""
+    dev = seq_idx_out.device
+    for name, t in (("seq_idx_out", seq_idx_out), ("query_start_out", query_start_out)):
+        if t.dim() != 1 or (t.numel() > 1 and t.stride(0) != 1):
+            raise ValueError(f"{name} must be a contiguous 1-D tensor")
+    padded = -1 if num_padded_tokens is None else int(num_padded_tokens)
+    args = (
+        _index(query_start_loc, torch.int32, "query_start_loc", dev, int(num_reqs) + 1),
+        int(num_reqs), int(num_actual_tokens), padded,
+        _dev(seq_idx_out, torch.int32, "seq_idx_out", dev), seq_idx_out.numel(),
+        _dev(query_start_out, torch.int32, "query_start_out", dev), query_start_out.numel(),
+    )
+    with torch.cuda.device(dev):
+        _call("sconv_seq_metadata", *args, _stream(dev))

@@ -14,7 +14,7 @@ namespace {
 
 constexpr int kVersionMajor = 1;
 constexpr int kMaxWidthHistory = SCONV_MAX_WIDTH - 1;
-constexpr int kVersionMinor = 1;
+constexpr int kVersionMinor = 2;
 
 // Byte range [lo, hi) covered by a strided bf16 tensor; empty when a size is 0.
 struct Span {
@@ -292,6 +292,34 @@ int conv1d_update_decode(const void *x, int64_t x_stride_seq, int64_t x_stride_d
                          num_cache_lines, width - 1, cache_indices, nullptr, nullptr, nullptr,
                          0, 0, 0, 0, nullptr, 0, 0, batch, dim, seqlen, width, activation,
                          pad_slot_id, out, o_stride_seq, o_stride_dim, o_stride_tok, stream);
+}
+
+int sconv_seq_metadata(const int32_t *query_start_loc, int32_t num_reqs,
+                       int64_t num_actual_tokens, int64_t num_padded_tokens,
+                       int32_t *seq_idx_out, int64_t seq_idx_capacity,
+                       int32_t *query_start_out, int64_t query_start_capacity,
+                       hipStream_t stream) {
+    if (num_padded_tokens < 0) num_padded_tokens = num_actual_tokens;
+    if (num_actual_tokens < 0 || num_reqs < 0) return SCONV_ERR_SHAPE;
+    if (num_padded_tokens < num_actual_tokens) return SCONV_ERR_SHAPE;
+    if (num_padded_tokens > seq_idx_capacity || num_padded_tokens > query_start_capacity)
+        return SCONV_ERR_SHAPE;
+    if (num_padded_tokens > INT32_MAX) return SCONV_ERR_SHAPE;
+    if (num_actual_tokens > 0 && num_reqs < 1) return SCONV_ERR_SHAPE;
+    if (num_padded_tokens == 0) return SCONV_OK;
+    if (!seq_idx_out || !query_start_out || (num_actual_tokens > 0 && !query_start_loc))
+        return SCONV_ERR_NULL;
+    if (!aligned(query_start_loc, 4) || !aligned(seq_idx_out, 4) || !aligned(query_start_out, 4))
+        return SCONV_ERR_ALIGN;
+    const Span si = span_of(seq_idx_out, {num_padded_tokens}, {1}, 4);
+    const Span sq = span_of(query_start_out, {num_padded_tokens}, {1}, 4);
+    const Span sl = span_of(num_actual_tokens > 0 ? query_start_loc : nullptr,
+                            {int64_t(num_reqs) + 1}, {1}, 4);
+    if (overlap(si, sq) || overlap(si, sl) || overlap(sq, sl)) return SCONV_ERR_ALIAS;
+    return launch_status(launch_seq_metadata(query_start_loc, num_reqs,
+                                             int32_t(num_actual_tokens),
+                                             int32_t(num_padded_tokens), seq_idx_out,
+                                             query_start_out, stream));
 }
 
 int sconv_paged_fused(const void *x, int64_t x_stride_tok, const void *weight,

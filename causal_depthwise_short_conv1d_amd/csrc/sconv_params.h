@@ -127,6 +127,9 @@ struct PagedParams {
 hipError_t launch_fwd_tokmajor(const FwdTokParams &p, int width, bool silu, hipStream_t s);
 hipError_t launch_fwd_chanlast(const FwdClParams &p, int width, bool silu, hipStream_t s);
 hipError_t launch_update(const UpdParams &p, int width, bool silu, hipStream_t s);
+hipError_t launch_seq_metadata(const int32_t *qsl, int32_t num_reqs, int32_t num_actual,
+                               int32_t num_padded, int32_t *seq_idx, int32_t *query_start,
+                               hipStream_t s);
 hipError_t launch_paged_fused(const PagedParams &p, int width, bool silu, bool residual,
                               hipStream_t s);
 

@@ -245,6 +245,33 @@ int conv1d_update(const void *x, int64_t x_stride_seq, int64_t x_stride_dim,
                   hipStream_t stream);
 
 /*
+ * sconv_seq_metadata -- per-token request metadata in one launch, for callers
+ * that keep persistent seq_idx / query_start buffers (Inkling sconv.py,
+ * sconv_seq_metadata / _seq_metadata_kernel).  sconv_paged_fused derives the
+ * same values inside its own kernel and does not need them.
+ *
+ * query_start_loc  [num_reqs+1] int32, non-decreasing row offsets (device).
+ *              Read only when num_actual_tokens > 0.
+ * Rows t < num_actual_tokens get seq_idx_out[t] = the largest j < num_reqs
+ * with query_start_loc[j] <= t (an empty request is passed over) and
+ * query_start_out[t] = query_start_loc[seq_idx_out[t]].  Rows in
+ * [num_actual_tokens, num_padded_tokens) get 0 / 0; such padded rows must
+ * carry slot_mapping == -1 in the paged call.  num_padded_tokens < 0 means
+ * num_actual_tokens.
+ * seq_idx_out, query_start_out  int32 device arrays with room for
+ *              seq_idx_capacity / query_start_capacity entries.
+ * Errors: num_padded_tokens < num_actual_tokens, or above either capacity
+ *   or INT32_MAX, or num_reqs < 1 with actual tokens -> SCONV_ERR_SHAPE (the
+ *   page raises for the first three); NULL arrays -> SCONV_ERR_NULL;
+ *   misaligned -> SCONV_ERR_ALIGN; overlapping arrays -> SCONV_ERR_ALIAS.
+ */
+int sconv_seq_metadata(const int32_t *query_start_loc, int32_t num_reqs,
+                       int64_t num_actual_tokens, int64_t num_padded_tokens,
+                       int32_t *seq_idx_out, int64_t seq_idx_capacity,
+                       int32_t *query_start_out, int64_t query_start_capacity,
+                       hipStream_t stream);
+
+/*
  * sconv_paged_fused -- one launch that inserts every token's input into a
  * paged sliding-window cache and convolves the width taps ending at its
  * absolute position.  Follows Inkling sconv.py, fused_sconv /

@@ -50,7 +50,8 @@ def lib():
 def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("conv1d_fwd_varlen", "conv1d_update_decode", "conv1d_update",
-                 "sconv_paged_fused", "sconv_status_string", "sconv_version"):
+                 "sconv_paged_fused", "sconv_seq_metadata", "sconv_status_string",
+                 "sconv_version"):
         assert name in fns
     assert sorted(S.exported_symbols()) == fns
 
@@ -65,7 +66,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert S.version() == (1, 1)
+    assert S.version() == (1, 2)
     for code in range(-8, 1):
         assert S.status_string(code) != "unknown status"
     assert S.status_string(-99) == "unknown status"
@@ -242,3 +243,27 @@ def test_paged_validation(lib):
     assert paged(lib, x=ctypes.c_void_p(BASE + GB + 8)) == EALIGN
     assert paged(lib, out=addr(1)) == EALIAS
     assert paged(lib, out=ctypes.c_void_p(BASE + 3 * GB + 1024)) == EALIAS   # out inside cache
+
+
+# ------------------------------------------------------------- metadata --
+
+def meta(lib, **kw):
+    no_gpu()
+    a = dict(qsl=addr(1), R=4, act=100, pad=-1, si=addr(2), sicap=128, qs=addr(3), qscap=128)
+    a.update(kw)
+    return lib.sconv_seq_metadata(a["qsl"], a["R"], a["act"], a["pad"], a["si"], a["sicap"],
+                                  a["qs"], a["qscap"], None)
+
+
+def test_seq_metadata_validation(lib):
+    assert meta(lib, pad=99) == ESHAPE            # padding must cover the actual rows
+    assert meta(lib, sicap=99) == ESHAPE          # seq_idx_out too small
+    assert meta(lib, qscap=50) == ESHAPE          # query_start_out too small
+    assert meta(lib, R=0) == ESHAPE               # actual rows need a request
+    assert meta(lib, act=-1) == ESHAPE
+    assert meta(lib, act=0, pad=0, si=None) == OK
+    assert meta(lib, si=None) == ENULL
+    assert meta(lib, qsl=None) == ENULL
+    assert meta(lib, qs=ctypes.c_void_p(BASE + 3 * GB + 2)) == EALIGN
+    assert meta(lib, qs=ctypes.c_void_p(BASE + 2 * GB + 64)) == EALIAS
+    assert meta(lib, qs=addr(1)) == EALIAS        # output over query_start_loc
