@@ -56,6 +56,53 @@ def fwd_bytes(dim, lengths, width, bias=True, n_init=None, n_state=None,
             + 4 * (B + 1) + (4 * B if cache_indices else 0) + (B if has_init else 0))
 
 
+def paged_bytes(C, T, valid, R, width, n_streams=1):
+    """Algorithmic bytes of one paged step: per stream x read, out written,
+    the valid rows inserted into the cache, width-1 cached taps read per
+    request and the taps; once for all streams the per-token positions and
+    slots and query_start_loc (block-table reads are counted with the taps'
+    rows they locate, not separately)."""
+    per_stream = 2 * C * T * 2 + 2 * C * valid + 2 * C * (width - 1) * R + 2 * C * width
+    return n_streams * per_stream + 16 * T + 4 * (R + 1)
+
+
+def spec_bytes(dim, batch_live, seqlen, width, n_idx):
+    """Algorithmic bytes of one speculative verify step that rolls the state:
+    x read and out written, the width-1 history read and width-2+seqlen
+    columns written per live entry, taps and bias, and the index arrays."""
+    return (2 * 2 * batch_live * dim * seqlen + 2 * batch_live * dim * (width - 1)
+            + 2 * batch_live * dim * (width - 2 + seqlen) + 2 * dim * width + 2 * dim
+            + 4 * n_idx)
+
+
+def graph_time_ms(fn, reps=100, replays=20):
+    """Per-launch device time of `reps` back-to-back launches captured in one
+    HIP graph: no host launch gap between them (the caches stay warm)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(replays):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) / reps)
+    del g
+    return statistics.median(times)
+
+
 def kernel_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -226,7 +273,8 @@ def extras(torch, S, W, dev):
                                         activation="silu", cache_indices=d["cache_indices"],
                                         out=xo)
     fn()
-    kern = event_time_ms(fn, 200, None)
+    cold = event_time_ms(fn, 50, flush)
+    warm = graph_time_ms(fn)
     lat = []
     for _ in range(1000):
         t0 = time.perf_counter()
@@ -234,11 +282,34 @@ def extras(torch, S, W, dev):
         torch.cuda.synchronize()
         lat.append(time.perf_counter() - t0)
     dec_bytes = 4 * 4096 + 4 * 3 * 4096 + 2 * 4096 * 4 + 2 * 4096 + 4
-    ex["decode_dim4096_T1"] = {"kernel_us": round(kern * 1e3, 2),
+    ex["decode_dim4096_T1"] = {"graph_us_per_launch": round(warm * 1e3, 2),
+                               "cold_cache_us": round(cold * 1e3, 2),
                                "host_latency_us_median": round(statistics.median(lat) * 1e6, 2),
                                "bytes": dec_bytes}
-    log(f"[bench] decode dim4096 T1: kernel {kern*1e3:.2f} us, host latency "
-        f"{statistics.median(lat)*1e6:.1f} us")
+    log(f"[bench] decode dim4096 T1: {warm*1e3:.2f} us/launch in a graph, {cold*1e3:.2f} us "
+        f"cold, host latency {statistics.median(lat)*1e6:.1f} us")
+
+    # speculative verify: 64 entries x dim 8192, 4 tokens each, state rolled
+    cfg = W.SPEC_DECODE
+    d = W.spec_decode_batch(batch=cfg["batch"], dim=cfg["dim"], width=cfg["width"],
+                            seqlen=cfg["seqlen"], num_lines=cfg["num_lines"],
+                            n_pad=cfg["n_pad"], seed=W.seed_for(6, 0), mode="roll",
+                            device=dev)
+    so = torch.empty_like(d["x"])
+    fn = lambda: S.conv1d_update(d["x"], d["conv_state"], d["weight"], d["bias"],
+                                 activation="silu", cache_indices=d["cache_indices"],
+                                 num_accepted_tokens=d["num_accepted_tokens"], out=so)
+    fn()
+    cold = event_time_ms(fn, 30, flush)
+    warm = graph_time_ms(fn)
+    live = cfg["batch"] - cfg["n_pad"]
+    nb = spec_bytes(cfg["dim"], live, cfg["seqlen"], cfg["width"], 2 * cfg["batch"])
+    ex["spec_verify_64x8192_seqlen4"] = {"cold_cache_us": round(cold * 1e3, 2),
+                                         "graph_us_per_launch": round(warm * 1e3, 2),
+                                         "GB/s_cold": round(nb / cold / 1e6, 1), "bytes": nb}
+    log(f"[bench] spec verify 64x8192x4: {cold*1e3:.2f} us cold ({nb/cold/1e6:.0f} GB/s), "
+        f"{warm*1e3:.2f} us/launch in a graph")
+    del d, so
 
     # varlen continuous batch, widths 2..5, channel-contiguous
     vl = {}
@@ -265,28 +336,34 @@ def extras(torch, S, W, dev):
         del d, out, cs
     ex["varlen_64seq_dim8192"] = vl
 
-    # paged mixed step
-    cfg = W.PAGED_MIXED
-    d = W.paged_batch(H=cfg["H"], ws=cfg["ws"], N=cfg["N"], D=cfg["D"], off_s=cfg["off_s"],
-                      num_blocks=cfg["num_blocks"], width=cfg["width"], n_decode=cfg["n_decode"],
-                      n_prefill=cfg["n_prefill"], chunk=cfg["chunk"], max_pos=cfg["max_pos"],
-                      pad_frac=cfg["pad_frac"], seed=W.seed_for(5), device=dev)
-    out = torch.empty_like(d["x"])
-    fn = lambda: S.sconv_paged_fused(d["x"], d["weight"], d["cache"], d["positions"],
-                                     d["slot_mapping"], d["query_start_loc"], d["block_table"],
-                                     d["off_s"], d["ws"], activation="silu", use_residual=True,
-                                     out=out)
-    fn()
-    ms = event_time_ms(fn, 20, flush)
+    # paged mixed step: one stream, then the four streams sharing the cache
+    cfg = {k: v for k, v in W.PAGED_MIXED.items() if k != "off_s"}
+    d = W.paged_multi_batch(seed=W.seed_for(5), device=dev, **cfg)
     Tp, C = d["x"].shape
     valid = int((d["slot_mapping"] >= 0).sum())
     R = d["query_start_loc"].numel() - 1
-    # cached taps read: width-1 positions per request (all >= 0 by construction)
-    nb = 2 * C * Tp * 2 + 2 * C * valid + 2 * C * 3 * R + 2 * C * 4 + 16 * Tp + 4 * (R + 1)
+    outs = [torch.empty_like(x) for x in d["xs"]]
+    fn = lambda: S.sconv_paged_fused(d["x"], d["weight"], d["cache"], d["positions"],
+                                     d["slot_mapping"], d["query_start_loc"], d["block_table"],
+                                     W.PAGED_MIXED["off_s"], d["ws"], activation="silu",
+                                     use_residual=True, out=outs[0])
+    fn()
+    ms = event_time_ms(fn, 20, flush)
+    nb = paged_bytes(C, Tp, valid, R, cfg["width"])
     ex["paged_mixed_T4128_C4096"] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
                                      "bytes": nb}
     log(f"[bench] paged: {ms*1e3:.1f} us {nb/ms/1e6:.0f} GB/s")
-    del d, out
+    fn = lambda: S.sconv_paged_fused_multi(d["xs"], d["weights"], d["cache"], d["positions"],
+                                           d["slot_mapping"], d["query_start_loc"],
+                                           d["block_table"], d["offs"], d["ws"],
+                                           activation="silu", use_residual=True, outs=outs)
+    fn()
+    ms = event_time_ms(fn, 20, flush)
+    nb = paged_bytes(C, Tp, valid, R, cfg["width"], n_streams=len(d["xs"]))
+    ex["paged_mixed_4streams_T4128_C4096"] = {"us": round(ms * 1e3, 2),
+                                              "GB/s": round(nb / ms / 1e6, 1), "bytes": nb}
+    log(f"[bench] paged 4 streams: {ms*1e3:.1f} us {nb/ms/1e6:.0f} GB/s")
+    del d, outs
 
     # practical copy ceiling: a device copy moving the headline's byte count
     n = 8192 * 14807

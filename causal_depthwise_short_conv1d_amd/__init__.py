@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   conv1d_update        -- decode update with speculative-decoding and
                           ring-buffer options
   sconv_paged_fused    -- paged sliding-window cache insert + conv
+  sconv_paged_fused_multi -- several conv streams sharing one paged cache
   sconv_seq_metadata   -- per-token (request, first row) buffers
 """
 from __future__ import annotations
@@ -22,7 +23,7 @@ import os
 import torch
 
 __all__ = ["conv1d_fwd_varlen", "conv1d_update_decode", "conv1d_update", "sconv_paged_fused",
-           "sconv_seq_metadata", "new_output",
+           "sconv_paged_fused_multi", "sconv_seq_metadata", "new_output",
            "SconvError", "library_path", "load_library", "exported_symbols",
            "version", "status_string"]
 
@@ -76,8 +77,11 @@ def load_library(path: str | None = None):
         P, I64, P, I64, P, P, I64, I64, I64, I64, I32, I32, I32, I32, I32,
         P, P, P, I32, P, I64, I32, I64, I32, I32, I32, P, I64, P]
     lib.sconv_seq_metadata.argtypes = [P, I32, I64, I64, P, I64, P, I64, P]
+    lib.sconv_paged_fused_multi.argtypes = [
+        I32, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I32, I32, I32,
+        P, P, P, I32, P, I64, I32, I64, I32, I32, I32, P]
     for f in (lib.conv1d_fwd_varlen, lib.conv1d_update_decode, lib.conv1d_update,
-              lib.sconv_paged_fused, lib.sconv_seq_metadata):
+              lib.sconv_paged_fused, lib.sconv_paged_fused_multi, lib.sconv_seq_metadata):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -87,7 +91,7 @@ def load_library(path: str | None = None):
 def exported_symbols() -> list[str]:
     return ["sconv_status_string", "sconv_version", "conv1d_fwd_varlen",
             "conv1d_update_decode", "conv1d_update", "sconv_paged_fused",
-            "sconv_seq_metadata"]
+            "sconv_paged_fused_multi", "sconv_seq_metadata"]
 
 
 def version() -> tuple[int, int]:
@@ -365,3 +369,64 @@ def sconv_seq_metadata(query_start_loc, num_reqs: int, num_actual_tokens: int,
     )
     with torch.cuda.device(dev):
         _call("sconv_seq_metadata", *args, _stream(dev))
+
+
+def sconv_paged_fused_multi(xs, weights, cache, positions, slot_mapping, query_start_loc,
+                            block_table, offs, ws: int, activation=None,
+                            use_residual: bool = True, biases=None, outs=None):
+    """Several conv streams sharing one paged cache, in one launch.  xs,
+    weights, offs (and biases / outs when given) are lists with one entry per
+    stream; every stream has H * ws channels (ws may also be a list).
+    Returns the list of outputs."""
+    n = len(xs)
+    if not (len(weights) == len(offs) == n) or n < 1:
+        raise ValueError("xs, weights and offs need one entry per stream")
+    wss = list(ws) if isinstance(ws, (list, tuple)) else [int(ws)] * n
+    dev = xs[0].device
+    num_blocks, H, N, D = cache.shape
+    width = weights[0].shape[1]
+    num_reqs = query_start_loc.numel() - 1
+    T = xs[0].shape[0]
+    if outs is None:
+        outs = [torch.empty_like(x) for x in xs]
+    if biases is None:
+        biases = [None] * n
+    bf = torch.bfloat16
+    for i in range(n):
+        x, w, b, o = xs[i], weights[i], biases[i], outs[i]
+        if x.dim() != 2 or x.shape != (T, H * wss[i]) or x.stride(1) != 1:
+            raise ValueError(f"stream {i}: x must be (T, H*ws) with unit channel stride")
+        if o.shape != x.shape or o.stride(1) != 1:
+            raise ValueError(f"stream {i}: out must match x")
+        if w.dim() != 2 or w.shape != (H * wss[i], width) or w.stride(1) != 1:
+            raise ValueError(f"stream {i}: weight must be (C, width) with unit width stride")
+        if b is not None and (b.shape != (H * wss[i],) or b.stride(0) != 1):
+            raise ValueError(f"stream {i}: bias must be a contiguous (C,) tensor")
+    if cache.stride(3) != 1:
+        raise ValueError("cache D must have unit stride")
+    if block_table.dim() != 2 or (block_table.numel() and block_table.stride(1) != 1):
+        raise ValueError("block_table must be (num_reqs, max_blocks) with unit inner stride")
+    VP = ctypes.c_void_p * n
+    I64A = ctypes.c_int64 * n
+    I32A = ctypes.c_int32 * n
+    xp = VP(*[_dev(x, bf, f"xs[{i}]", dev) for i, x in enumerate(xs)])
+    wp = VP(*[_dev(w, bf, f"weights[{i}]", dev) for i, w in enumerate(weights)])
+    bp = VP(*[_dev(b, bf, f"biases[{i}]", dev) for i, b in enumerate(biases)])
+    op = VP(*[_dev(o, bf, f"outs[{i}]", dev) for i, o in enumerate(outs)])
+    args = (
+        n, xp, I64A(*[x.stride(0) for x in xs]), wp, I64A(*[w.stride(0) for w in weights]),
+        bp if any(b is not None for b in biases) else None,
+        I32A(*[int(o) for o in offs]), I32A(*wss), op, I64A(*[o.stride(0) for o in outs]),
+        _dev(cache, bf, "cache", dev), cache.stride(0), cache.stride(1), cache.stride(2),
+        num_blocks, H, N, D,
+        _index(positions, torch.int64, "positions", dev, T),
+        _index(slot_mapping, torch.int64, "slot_mapping", dev, T),
+        _index(query_start_loc, torch.int32, "query_start_loc", dev, num_reqs + 1), num_reqs,
+        _dev(block_table, torch.int32, "block_table", dev),
+        block_table.stride(0) if block_table.dim() == 2 else 0,
+        block_table.shape[1] if block_table.dim() == 2 else 0,
+        T, width, _act(activation), int(bool(use_residual)),
+    )
+    with torch.cuda.device(dev):
+        _call("sconv_paged_fused_multi", *args, _stream(dev))
+    return outs

@@ -139,30 +139,44 @@ __device__ __forceinline__ void run_segment(const FwdClParams &p, const SeqInfo 
         // One state line through a buffer descriptor: element (c, k) at byte
         // 2*(c*cs_sd + k*cs_st) from the line start (the host bounds a line's
         // extent below 2 GiB); only the lane's channel offsets are vectors.
-        // (no state: a zero-length descriptor, never dereferenced)
-        const __amdgpu_buffer_rsrc_t cs = __builtin_amdgcn_make_buffer_rsrc(
-            p.sb.cs ? p.sb.cs + si.line * p.sb.cs_sl : p.sb.cs, short(0),
-            p.sb.cs ? 0x7fffffff : 0, 0x00020000);
+        // Every load below is issued unconditionally (a descriptor of zero
+        // extent, or an out-of-range offset, reads 0), so none waits for
+        // another.
+        const bool has_cs = p.sb.cs != nullptr;
+        const Rsrc cs = make_rsrc(has_cs ? p.sb.cs + si.line * p.sb.cs_sl : p.x,
+                                  has_cs ? 0x7fffffff : 0);
+        const Rsrc hist = make_rsrc(has_cs ? p.sb.cs + si.line * p.sb.cs_sl : p.x,
+                                    has_cs && si.init ? 0x7fffffff : 0);
         uint32_t coff[kCpl];
 #pragma unroll
-        for (int ch = 0; ch < kCpl; ++ch) coff[ch] = uint32_t(int64_t(c0 + ch) * p.sb.cs_sd * 2);
+        for (int ch = 0; ch < kCpl; ++ch)
+            coff[ch] = ch < nv ? uint32_t(int64_t(c0 + ch) * p.sb.cs_sd * 2) : kOob;
         // the cached history, packed as it arrives
 #pragma unroll
         for (int k = 0; k < H; ++k) {
             uint32_t d[2] = {0u, 0u};
-            if (si.init) {
 #pragma unroll
-                for (int ch = 0; ch < kCpl; ++ch)
-                    if (ch < nv)
-                        d[ch >> 1] |= uint32_t(__builtin_amdgcn_raw_buffer_load_b16(
-                                          cs, coff[ch], int(k * p.sb.cs_st * 2), 0))
-                                      << (16 * (ch & 1));
-            }
+            for (int ch = 0; ch < kCpl; ++ch)
+                d[ch >> 1] |= uint32_t(__builtin_amdgcn_raw_buffer_load_b16(
+                                  hist, coff[ch], int(k * p.sb.cs_st * 2), 0))
+                              << (16 * (ch & 1));
             win[k] = u32x2{d[0], d[1]};
         }
-        if (p.sb.cs) {
-            // new state = the last width-1 entries of (history ++ sequence)
+        if (has_cs) {
+            // new state = the last width-1 entries of (history ++ sequence):
+            // rows of the sequence are loaded (those before its start read 0)
+            // and the history entries are picked after the loads
             const int64_t L = si.end - si.start;
+            u32x2 tail[H];
+#pragma unroll
+            for (int k = 0; k < H; ++k) {
+                const int64_t row = si.start + L + k - H;
+                const bool in = row >= si.start;
+                const Rows rk = make_rows(p.x, in ? row : si.start, p.x_st, si.end, p.dim);
+                tail[k] = FULL ? __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                     rk.rsrc, in ? uint32_t(c0) * 2 : kOob, 0, 0))
+                               : (in ? ld_row<FULL>(p.x + row * p.x_st + c0, nv) : u32x2{0u, 0u});
+            }
             u32x2 nh[H];
 #pragma unroll
             for (int k = 0; k < H; ++k) {
@@ -171,28 +185,20 @@ __device__ __forceinline__ void run_segment(const FwdClParams &p, const SeqInfo 
 #pragma unroll
                 for (int q = 1; q < H; ++q)
                     if (m == q) hv = win[q];
-                if (m < H) {
-                    nh[k] = hv;
-                } else {
-                    const int64_t row = si.start + m - H;
-                    nh[k] = FULL ? ld_rows(make_rows(p.x, row, p.x_st, p.sb.total_T, p.dim), row,
-                                           uint32_t(c0) * 2)
-                                 : ld_row<FULL>(p.x + row * p.x_st + c0, nv);
-                }
+                nh[k] = m < H ? hv : tail[k];
             }
 #pragma unroll
             for (int k = 0; k < H; ++k)
 #pragma unroll
                 for (int ch = 0; ch < kCpl; ++ch)
-                    if (ch < nv)
-                        __builtin_amdgcn_raw_buffer_store_b16(row_elem(nh[k], ch), cs, coff[ch],
-                                                              int(k * p.sb.cs_st * 2), 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(row_elem(nh[k], ch), cs, coff[ch],
+                                                          int(k * p.sb.cs_st * 2), 0);
         }
     }
-    const int64_t T = p.sb.total_T;
     const int64_t base = head ? b : b - H;
-    const Rows xr = make_rows(p.x, base, p.x_st, T, p.dim);
-    const Rows orr = make_rows(p.out, base, p.o_st, T, p.dim);
+    // both descriptors end with the segment: rows past it read 0, store nothing
+    const Rows xr = make_rows(p.x, base, p.x_st, e, p.dim);
+    const Rows orr = make_rows(p.out, base, p.o_st, e, p.dim);
     const uint32_t voff = uint32_t(c0) * 2;
     if (!head) {
         // interior: the previous width-1 rows belong to the same sequence
@@ -206,9 +212,10 @@ __device__ __forceinline__ void run_segment(const FwdClParams &p, const SeqInfo 
         const int n = (e - t) < kUnroll ? int(e - t) : kUnroll;
         u32x2 xv[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            if (u < n)
-                xv[u] = FULL ? ld_rows(xr, t + u, voff) : ld_row<FULL>(p.x + (t + u) * p.x_st + c0, nv);
+        for (int u = 0; u < kUnroll; ++u) {
+            if constexpr (FULL) xv[u] = ld_rows(xr, t + u, voff);     // past the segment: 0
+            else if (u < n) xv[u] = ld_row<FULL>(p.x + (t + u) * p.x_st + c0, nv);
+        }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             if (u < n) {
@@ -241,16 +248,22 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_chanlast_ker
     nv = nv < 0 ? 0 : (nv > kCpl ? kCpl : nv);
     if (nv == 0) c0 = 0;                   // idle lane: in-range reads, no writes
 
+    // taps of the lane's channels, loaded without branches (channels past
+    // dim, and a missing bias, read 0)
+    const int32_t c_lo = slab * kClSlab;
+    const int32_t n_ch = p.dim - c_lo < kClSlab ? p.dim - c_lo : kClSlab;
+    const Rsrc wr = make_rsrc(p.w + int64_t(c_lo) * p.w_sd, int64_t(n_ch) * p.w_sd * 2);
+    const Rsrc br = make_rsrc(p.bias ? p.bias + c_lo : p.w, p.bias ? int64_t(n_ch) * 2 : 0);
     LaneTaps<W> tp;
 #pragma unroll
     for (int ch = 0; ch < kCpl; ++ch) {
-        const bool ok = ch < nv;
-        const uint16_t *w = p.w + int64_t(ok ? c0 + ch : 0) * p.w_sd;
+        const int32_t lc = lane * kCpl + ch;              // channel within the slab
+        const uint32_t wo = lc < n_ch ? uint32_t(int64_t(lc) * p.w_sd * 2) : kOob;
 #pragma unroll
         for (int q = 0; q < W / 2; ++q)
-            tp.wp[q][ch] = ok ? (uint32_t(w[2 * q]) | (uint32_t(w[2 * q + 1]) << 16)) : 0u;
-        tp.wl[ch] = (ok && (W & 1)) ? bf_one(w[W - 1]) : 0.0f;
-        tp.b[ch] = (ok && p.bias) ? bf_one(p.bias[c0 + ch]) : 0.0f;
+            tp.wp[q][ch] = uint32_t(buf_ld16(wr, wo + 4 * q)) | (uint32_t(buf_ld16(wr, wo + 4 * q + 2)) << 16);
+        tp.wl[ch] = (W & 1) ? bf_one(buf_ld16(wr, wo + 2 * (W - 1))) : 0.0f;
+        tp.b[ch] = bf_one(buf_ld16(br, lc < n_ch ? uint32_t(lc) * 2 : kOob));
     }
 
     const int64_t T = p.sb.total_T;

@@ -36,6 +36,8 @@ namespace {
 
 constexpr int kChunksPerWave = kWaveSize * kTokRounds;
 constexpr uint32_t kWaveElems = kChunksPerWave * kVec;
+constexpr int kShortMinT = 16;                    // shortest row of the short-row kernel
+constexpr int kShortBigChunks = 256 * 16 * 2 * kWaveSize;  // 2 rounds from here on
 
 // Weights of one channel for the dot2 path: taps as packed bf16 pairs
 // (w[2p], w[2p+1]), the odd last tap and the bias as fp32.
@@ -112,14 +114,21 @@ __device__ __forceinline__ u32x4 fast_chunk(const Window &win, const PairTaps<W>
     return pack8(o);
 }
 
-// Bits of the history entry h[H+l], l in [-H, -1], without dynamic indexing.
+// The history h[0..H) packed four 16-bit entries to a 64-bit value, and entry
+// h[H+l] (l in [-H, -1]) read back by shifting.  Arithmetic, not an array:
+// a select chain over an array indexed by a lane-dependent l gets folded
+// into an indexed load, the array then moves to LDS, and indexing it costs
+// every wave a read of the dispatch packet -- about 15 us per launch.
 template <int H>
-__device__ __forceinline__ uint32_t hist_bits(const uint32_t (&h)[H], int l) {
-    uint32_t v = h[0];
+__device__ __forceinline__ uint64_t pack_hist(const uint32_t (&h)[H]) {
+    uint64_t v = 0;
 #pragma unroll
-    for (int k = 1; k < H; ++k)
-        if (l == k - H) v = h[k];
+    for (int k = 0; k < H; ++k) v |= uint64_t(h[k] & 0xffffu) << (16 * k);
     return v;
+}
+template <int H>
+__device__ __forceinline__ uint32_t hist_bits(uint64_t hv, int l) {
+    return uint32_t(hv >> (16 * (H + l))) & 0xffffu;
 }
 
 // A chunk that holds part of the first width-1 tokens of a row whose head is
@@ -133,16 +142,15 @@ __device__ __forceinline__ u32x4 head_chunk(const Window &win, uint32_t i0, uint
                                             const PairTaps<W> &t_prev, const PairTaps<W> &t_head,
                                             const uint32_t (&h)[W - 1]) {
     constexpr int H = W - 1;
+    const uint64_t hv = pack_hist<H>(h);
     Window wh = win;
 #pragma unroll
     for (int d = 0; d < 6; ++d) {
-        uint32_t half[2] = {wh.d[d] & 0xffffu, wh.d[d] >> 16};
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int l = int(i0 - 4 + 2 * d + q) - int(hp);   // position relative to the head
-            if (l >= -H && l < 0) half[q] = hist_bits<H>(h, l);
-        }
-        wh.d[d] = half[0] | (half[1] << 16);
+        uint32_t lo = wh.d[d] & 0xffffu, hi = wh.d[d] >> 16;
+        const int l0 = int(i0 - 4 + 2 * d) - int(hp);          // position relative to the head
+        if (l0 >= -H && l0 < 0) lo = hist_bits<H>(hv, l0);
+        if (l0 + 1 >= -H && l0 + 1 < 0) hi = hist_bits<H>(hv, l0 + 1);
+        wh.d[d] = lo | (hi << 16);
     }
     const u32x4 a = fast_chunk<W, SILU>(win, t_prev);
     const u32x4 b = fast_chunk<W, SILU>(wh, t_head);
@@ -397,6 +405,238 @@ __global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tok_long_ke
         if (slow & (1u << r)) slow_chunk<W, SILU>(p, p.sb.qsl, (wbase + r * kWaveSize + lane) * kVec);
 }
 
+// Tap k of a PairTaps as fp32.
+template <int W>
+__device__ __forceinline__ float tap_of(const PairTaps<W> &t, int k) {
+    if ((W & 1) && k == W - 1) return t.wl;
+    const uint32_t pr = t.wp[k >> 1];
+    return (k & 1) ? bf_hi(pr) : bf_lo(pr);
+}
+
+// Taps of channel row `lr` of a wave-local weight descriptor (row pitch
+// w_sd elements), loaded without branches (past the extent: 0).
+template <int W>
+__device__ __forceinline__ PairTaps<W> buf_pair_taps(Rsrc wr, Rsrc br, uint32_t lr, int64_t w_sd) {
+    PairTaps<W> t;
+    const uint32_t o = uint32_t(int64_t(lr) * w_sd) * 2;
+#pragma unroll
+    for (int q = 0; q < W / 2; ++q)
+        t.wp[q] = uint32_t(buf_ld16(wr, o + 4 * q)) | (uint32_t(buf_ld16(wr, o + 4 * q + 2)) << 16);
+    t.wl = (W & 1) ? bf_one(buf_ld16(wr, o + 2 * (W - 1))) : 0.0f;
+    t.b = bf_one(buf_ld16(br, lr * 2));
+    return t;
+}
+
+// One sequence whose rows are short (kShortMinT <= T < one wave): a chunk
+// holds at most one row start, and every element of a chunk before that
+// start has its whole window inside its own row (T >= 16 > 8 + width-1).
+// The lane whose chunk holds a row start owns that row's history: together
+// with its chunk it loads the cached state, the row's first width-1 inputs
+// and its last width-1 inputs; it computes the chunk (head_chunk), the head
+// outputs that spill into the next chunk, and writes the new state, while
+// the next chunk leaves those spilled outputs alone.
+// Latency decides this kernel (a few waves per CU at most), so every load of
+// a lane -- its chunk, the taps of its row and of the next, and the owner's
+// history / head / tail inputs -- is issued up front and unconditionally,
+// through descriptors based at the wave's own rows (out-of-range offsets read
+// 0): one memory round trip per wave.
+template <int W, bool SILU, int ROUNDS>
+__global__ __launch_bounds__(kWaveSize) void fwd_tok_short_kernel(FwdTokParams p) {
+    constexpr int H = W - 1;
+    constexpr uint32_t kNone = 0xffffffffu;
+    constexpr int kNt = 2;
+    const int lane = threadIdx.x;
+    const uint32_t wbase = blockIdx.x * uint32_t(ROUNDS * kWaveSize);
+    if (wbase >= p.n_chunks) return;
+    const uint32_t T = p.T;
+    const uint32_t n_full = p.n_elems / kVec;
+    const SeqInfo s0 = seq_info(p.sb, p.sb.qsl, 0);      // used after the loads are issued
+
+    // The wave's reach: its elements [e0, e_end) and, for a row starting in
+    // them, that row's last width-1 inputs (less than T past e_end).
+    const uint32_t e0 = wbase * kVec;
+    const uint32_t e_end = e0 + uint32_t(ROUNDS * kWaveSize * kVec) < p.n_elems
+                               ? e0 + uint32_t(ROUNDS * kWaveSize * kVec) : p.n_elems;
+    const uint32_t xb0 = e0 >= uint32_t(kVec) ? e0 - kVec : 0;      // keeps the halo in range
+    const uint32_t x_hi = uint64_t(e_end) + T < p.n_elems ? e_end + T : p.n_elems;
+    const Rsrc xr = make_rsrc(p.x + xb0, int64_t(x_hi - xb0) * 2);
+    const uint32_t c_first = p.divT.div(e0);
+    const uint32_t c_last = p.divT.div(e_end - 1) + 1 < uint32_t(p.dim) ? p.divT.div(e_end - 1) + 1
+                                                                         : uint32_t(p.dim) - 1;
+    const uint32_t n_rows = c_last - c_first + 1;
+    const Rsrc wr = make_rsrc(p.w + int64_t(c_first) * p.w_sd, int64_t(n_rows) * p.w_sd * 2);
+    const Rsrc br = make_rsrc(p.bias ? p.bias + c_first : p.x, p.bias ? int64_t(n_rows) * 2 : 0);
+    const bool state_ok = p.sb.cs != nullptr && !s0.skip;
+    const Rsrc sr = make_rsrc(state_ok ? p.sb.cs + s0.line * p.sb.cs_sl + int64_t(c_first) * p.sb.cs_sd
+                                       : p.x,
+                              state_ok ? (int64_t(n_rows - 1) * p.sb.cs_sd + int64_t(H - 1) * p.sb.cs_st + 1) * 2
+                                       : 0);
+
+    u32x4 v[ROUNDS];
+    uint32_t hpos[ROUNDS], lead[ROUNDS];
+    uint32_t hb[ROUNDS][H], xh[ROUNDS][H], nb[ROUNDS][H];
+    PairTaps<W> ta[ROUNDS], tb[ROUNDS];
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+        const uint32_t chunk = wbase + r * kWaveSize + lane;
+        const bool full = chunk < n_full;
+        const uint32_t i0 = (full ? chunk : wbase) * kVec;
+        v[r] = buf_ld128<kNt>(xr, full ? (i0 - xb0) * 2 : kOob);
+        const uint32_t c = p.divT.div(i0);
+        const uint32_t t0 = i0 - c * T;
+        uint32_t hp = kNone, hrow = c;
+        lead[r] = 0;
+        if (full) {
+            if (t0 == 0) hp = i0;
+            else if (t0 + kVec > T) { hp = i0 + (T - t0); hrow = c + 1; }   // next row starts inside
+            else if (t0 < uint32_t(H)) lead[r] = H - t0;   // those outputs belong to the row's owner
+        }
+        hpos[r] = hp;
+        const bool own = hp != kNone;
+        ta[r] = buf_pair_taps<W>(wr, br, c - c_first, p.w_sd);
+        tb[r] = buf_pair_taps<W>(wr, br, hrow - c_first, p.w_sd);
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            hb[r][k] = buf_ld16(sr, own ? uint32_t(int64_t(hrow - c_first) * p.sb.cs_sd +
+                                                   int64_t(k) * p.sb.cs_st) * 2
+                                        : kOob);
+            xh[r][k] = buf_ld16(xr, own ? (hp + k - xb0) * 2 : kOob);
+            nb[r][k] = buf_ld16(xr, own ? (hp + T - H + k - xb0) * 2 : kOob);
+        }
+    }
+    const u32x2 prev = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(xr, lane == 0 && wbase > 0 ? (e0 - 4 - xb0) * 2
+                                                                                : kOob, 0, 0));
+
+    if (s0.skip) return;                                // padded sequence: nothing to do
+    if (s0.start != 0 || s0.end != int64_t(T)) {        // the sequence is not the whole row
+#pragma unroll 1
+        for (int r = 0; r < ROUNDS; ++r) {
+            const uint32_t chunk = wbase + r * kWaveSize + lane;
+            if (chunk < p.n_chunks) slow_chunk<W, SILU>(p, p.sb.qsl, chunk * kVec);
+        }
+        return;
+    }
+    const bool init = s0.init;
+    uint16_t *cs_line = p.sb.cs ? p.sb.cs + s0.line * p.sb.cs_sl : nullptr;
+
+    uint32_t prev_z = prev.x, prev_w = prev.y;
+    const int src_lane = (lane + kWaveSize - 1) & (kWaveSize - 1);
+    uint32_t hz[ROUNDS], hw[ROUNDS];
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+        const uint32_t rz = uint32_t(__shfl(int(v[r].z), src_lane));
+        const uint32_t rw = uint32_t(__shfl(int(v[r].w), src_lane));
+        hz[r] = lane == 0 ? prev_z : rz;
+        hw[r] = lane == 0 ? prev_w : rw;
+        prev_z = rz;
+        prev_w = rw;
+    }
+
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+        const uint32_t chunk = wbase + r * kWaveSize + lane;
+        if (chunk >= n_full) continue;
+        const uint32_t i0 = chunk * kVec;
+        Window win;
+        win.d[0] = hz[r];
+        win.d[1] = hw[r];
+        win.d[2] = v[r].x;
+        win.d[3] = v[r].y;
+        win.d[4] = v[r].z;
+        win.d[5] = v[r].w;
+        if (hpos[r] == kNone) {
+            const u32x4 o = fast_chunk<W, SILU>(win, ta[r]);
+            if (lead[r] == 0) {
+                st16_stream(p.out + size_t(i0), o);
+            } else {
+#pragma unroll
+                for (int j = 0; j < kVec; ++j)
+                    if (j >= int(lead[r])) p.out[size_t(i0) + j] = lane_elem(o, j);
+            }
+            continue;
+        }
+        const uint32_t hp = hpos[r];
+        uint32_t h[H];
+#pragma unroll
+        for (int k = 0; k < H; ++k) h[k] = init ? hb[r][k] : 0u;
+        st16_stream(p.out + size_t(i0), head_chunk<W, SILU>(win, i0, hp, ta[r], tb[r], h));
+        // head outputs past the chunk: u = history ++ row, output j uses u[j .. j+H]
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+            if (hp + j < i0 + kVec) continue;
+            float acc = tb[r].b;
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int m = j + k;                   // index into history ++ row
+                uint32_t bits = 0;
+#pragma unroll
+                for (int q = 0; q < H; ++q) {
+                    if (m == q) bits = h[q];
+                    if (m == H + q) bits = xh[r][q];
+                }
+                acc = __builtin_fmaf(tap_of<W>(tb[r], k), bf_one(uint16_t(bits)), acc);
+            }
+            p.out[size_t(hp) + j] = to_bf16(act<SILU>(acc));
+        }
+        if (cs_line) {
+            const uint32_t hrow = hp == i0 ? p.divT.div(i0) : p.divT.div(i0) + 1;
+#pragma unroll
+            for (int k = 0; k < H; ++k)
+                cs_line[int64_t(hrow) * p.sb.cs_sd + k * p.sb.cs_st] = uint16_t(nb[r][k]);
+        }
+    }
+#pragma unroll 1
+    for (int r = 0; r < ROUNDS; ++r) {
+        const uint32_t chunk = wbase + r * kWaveSize + lane;
+        if (chunk >= n_full && chunk < p.n_chunks) slow_chunk<W, SILU>(p, p.sb.qsl, chunk * kVec);
+    }
+}
+
+// One sequence with very short rows (T < kShortMinT): one lane per channel
+// row holds the row's history and inputs in registers.
+constexpr int kRowsBlock = 256;
+
+template <int W, bool SILU>
+__global__ __launch_bounds__(kRowsBlock) void fwd_tok_rows_kernel(FwdTokParams p) {
+    constexpr int H = W - 1;
+    constexpr int kMaxT = kShortMinT - 1;
+    const int32_t c = int32_t(blockIdx.x) * kRowsBlock + int32_t(threadIdx.x);
+    if (c >= p.dim) return;
+    const SeqInfo s0 = seq_info(p.sb, p.sb.qsl, 0);
+    if (s0.skip) return;
+    const int32_t a = int32_t(s0.start), L = int32_t(s0.end - s0.start);
+    if (L <= 0) return;
+    const uint16_t *xr = p.x + size_t(c) * p.T + a;
+    uint16_t *orow = p.out + size_t(c) * p.T + a;
+    uint16_t *st = p.sb.cs ? p.sb.cs + s0.line * p.sb.cs_sl + int64_t(c) * p.sb.cs_sd : nullptr;
+    uint16_t u[H + kMaxT];
+#pragma unroll
+    for (int k = 0; k < H; ++k) u[k] = s0.init ? st[k * p.sb.cs_st] : uint16_t(0);
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) u[H + t] = t < L ? xr[t] : uint16_t(0);
+    const Taps<W> tp = load_taps<W>(p, uint32_t(c));
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) {
+        if (t >= L) break;
+        float acc = tp.b;
+#pragma unroll
+        for (int k = 0; k < W; ++k) acc = __builtin_fmaf(tp.w[k], bf_one(u[t + k]), acc);
+        orow[t] = to_bf16(act<SILU>(acc));
+    }
+    if (st) {
+        // new state: u[L .. L+H), picked without dynamic indexing
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            uint16_t hv = 0;
+#pragma unroll
+            for (int m = 0; m < H + kMaxT; ++m)
+                if (m == L + k) hv = u[m];
+            st[k * p.sb.cs_st] = hv;
+        }
+    }
+}
+
 template <int W, bool SILU, bool VARLEN>
 __global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tokmajor_kernel(FwdTokParams p) {
     constexpr int H = W - 1;
@@ -522,9 +762,23 @@ hipError_t launch_ws(const FwdTokParams &p, hipStream_t s) {
     const uint32_t blocks = (p.n_chunks + kTokWavesPerBlock * kChunksPerWave - 1) /
                             (kTokWavesPerBlock * kChunksPerWave);
     const dim3 grid(blocks), block(kTokWavesPerBlock * kWaveSize);
-    if (p.sb.batch > 1) fwd_tokmajor_kernel<W, SILU, true><<<grid, block, 0, s>>>(p);
-    else if (p.T >= kWaveElems) fwd_tok_long_kernel<W, SILU><<<grid, block, 0, s>>>(p);
-    else fwd_tokmajor_kernel<W, SILU, false><<<grid, block, 0, s>>>(p);
+    if (p.sb.batch > 1) {
+        fwd_tokmajor_kernel<W, SILU, true><<<grid, block, 0, s>>>(p);
+    } else if (p.T >= kWaveElems) {
+        fwd_tok_long_kernel<W, SILU><<<grid, block, 0, s>>>(p);
+    } else if (p.T >= uint32_t(kShortMinT)) {
+        // two rounds per wave once that still leaves ~16 waves per CU
+        if (p.n_chunks >= uint32_t(kShortBigChunks)) {
+            const dim3 g((p.n_chunks + 2 * kWaveSize - 1) / (2 * kWaveSize));
+            fwd_tok_short_kernel<W, SILU, 2><<<g, dim3(kWaveSize), 0, s>>>(p);
+        } else {
+            const dim3 g((p.n_chunks + kWaveSize - 1) / kWaveSize);
+            fwd_tok_short_kernel<W, SILU, 1><<<g, dim3(kWaveSize), 0, s>>>(p);
+        }
+    } else {
+        const dim3 g((uint32_t(p.dim) + kRowsBlock - 1) / kRowsBlock);
+        fwd_tok_rows_kernel<W, SILU><<<g, dim3(kRowsBlock), 0, s>>>(p);
+    }
     return hipGetLastError();
 }
 

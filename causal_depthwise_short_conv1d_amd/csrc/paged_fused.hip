@@ -1,8 +1,13 @@
 // Paged sliding-window insert + depthwise causal conv in one launch --
 // Inkling sconv.py, fused_sconv / _fused_sconv_kernel, with the
-// token -> request search of its _seq_metadata_kernel done in-kernel.
+// token -> request search of its _seq_metadata_kernel done in-kernel.  One
+// launch may carry several of the conv streams that share the cache (the
+// page's module docstring: K, V, attention output and MLP output, each at its
+// own D sub-range): they share the per-token metadata and differ only in
+// their rows of x / out, taps and D offsets.
 //
-// Decomposition: a wave owns [kPagedBT tokens x 256 channels]; each lane owns
+// Decomposition: a wave owns [kPagedBT tokens x 256 channels of one stream]
+// (the slabs of all streams are numbered consecutively); each lane owns
 // 4 adjacent channels, which lie in one head (ws % 8 == 0), so every cache
 // access of a lane is one 8-byte vector at D offset off_s + c % ws.
 // Latency, not bandwidth, is the hazard here (decode rows are pure gathers
@@ -84,15 +89,22 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     // wave index within the block: uniform, and marked so for the compiler
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
     const uint32_t wt = blockIdx.x * kPagedWavesPerBlock + wave;
-    const int32_t slab = int32_t(wt % uint32_t(p.n_slabs));
-    const int32_t tt = int32_t(wt / uint32_t(p.n_slabs));
+    const int32_t gslab = int32_t(wt % uint32_t(p.total_slabs));
+    const int32_t tt = int32_t(wt / uint32_t(p.total_slabs));
     if (tt >= p.n_tiles) return;
+    // the wave's stream: the last one whose first slab is at or below gslab
+    int si = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxPagedStreams; ++i)
+        if (i < p.num_streams && p.s[i].slab0 <= gslab) si = i;
+    const PagedStream &st = p.s[si];
+    const int32_t slab = gslab - st.slab0;
 
     int32_t c0 = slab * kPSlab + lane * kPCpl;
-    const bool active = c0 < p.C;
+    const bool active = c0 < st.C;
     if (!active) c0 = 0;                 // idle lane: in-range reads, no writes
     // byte offsets of the lane's 4 channels inside a block and inside a row
-    const uint32_t coff = uint32_t((int64_t(c0 / p.ws) * p.c_sh + (p.off_s + c0 % p.ws)) * 2);
+    const uint32_t coff = uint32_t((int64_t(c0 / st.ws) * p.c_sh + (st.off_s + c0 % st.ws)) * 2);
     const uint32_t xoff = uint32_t(c0) * 2;
 
     // taps: pair q of channel ch is (w[ch][2q], w[ch][2q+1]); odd last tap fp32
@@ -100,11 +112,11 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     float wl[kPCpl], bf[kPCpl];
 #pragma unroll
     for (int ch = 0; ch < kPCpl; ++ch) {
-        const uint16_t *w = p.w + int64_t(c0 + ch) * p.w_sd;
+        const uint16_t *w = st.w + int64_t(c0 + ch) * st.w_sd;
 #pragma unroll
         for (int q = 0; q < W / 2; ++q) wp[q][ch] = uint32_t(w[2 * q]) | (uint32_t(w[2 * q + 1]) << 16);
         wl[ch] = (W & 1) ? bf_one(w[W - 1]) : 0.0f;
-        bf[ch] = p.bias ? bf_one(p.bias[c0 + ch]) : 0.0f;
+        bf[ch] = st.bias ? bf_one(st.bias[c0 + ch]) : 0.0f;
     }
 
     const int64_t tile_start = int64_t(tt) * kPagedBT;
@@ -159,9 +171,9 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     // x rows of the tile (and its width-1 predecessors), out rows of the tile
     const int64_t xbase = tile_start >= H ? tile_start - H : 0;
     const __amdgpu_buffer_rsrc_t xr =
-        rsrc(p.x + xbase * p.x_st, (p.T - xbase - 1) * p.x_st * 2 + int64_t(p.C) * 2);
+        rsrc(st.x + xbase * st.x_st, (p.T - xbase - 1) * st.x_st * 2 + int64_t(st.C) * 2);
     const __amdgpu_buffer_rsrc_t orr =
-        rsrc(p.out + tile_start * p.o_st, (p.T - tile_start - 1) * p.o_st * 2 + int64_t(p.C) * 2);
+        rsrc(st.out + tile_start * st.o_st, (p.T - tile_start - 1) * st.o_st * 2 + int64_t(st.C) * 2);
 
     // Previous width-1 rows of x for the tile's first tokens; rows before
     // the first token's request are never an intra tap of this tile.
@@ -170,7 +182,7 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
 #pragma unroll
     for (int k = 0; k < H; ++k) {
         const int64_t row = tile_start - H + k;
-        win[k] = (row >= 0 && row >= qs0) ? ld8<kNt>(xr, xoff, (row - xbase) * p.x_st * 2)
+        win[k] = (row >= 0 && row >= qs0) ? ld8<kNt>(xr, xoff, (row - xbase) * st.x_st * 2)
                                           : u32x2{0u, 0u};
     }
 
@@ -181,7 +193,7 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
         for (int u = 0; u < kPagedUnroll; ++u) {
             if (u0 + u < n_tok) {
                 const int64_t t = tile_start + u0 + u;
-                xv[u] = ld8<kNt>(xr, xoff, (t - xbase) * p.x_st * 2);
+                xv[u] = ld8<kNt>(xr, xoff, (t - xbase) * st.x_st * 2);
 #pragma unroll
                 for (int j = 0; j < H; ++j) {
                     const int32_t blk = __builtin_amdgcn_readlane(m_tblk[j], u0 + u);
@@ -239,7 +251,7 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
                     }
                 }
                 if (active)
-                    st8<kNt>(orr, xoff, (t - tile_start) * p.o_st * 2,
+                    st8<kNt>(orr, xoff, (t - tile_start) * st.o_st * 2,
                              u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
 #pragma unroll
                 for (int k = 0; k + 1 < H; ++k) win[k] = win[k + 1];
@@ -251,7 +263,7 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
 
 template <int W, bool SILU>
 hipError_t launch_ws(const PagedParams &p, bool residual, hipStream_t s) {
-    const uint64_t waves = uint64_t(p.n_tiles) * uint64_t(p.n_slabs);
+    const uint64_t waves = uint64_t(p.n_tiles) * uint64_t(p.total_slabs);
     const uint32_t blocks = uint32_t((waves + kPagedWavesPerBlock - 1) / kPagedWavesPerBlock);
     const dim3 grid(blocks), block(kPagedWavesPerBlock * kWaveSize);
     if (residual) paged_fused_kernel<W, SILU, true><<<grid, block, 0, s>>>(p);

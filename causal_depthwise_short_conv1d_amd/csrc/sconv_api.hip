@@ -14,7 +14,8 @@ namespace {
 
 constexpr int kVersionMajor = 1;
 constexpr int kMaxWidthHistory = SCONV_MAX_WIDTH - 1;
-constexpr int kVersionMinor = 2;
+static_assert(kMaxPagedStreams == SCONV_MAX_PAGED_STREAMS, "stream table size");
+constexpr int kVersionMinor = 3;
 
 // Byte range [lo, hi) covered by a strided bf16 tensor; empty when a size is 0.
 struct Span {
@@ -55,13 +56,14 @@ bool tokmajor_ok(int64_t sd, int64_t st, int64_t dim, int64_t T) {
 }
 
 // Tokens per channel-contiguous wave tile: enough tiles for ~32 waves per
-// CU (a full occupancy of the 256 CUs), never fewer than 32 tokens (halo
-// re-reads stay under 10%), never more than 256.
+// CU (a full occupancy of the 256 CUs), a multiple of the 8 rows a lane keeps
+// in flight, never more than 256.  Small problems get 8-token tiles: their
+// time is latency, and one batch of rows per wave beats the extra halo reads.
 int32_t chanlast_tile(int64_t T, int32_t n_slabs) {
     const int64_t target_waves = 256 * 32;
     int64_t bt = (T * n_slabs + target_waves - 1) / target_waves;
-    bt = (bt + 15) / 16 * 16;
-    if (bt < 32) bt = 32;
+    bt = (bt + 7) / 8 * 8;
+    if (bt < 8) bt = 8;
     if (bt > 256) bt = 256;
     return int32_t(bt);
 }
@@ -322,6 +324,120 @@ int sconv_seq_metadata(const int32_t *query_start_loc, int32_t num_reqs,
                                              query_start_out, stream));
 }
 
+int sconv_paged_fused_multi(int32_t num_streams, const void *const *x,
+                            const int64_t *x_stride_tok, const void *const *weight,
+                            const int64_t *w_stride_dim, const void *const *bias,
+                            const int32_t *off_s, const int32_t *ws, void *const *out,
+                            const int64_t *o_stride_tok, void *cache, int64_t c_stride_blk,
+                            int64_t c_stride_head, int64_t c_stride_slot, int64_t num_blocks,
+                            int32_t num_heads, int32_t block_size, int32_t head_dim,
+                            const int64_t *positions, const int64_t *slot_mapping,
+                            const int32_t *query_start_loc, int32_t num_reqs,
+                            const int32_t *block_table, int64_t bt_stride_req,
+                            int32_t max_blocks, int64_t num_tokens, int32_t width,
+                            int32_t activation, int32_t use_residual, hipStream_t stream) {
+    if (width < SCONV_MIN_WIDTH || width > SCONV_MAX_WIDTH) return SCONV_ERR_WIDTH;
+    if (activation != SCONV_ACT_NONE && activation != SCONV_ACT_SILU) return SCONV_ERR_ARG;
+    if (use_residual != 0 && use_residual != 1) return SCONV_ERR_ARG;
+    if (num_streams < 1 || num_streams > SCONV_MAX_PAGED_STREAMS) return SCONV_ERR_SHAPE;
+    if (!x || !x_stride_tok || !weight || !w_stride_dim || !off_s || !ws || !out ||
+        !o_stride_tok)
+        return SCONV_ERR_NULL;
+    if (num_tokens < 0 || num_reqs < 0 || max_blocks < 0 || num_blocks < 0) return SCONV_ERR_SHAPE;
+    if (num_heads < 1 || block_size < 1 || head_dim < 1) return SCONV_ERR_SHAPE;
+    for (int i = 0; i < num_streams; ++i)
+        if (ws[i] < 1 || off_s[i] < 0 || int64_t(off_s[i]) + ws[i] > head_dim)
+            return SCONV_ERR_SHAPE;
+    // every stream writes its own D sub-range of the inserted slots
+    for (int i = 0; i < num_streams; ++i)
+        for (int j = i + 1; j < num_streams; ++j)
+            if (off_s[i] < off_s[j] + ws[j] && off_s[j] < off_s[i] + ws[i]) return SCONV_ERR_ALIAS;
+    if (num_tokens == 0) return SCONV_OK;
+    if (num_tokens > INT32_MAX) return SCONV_ERR_SHAPE;
+    if (!cache || !positions || !slot_mapping || !query_start_loc ||
+        (num_reqs > 0 && max_blocks > 0 && !block_table))
+        return SCONV_ERR_NULL;
+    if (bt_stride_req < 0 || c_stride_blk < 0 || c_stride_head < 0 || c_stride_slot < 0)
+        return SCONV_ERR_STRIDE;
+    if (c_stride_blk % kVec || c_stride_head % kVec || c_stride_slot % kVec ||
+        !aligned(cache, 16) || !aligned(positions, 8) || !aligned(slot_mapping, 8) ||
+        !aligned(query_start_loc, 4) || !aligned(block_table, 4))
+        return SCONV_ERR_ALIGN;
+    if (c_stride_blk * 2 >= kMaxDescriptorSpan) return SCONV_ERR_SHAPE;
+    const Span sc = span_of(cache, {num_blocks, num_heads, block_size, head_dim},
+                            {c_stride_blk, c_stride_head, c_stride_slot, 1});
+
+    PagedParams p;
+    Span sx[kMaxPagedStreams], so[kMaxPagedStreams], sw[kMaxPagedStreams], sb[kMaxPagedStreams];
+    int64_t total_slabs = 0;
+    for (int i = 0; i < num_streams; ++i) {
+        const void *bi = bias ? bias[i] : nullptr;
+        if (!x[i] || !weight[i] || !out[i]) return SCONV_ERR_NULL;
+        const int64_t C = int64_t(num_heads) * ws[i];
+        if (C > INT32_MAX) return SCONV_ERR_SHAPE;
+        if (x_stride_tok[i] < C || o_stride_tok[i] < C || w_stride_dim[i] < width)
+            return SCONV_ERR_STRIDE;
+        if (ws[i] % kVec || off_s[i] % kVec || x_stride_tok[i] % kVec ||
+            o_stride_tok[i] % kVec || !aligned(x[i], 16) || !aligned(out[i], 16) ||
+            !aligned(weight[i], 2) || !aligned(bi, 2))
+            return SCONV_ERR_ALIGN;
+        // one descriptor spans a tile's rows of x (with the width-1 before it) or of out
+        const int64_t row_span = int64_t(kPagedBT + SCONV_MAX_WIDTH) *
+                                     (x_stride_tok[i] > o_stride_tok[i] ? x_stride_tok[i]
+                                                                        : o_stride_tok[i]) * 2 +
+                                 C * 2;
+        if (row_span >= kMaxDescriptorSpan) return SCONV_ERR_SHAPE;
+        sx[i] = span_of(x[i], {num_tokens, C}, {x_stride_tok[i], 1});
+        so[i] = span_of(out[i], {num_tokens, C}, {o_stride_tok[i], 1});
+        sw[i] = span_of(weight[i], {C, width}, {w_stride_dim[i], 1});
+        sb[i] = span_of(bi, {C}, {1});
+        PagedStream &st = p.s[i];
+        st.x = static_cast<const uint16_t *>(x[i]);
+        st.out = static_cast<uint16_t *>(out[i]);
+        st.w = static_cast<const uint16_t *>(weight[i]);
+        st.bias = static_cast<const uint16_t *>(bi);
+        st.x_st = x_stride_tok[i];
+        st.o_st = o_stride_tok[i];
+        st.w_sd = w_stride_dim[i];
+        st.off_s = off_s[i];
+        st.ws = ws[i];
+        st.C = int32_t(C);
+        st.slab0 = int32_t(total_slabs);
+        total_slabs += (C + kPagedSlab - 1) / kPagedSlab;
+    }
+    for (int i = num_streams; i < kMaxPagedStreams; ++i) p.s[i] = p.s[0];
+    // outputs overlap nothing; the cache overlaps no input
+    for (int i = 0; i < num_streams; ++i) {
+        if (overlap(so[i], sc) || overlap(sc, sx[i]) || overlap(sc, sw[i]) || overlap(sc, sb[i]))
+            return SCONV_ERR_ALIAS;
+        for (int j = 0; j < num_streams; ++j)
+            if (overlap(so[i], sx[j]) || overlap(so[i], sw[j]) || overlap(so[i], sb[j]) ||
+                (j != i && overlap(so[i], so[j])))
+                return SCONV_ERR_ALIAS;
+    }
+
+    p.num_streams = num_streams;
+    p.cache = static_cast<uint16_t *>(cache);
+    p.c_sb = c_stride_blk;
+    p.c_sh = c_stride_head;
+    p.c_sn = c_stride_slot;
+    p.num_blocks = num_blocks;
+    p.block_size = block_size;
+    p.pos = positions;
+    p.slot = slot_mapping;
+    p.qsl = query_start_loc;
+    p.num_reqs = num_reqs;
+    p.bt = block_table;
+    p.bt_sr = bt_stride_req;
+    p.max_blocks = block_table ? max_blocks : 0;
+    p.T = num_tokens;
+    p.n_tiles = int32_t((num_tokens + kPagedBT - 1) / kPagedBT);
+    if (uint64_t(p.n_tiles) * uint64_t(total_slabs) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;
+    p.total_slabs = int32_t(total_slabs);
+    return launch_status(launch_paged_fused(p, width, activation == SCONV_ACT_SILU,
+                                            use_residual != 0, stream));
+}
+
 int sconv_paged_fused(const void *x, int64_t x_stride_tok, const void *weight,
                       int64_t w_stride_dim, const void *bias, void *cache, int64_t c_stride_blk,
                       int64_t c_stride_head, int64_t c_stride_slot, int64_t num_blocks,
@@ -332,75 +448,13 @@ int sconv_paged_fused(const void *x, int64_t x_stride_tok, const void *weight,
                       int64_t num_tokens, int32_t width, int32_t activation,
                       int32_t use_residual, void *out, int64_t o_stride_tok,
                       hipStream_t stream) {
-    if (width < SCONV_MIN_WIDTH || width > SCONV_MAX_WIDTH) return SCONV_ERR_WIDTH;
-    if (activation != SCONV_ACT_NONE && activation != SCONV_ACT_SILU) return SCONV_ERR_ARG;
-    if (use_residual != 0 && use_residual != 1) return SCONV_ERR_ARG;
-    if (num_tokens < 0 || num_reqs < 0 || max_blocks < 0 || num_blocks < 0) return SCONV_ERR_SHAPE;
-    if (num_heads < 1 || ws < 1 || block_size < 1 || head_dim < 1 || off_s < 0 ||
-        int64_t(off_s) + ws > head_dim)
-        return SCONV_ERR_SHAPE;
-    if (num_tokens == 0) return SCONV_OK;
-    if (num_tokens > INT32_MAX) return SCONV_ERR_SHAPE;
-    if (!x || !weight || !cache || !positions || !slot_mapping || !query_start_loc || !out ||
-        (num_reqs > 0 && max_blocks > 0 && !block_table))
-        return SCONV_ERR_NULL;
-    const int64_t C = int64_t(num_heads) * ws;
-    if (C > INT32_MAX) return SCONV_ERR_SHAPE;
-    if (x_stride_tok < C || o_stride_tok < C || w_stride_dim < width || bt_stride_req < 0 ||
-        c_stride_blk < 0 || c_stride_head < 0 || c_stride_slot < 0)
-        return SCONV_ERR_STRIDE;
-    if (ws % kVec || off_s % kVec || c_stride_blk % kVec || c_stride_head % kVec ||
-        c_stride_slot % kVec || x_stride_tok % kVec || o_stride_tok % kVec || !aligned(x, 16) ||
-        !aligned(out, 16) || !aligned(cache, 16) || !aligned(weight, 2) || !aligned(bias, 2) ||
-        !aligned(positions, 8) || !aligned(slot_mapping, 8) || !aligned(query_start_loc, 4) ||
-        !aligned(block_table, 4))
-        return SCONV_ERR_ALIGN;
-
-    const Span sx = span_of(x, {num_tokens, C}, {x_stride_tok, 1});
-    const Span so = span_of(out, {num_tokens, C}, {o_stride_tok, 1});
-    const Span sc = span_of(cache, {num_blocks, num_heads, block_size, head_dim},
-                            {c_stride_blk, c_stride_head, c_stride_slot, 1});
-    const Span sw = span_of(weight, {C, width}, {w_stride_dim, 1});
-    const Span sbias = span_of(bias, {C}, {1});
-    if (overlap(so, sx) || overlap(so, sc) || overlap(so, sw) || overlap(so, sbias) ||
-        overlap(sc, sx) || overlap(sc, sw) || overlap(sc, sbias))
-        return SCONV_ERR_ALIAS;
-
-    PagedParams p;
-    p.x = static_cast<const uint16_t *>(x);
-    p.x_st = x_stride_tok;
-    p.out = static_cast<uint16_t *>(out);
-    p.o_st = o_stride_tok;
-    p.w = static_cast<const uint16_t *>(weight);
-    p.w_sd = w_stride_dim;
-    p.bias = static_cast<const uint16_t *>(bias);
-    p.cache = static_cast<uint16_t *>(cache);
-    p.c_sb = c_stride_blk;
-    p.c_sh = c_stride_head;
-    p.c_sn = c_stride_slot;
-    p.num_blocks = num_blocks;
-    p.block_size = block_size;
-    p.off_s = off_s;
-    p.ws = ws;
-    p.C = int32_t(C);
-    p.pos = positions;
-    p.slot = slot_mapping;
-    p.qsl = query_start_loc;
-    p.num_reqs = num_reqs;
-    p.bt = block_table;
-    p.bt_sr = bt_stride_req;
-    p.max_blocks = block_table ? max_blocks : 0;
-    p.T = num_tokens;
-    p.n_slabs = int32_t((C + kPagedSlab - 1) / kPagedSlab);
-    // one descriptor spans a tile's rows, another one cache block
-    const int64_t row_span = int64_t(kPagedBT + SCONV_MAX_WIDTH) *
-                                 (x_stride_tok > o_stride_tok ? x_stride_tok : o_stride_tok) * 2 + C * 2;
-    if (row_span >= kMaxDescriptorSpan || c_stride_blk * 2 >= kMaxDescriptorSpan)
-        return SCONV_ERR_SHAPE;
-    p.n_tiles = int32_t((num_tokens + kPagedBT - 1) / kPagedBT);
-    if (uint64_t(p.n_tiles) * uint64_t(p.n_slabs) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;
-    return launch_status(launch_paged_fused(p, width, activation == SCONV_ACT_SILU,
-                                            use_residual != 0, stream));
+    if (num_tokens > 0 && (!x || !weight || !out)) return SCONV_ERR_NULL;
+    return sconv_paged_fused_multi(1, &x, &x_stride_tok, &weight, &w_stride_dim, &bias, &off_s,
+                                   &ws, &out, &o_stride_tok, cache, c_stride_blk, c_stride_head,
+                                   c_stride_slot, num_blocks, num_heads, block_size, head_dim,
+                                   positions, slot_mapping, query_start_loc, num_reqs,
+                                   block_table, bt_stride_req, max_blocks, num_tokens, width,
+                                   activation, use_residual, stream);
 }
 
 }  // extern "C"

@@ -103,6 +103,28 @@ __device__ __forceinline__ uint16_t lane_elem(const u32x4 &v, int i) {
     return uint16_t((w >> ((i & 1) * 16)) & 0xffffu);
 }
 
+// ---------------------------------------------------- buffer descriptors --
+// A load through a buffer descriptor whose offset lies past the descriptor's
+// extent returns 0 without touching memory (a store is dropped).  Latency-
+// critical paths use this to issue every load unconditionally -- a load under
+// a branch makes the compiler wait for it before the branch joins, which
+// turns a handful of independent loads into a chain of round trips.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOob = 0x80000000u;            // an offset past every extent
+
+// `bytes` is clamped to [0, 2^31 - 1]; 0 makes every access out of range.
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes < 0x7fffffff ? int(bytes) : 0x7fffffff);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), n, 0x00020000);
+}
+__device__ __forceinline__ uint16_t buf_ld16(Rsrc r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+template <int AUX>
+__device__ __forceinline__ u32x4 buf_ld128(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+}
+
 // -------------------------------------------------- varlen sequence lookup --
 // Largest j in [0, n) with qsl[j] <= t (the token -> sequence search of the
 // Inkling page's metadata kernel).  Works for any qsl contents: the result

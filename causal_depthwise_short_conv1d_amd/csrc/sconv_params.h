@@ -99,18 +99,28 @@ struct UpdParams {
     int32_t batch, dim, seqlen, pad_slot_id;
 };
 
-struct PagedParams {
+constexpr int kMaxPagedStreams = 8;              // streams of one paged launch
+
+// One conv stream of the paged cache: its own input / output rows, taps and
+// D sub-range [off_s, off_s + ws) of every head; C = num_heads * ws.
+struct PagedStream {
     const uint16_t *x;
-    int64_t x_st;
     uint16_t *out;
-    int64_t o_st;
     const uint16_t *w;
-    int64_t w_sd;
     const uint16_t *bias;
+    int64_t x_st, o_st, w_sd;
+    int32_t off_s, ws, C;
+    int32_t slab0;      // index of the stream's first 256-channel slab in the launch
+};
+
+struct PagedParams {
+    PagedStream s[kMaxPagedStreams];
+    int32_t num_streams;
+    int32_t total_slabs;
     uint16_t *cache;
     int64_t c_sb, c_sh, c_sn;
     int64_t num_blocks;
-    int32_t block_size, off_s, ws, C;
+    int32_t block_size;
     const int64_t *pos;
     const int64_t *slot;
     const int32_t *qsl;
@@ -119,7 +129,6 @@ struct PagedParams {
     int64_t bt_sr;
     int32_t max_blocks;
     int64_t T;
-    int32_t n_slabs;
     int32_t n_tiles;
 };
 

@@ -50,7 +50,8 @@ def lib():
 def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("conv1d_fwd_varlen", "conv1d_update_decode", "conv1d_update",
-                 "sconv_paged_fused", "sconv_seq_metadata", "sconv_status_string",
+                 "sconv_paged_fused", "sconv_paged_fused_multi", "sconv_seq_metadata",
+                 "sconv_status_string",
                  "sconv_version"):
         assert name in fns
     assert sorted(S.exported_symbols()) == fns
@@ -66,7 +67,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert S.version() == (1, 2)
+    assert S.version() == (1, 3)
     for code in range(-8, 1):
         assert S.status_string(code) != "unknown status"
     assert S.status_string(-99) == "unknown status"
@@ -267,3 +268,35 @@ def test_seq_metadata_validation(lib):
     assert meta(lib, qs=ctypes.c_void_p(BASE + 3 * GB + 2)) == EALIGN
     assert meta(lib, qs=ctypes.c_void_p(BASE + 2 * GB + 64)) == EALIAS
     assert meta(lib, qs=addr(1)) == EALIAS        # output over query_start_loc
+
+
+# ---------------------------------------------------------- paged, multi --
+
+def pmulti(lib, n=2, offs=(0, 128), wss=(128, 128), xs=None, outs=None, **kw):
+    no_gpu()
+    VP, I64A, I32A = ctypes.c_void_p * n, ctypes.c_int64 * n, ctypes.c_int32 * n
+    xs = xs or [addr(10 + i) for i in range(n)]
+    outs = outs or [addr(20 + i) for i in range(n)]
+    a = dict(c=addr(3), csb=32 * 16 * 512, csh=16 * 512, csn=512, nb=64, H=32, N=16, D=512,
+             pos=addr(4), slot=addr(5), qsl=addr(6), R=3, bt=addr(7), btsr=64, mb=64, T=100,
+             width=4, act=1, res=1)
+    a.update(kw)
+    return lib.sconv_paged_fused_multi(
+        n, VP(*xs), I64A(*[32 * w for w in wss]), VP(*[addr(30 + i) for i in range(n)]),
+        I64A(*[4] * n), None, I32A(*offs), I32A(*wss), VP(*outs), I64A(*[32 * w for w in wss]),
+        a["c"], a["csb"], a["csh"], a["csn"], a["nb"], a["H"], a["N"], a["D"], a["pos"],
+        a["slot"], a["qsl"], a["R"], a["bt"], a["btsr"], a["mb"], a["T"], a["width"], a["act"],
+        a["res"], None)
+
+
+def test_paged_multi_validation(lib):
+    assert pmulti(lib, T=0) == OK
+    assert pmulti(lib, offs=(0, 64), T=0) == EALIAS              # D ranges overlap
+    assert pmulti(lib, n=1, offs=(400,), wss=(128,), T=0) == ESHAPE   # past head_dim
+    assert pmulti(lib, n=9, offs=tuple(range(0, 512, 64))[:8] + (0,), wss=(8,) * 9,
+                  T=0) == ESHAPE                                 # too many streams
+    assert pmulti(lib, xs=[addr(10), None]) == ENULL
+    assert pmulti(lib, outs=[addr(20), addr(10)]) == EALIAS      # out over another x
+    assert pmulti(lib, outs=[addr(20), addr(20)]) == EALIAS      # two outs coincide
+    assert pmulti(lib, outs=[addr(20), addr(3)]) == EALIAS       # out over the cache
+    assert pmulti(lib, offs=(0, 132), wss=(128, 120)) == EALIGN  # off_s not a multiple of 8

@@ -116,6 +116,50 @@ def test_long_rows_every_head_position(T, width, init):
     check_full(g, activation="silu", label=f"long rows T{T} W{width} silu")
 
 
+@pytest.mark.parametrize("T", [16, 17, 18, 19, 20, 23, 24, 25, 31, 33, 100, 127, 128, 129,
+                               514, 1000, 1023, 1024, 2047])
+@pytest.mark.parametrize("width", [2, 3, 4, 5])
+def test_short_rows_every_head_position(T, width):
+    """Rows of 16..2047 tokens: a chunk holds at most one row start; the
+    row's owner computes the head outputs that spill into the next chunk."""
+    d = W.single_sequence(dim=72, T=T, width=width, seed=T * 10 + width + 7, values="exact")
+    g = to_dev(d)
+    check_full(g, activation=None, exact=True, label=f"short rows T{T} W{width}")
+    check_full(g, activation="silu", label=f"short rows T{T} W{width} silu")
+    g["has_initial_state"] = torch.zeros(1, dtype=torch.bool, device=DEV)
+    check_full(g, activation=None, exact=True, label=f"short rows T{T} W{width} no init")
+
+
+@pytest.mark.parametrize("T", list(range(1, 16)))
+@pytest.mark.parametrize("width", [2, 3, 4, 5])
+def test_very_short_rows(T, width):
+    d = W.single_sequence(dim=300, T=T, width=width, seed=T * 10 + width + 9, values="exact")
+    g = to_dev(d)
+    check_full(g, activation=None, exact=True, label=f"very short rows T{T} W{width}")
+    check_full(g, activation="silu", label=f"very short rows T{T} W{width} silu")
+    g["has_initial_state"] = torch.zeros(1, dtype=torch.bool, device=DEV)
+    check_full(g, activation=None, exact=True, label=f"very short rows T{T} W{width} no init")
+
+
+@pytest.mark.parametrize("T,start", [(100, 5), (10, 3), (3000, 2)])
+def test_single_sequence_not_starting_at_zero(T, start):
+    """query_start_loc [start, T] (outside the documented contract, which
+    asks for a leading 0): the kernels still follow the oracle, which covers
+    tokens [start, T) only."""
+    d = W.single_sequence(dim=40, T=T, width=4, seed=T + start, values="exact")
+    d["query_start_loc"] = torch.tensor([start, T], dtype=torch.int32)
+    check_full(to_dev(d), activation=None, exact=True, label=f"start {start} T{T}")
+
+
+def test_prefill_dim8192_T1024_four_round_short_rows():
+    """Large enough for the four-round short-row variant."""
+    d = W.single_sequence(dim=8192, T=1024, width=4, seed=W.seed_for(3, 1), device=DEV)
+    g_out, g_cs = run_gpu(d)
+    r_out, r_cs = run_oracle(d)
+    assert_close(g_out, r_out, "dim8192 T1024 out")
+    assert_bits(g_cs, r_cs, "dim8192 T1024 state")
+
+
 def test_long_prefill_channel_contiguous():
     T = 4195
     d = W.single_sequence(dim=8192, T=T, width=4, seed=W.seed_for(3, 50), device=DEV,

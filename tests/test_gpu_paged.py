@@ -12,6 +12,7 @@ DEV = "cuda"
 BF = torch.bfloat16
 SMALL = dict(H=4, ws=16, N=4, D=48, off_s=16, num_blocks=96, n_decode=5,
              n_prefill=3, chunk=37, max_pos=60)
+SMALL_NO_OFF = {k: v for k, v in SMALL.items() if k != "off_s"}
 
 
 def run_both(d, activation="silu", residual=True, exact=False, cache_dev=None, label=""):
@@ -91,3 +92,80 @@ def test_paged_partial_slab_and_many_heads():
 def test_paged_only_decode_tokens():
     d = W.paged_batch(**dict(SMALL, n_decode=40, n_prefill=0), width=4, pad_frac=0.1, seed=500)
     run_both(d, label="decode only")
+
+
+# ---------------------------------------------------------- multi-stream --
+
+def run_multi(d, activation="silu", residual=True, exact=False, label=""):
+    """All streams of d in one sconv_paged_fused_multi launch against the
+    oracle run stream by stream on one cache (the D sub-ranges are disjoint,
+    so the order of the streams does not matter)."""
+    say(f"[paged multi] {label} streams={len(d['xs'])} T={d['x'].shape[0]}")
+    cache_gpu = d["cache"].to(DEV)
+    cache_ref = d["cache"].clone()
+    refs = []
+    for x, w, b, off in zip(d["xs"], d["weights"], d["biases"], d["offs"]):
+        o = torch.full(x.shape, float("nan"), dtype=BF)
+        oracle.paged(x, w, b, cache_ref, d["positions"], d["slot_mapping"],
+                     d["query_start_loc"], d["block_table"], off, d["ws"], o,
+                     activation=activation, use_residual=residual)
+        refs.append(o)
+    dv = lambda t: None if t is None else t.to(DEV)
+    outs = S.sconv_paged_fused_multi([dv(x) for x in d["xs"]], [dv(w) for w in d["weights"]],
+                                     cache_gpu, dv(d["positions"]), dv(d["slot_mapping"]),
+                                     dv(d["query_start_loc"]), dv(d["block_table"]), d["offs"],
+                                     d["ws"], activation=activation, use_residual=residual,
+                                     biases=[dv(b) for b in d["biases"]])
+    torch.cuda.synchronize()
+    for i, (o, r) in enumerate(zip(outs, refs)):
+        if exact:
+            assert_bits(o, r, f"{label} stream {i} out")
+        else:
+            assert_close(o, r, f"{label} stream {i} out")
+    assert_bits(cache_gpu, cache_ref, f"{label} cache")
+    return outs, cache_gpu
+
+
+def test_paged_multi_four_streams_full_size():
+    """The mixed step with the page's four streams filling D = 512."""
+    cfg = {k: v for k, v in W.PAGED_MIXED.items() if k != "off_s"}
+    d = W.paged_multi_batch(seed=W.seed_for(5, 1), **cfg)
+    run_multi(d, label="four streams")
+
+
+@pytest.mark.parametrize("width", [2, 3, 4, 5])
+@pytest.mark.parametrize("residual", [True, False])
+def test_paged_multi_small(width, residual):
+    d = W.paged_multi_batch(offsets=(32, 0, 16), width=width, pad_frac=0.1, trailing_pad=2,
+                            seed=600 + width, with_bias=(width % 2 == 1), min_pos=0, **SMALL_NO_OFF)
+    run_multi(d, residual=residual, label=f"small W{width}")
+
+
+def test_paged_multi_exact_bit_exact():
+    d = W.paged_multi_batch(offsets=(0, 24), width=4, pad_frac=0.2, seed=610, values="exact",
+                            with_bias=True, min_pos=0, **dict(SMALL_NO_OFF, ws=8, D=40))
+    run_multi(d, activation=None, exact=True, label="exact")
+
+
+def test_paged_multi_equals_single_stream_calls():
+    d = W.paged_multi_batch(offsets=(16, 0), width=4, pad_frac=0.1, seed=620, **SMALL_NO_OFF)
+    outs, cache_multi = run_multi(d, label="vs singles")
+    cache = d["cache"].to(DEV)
+    dv = lambda t: None if t is None else t.to(DEV)
+    for i, (x, w, off) in enumerate(zip(d["xs"], d["weights"], d["offs"])):
+        o = S.sconv_paged_fused(dv(x), dv(w), cache, dv(d["positions"]), dv(d["slot_mapping"]),
+                                dv(d["query_start_loc"]), dv(d["block_table"]), off, d["ws"],
+                                activation="silu", use_residual=True)
+        torch.cuda.synchronize()
+        assert_bits(o, outs[i], f"single stream {i}")
+    assert_bits(cache, cache_multi, "cache after singles")
+
+
+def test_paged_multi_rejects_overlapping_streams():
+    d = W.paged_multi_batch(offsets=(0, 8), width=4, seed=630, **SMALL_NO_OFF)
+    dv = lambda t: t.to(DEV)
+    with pytest.raises(S.SconvError):
+        S.sconv_paged_fused_multi([dv(x) for x in d["xs"]], [dv(w) for w in d["weights"]],
+                                  dv(d["cache"]), dv(d["positions"]), dv(d["slot_mapping"]),
+                                  dv(d["query_start_loc"]), dv(d["block_table"]), d["offs"],
+                                  d["ws"])
