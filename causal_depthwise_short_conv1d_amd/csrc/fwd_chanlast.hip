@@ -255,15 +255,25 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_chanlast_ker
     const Rsrc wr = make_rsrc(p.w + int64_t(c_lo) * p.w_sd, int64_t(n_ch) * p.w_sd * 2);
     const Rsrc br = make_rsrc(p.bias ? p.bias + c_lo : p.w, p.bias ? int64_t(n_ch) * 2 : 0);
     LaneTaps<W> tp;
+    const bool wide = FULL && p.w_sd == W && (reinterpret_cast<uintptr_t>(p.w) & 15) == 0 &&
+                      (reinterpret_cast<uintptr_t>(p.bias) & 7) == 0;
+    if (wide) {
+        // contiguous weights, whole lanes: three or fewer wide loads
+        const uint32_t lc0 = uint32_t(lane * kCpl);
+        load_taps4<W>(wr, lc0 < uint32_t(n_ch) ? lc0 * W * 2 : kOob, br,
+                      lc0 < uint32_t(n_ch) ? lc0 * 2 : kOob, tp.wp, tp.wl, tp.b);
+    } else {
 #pragma unroll
-    for (int ch = 0; ch < kCpl; ++ch) {
-        const int32_t lc = lane * kCpl + ch;              // channel within the slab
-        const uint32_t wo = lc < n_ch ? uint32_t(int64_t(lc) * p.w_sd * 2) : kOob;
+        for (int ch = 0; ch < kCpl; ++ch) {
+            const int32_t lc = lane * kCpl + ch;          // channel within the slab
+            const uint32_t wo = lc < n_ch ? uint32_t(int64_t(lc) * p.w_sd * 2) : kOob;
 #pragma unroll
-        for (int q = 0; q < W / 2; ++q)
-            tp.wp[q][ch] = uint32_t(buf_ld16(wr, wo + 4 * q)) | (uint32_t(buf_ld16(wr, wo + 4 * q + 2)) << 16);
-        tp.wl[ch] = (W & 1) ? bf_one(buf_ld16(wr, wo + 2 * (W - 1))) : 0.0f;
-        tp.b[ch] = bf_one(buf_ld16(br, lc < n_ch ? uint32_t(lc) * 2 : kOob));
+            for (int q = 0; q < W / 2; ++q)
+                tp.wp[q][ch] = uint32_t(buf_ld16(wr, wo + 4 * q)) |
+                               (uint32_t(buf_ld16(wr, wo + 4 * q + 2)) << 16);
+            tp.wl[ch] = (W & 1) ? bf_one(buf_ld16(wr, wo + 2 * (W - 1))) : 0.0f;
+            tp.b[ch] = bf_one(buf_ld16(br, lc < n_ch ? uint32_t(lc) * 2 : kOob));
+        }
     }
 
     const int64_t T = p.sb.total_T;

@@ -110,13 +110,22 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     // taps: pair q of channel ch is (w[ch][2q], w[ch][2q+1]); odd last tap fp32
     uint32_t wp[W / 2 > 0 ? W / 2 : 1][kPCpl];
     float wl[kPCpl], bf[kPCpl];
+    const Rsrc br = make_rsrc(st.bias ? st.bias : st.w, st.bias ? int64_t(st.C) * 2 : 0);
+    if (st.w_sd == W && int64_t(st.C) * W * 2 < kMaxDescriptorSpan &&
+        (reinterpret_cast<uintptr_t>(st.w) & 15) == 0 &&
+        (reinterpret_cast<uintptr_t>(st.bias) & 7) == 0) {
+        // contiguous weights: three or fewer wide loads per lane
+        const Rsrc wr = make_rsrc(st.w, int64_t(st.C) * W * 2);
+        load_taps4<W>(wr, uint32_t(c0) * W * 2, br, uint32_t(c0) * 2, wp, wl, bf);
+    } else {
 #pragma unroll
-    for (int ch = 0; ch < kPCpl; ++ch) {
-        const uint16_t *w = st.w + int64_t(c0 + ch) * st.w_sd;
+        for (int ch = 0; ch < kPCpl; ++ch) {
+            const uint16_t *w = st.w + int64_t(c0 + ch) * st.w_sd;
 #pragma unroll
-        for (int q = 0; q < W / 2; ++q) wp[q][ch] = uint32_t(w[2 * q]) | (uint32_t(w[2 * q + 1]) << 16);
-        wl[ch] = (W & 1) ? bf_one(w[W - 1]) : 0.0f;
-        bf[ch] = st.bias ? bf_one(st.bias[c0 + ch]) : 0.0f;
+            for (int q = 0; q < W / 2; ++q) wp[q][ch] = uint32_t(w[2 * q]) | (uint32_t(w[2 * q + 1]) << 16);
+            wl[ch] = (W & 1) ? bf_one(w[W - 1]) : 0.0f;
+            bf[ch] = bf_one(buf_ld16(br, uint32_t(c0 + ch) * 2));
+        }
     }
 
     const int64_t tile_start = int64_t(tt) * kPagedBT;

@@ -55,16 +55,19 @@ bool tokmajor_ok(int64_t sd, int64_t st, int64_t dim, int64_t T) {
     return st == 1 && (dim == 1 || sd == T);
 }
 
-// Tokens per channel-contiguous wave tile: enough tiles for ~32 waves per
-// CU (a full occupancy of the 256 CUs), a multiple of the 8 rows a lane keeps
-// in flight, never more than 256.  Small problems get 8-token tiles: their
-// time is latency, and one batch of rows per wave beats the extra halo reads.
-int32_t chanlast_tile(int64_t T, int32_t n_slabs) {
+// Tokens per channel-contiguous wave tile (measured on gfx950): a single
+// sequence runs fastest with 8-token tiles at every length -- one batch of
+// rows per wave, the most waves in flight, the halo rows re-read from L2.
+// A batch of sequences pays a search of query_start_loc and a segment split
+// per tile, so it takes the tile that leaves ~32 waves per CU, between 16
+// and 128 tokens.
+int32_t chanlast_tile(int64_t T, int32_t n_slabs, int32_t batch) {
+    if (batch <= 1) return 8;
     const int64_t target_waves = 256 * 32;
     int64_t bt = (T * n_slabs + target_waves - 1) / target_waves;
     bt = (bt + 7) / 8 * 8;
-    if (bt < 8) bt = 8;
-    if (bt > 256) bt = 256;
+    if (bt < 16) bt = 16;
+    if (bt > 128) bt = 128;
     return int32_t(bt);
 }
 
@@ -155,7 +158,7 @@ int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
         p.sb = sb;
         p.dim = dim;
         p.n_slabs = (dim + kClSlab - 1) / kClSlab;
-        p.bt = chanlast_tile(T, p.n_slabs);
+        p.bt = chanlast_tile(T, p.n_slabs, batch);
         // one descriptor spans a tile's rows (plus the spilled head) and one
         // state line
         const int64_t row_span = int64_t(p.bt + 2 * kMaxWidthHistory) *

@@ -125,6 +125,43 @@ __device__ __forceinline__ u32x4 buf_ld128(Rsrc r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
 }
 
+// Taps of 4 adjacent channels whose weights are stored contiguously
+// (row stride == width): 4*W bf16 = 8W bytes from byte `off` of `wr`, read
+// with 16- and 8-byte loads (W * 8 = 16, 24, 32, 40 bytes for W = 2..5; the
+// offset is a multiple of 8W, so every load is 8-byte aligned).  Pair q of
+// channel ch is (w[ch][2q], w[ch][2q+1]) as packed bf16, wl[ch] the odd last
+// tap; bias (4 bf16 at byte `boff` of `br`) as fp32.
+template <int W>
+__device__ __forceinline__ void load_taps4(Rsrc wr, uint32_t off, Rsrc br, uint32_t boff,
+                                           uint32_t (&wp)[W / 2 > 0 ? W / 2 : 1][4],
+                                           float (&wl)[4], float (&b)[4]) {
+    constexpr int kDw = 2 * W;                 // dwords of the 4 channels' taps
+    uint32_t d[kDw];
+#pragma unroll
+    for (int i = 0; i + 4 <= kDw; i += 4) {
+        const u32x4 v = buf_ld128<0>(wr, off + 4 * i);
+        d[i] = v.x; d[i + 1] = v.y; d[i + 2] = v.z; d[i + 3] = v.w;
+    }
+    if constexpr (kDw % 4 == 2) {
+        const u32x2 v = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(wr, off + 4 * (kDw - 2), 0, 0));
+        d[kDw - 2] = v.x; d[kDw - 1] = v.y;
+    }
+    // element e of the 4W is half (e & 1) of dword e / 2
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+#pragma unroll
+        for (int q = 0; q < W / 2; ++q) {
+            const int e = ch * W + 2 * q;
+            wp[q][ch] = (e & 1) ? __builtin_amdgcn_alignbit(d[(e + 1) / 2], d[e / 2], 16) : d[e / 2];
+        }
+        const int el = ch * W + W - 1;
+        wl[ch] = (W & 1) ? ((el & 1) ? bf_hi(d[el / 2]) : bf_lo(d[el / 2])) : 0.0f;
+    }
+    const u32x2 bv = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(br, boff, 0, 0));
+    b[0] = bf_lo(bv.x); b[1] = bf_hi(bv.x); b[2] = bf_lo(bv.y); b[3] = bf_hi(bv.y);
+}
+
 // -------------------------------------------------- varlen sequence lookup --
 // Largest j in [0, n) with qsl[j] <= t (the token -> sequence search of the
 // Inkling page's metadata kernel).  Works for any qsl contents: the result
