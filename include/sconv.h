@@ -68,6 +68,7 @@ typedef enum sconv_status {
 
 #define SCONV_MIN_WIDTH 2
 #define SCONV_MAX_WIDTH 5
+#define SCONV_MAX_PAGED_STREAMS 8   /* conv streams of one sconv_paged_fused_multi call */
 #define SCONV_ACT_NONE 0
 #define SCONV_ACT_SILU 1
 
@@ -324,6 +325,45 @@ int sconv_paged_fused(const void *x, int64_t x_stride_tok,
                       int32_t use_residual,
                       void *out, int64_t o_stride_tok,
                       hipStream_t stream);
+
+/*
+ * sconv_paged_fused_multi -- sconv_paged_fused for several conv streams that
+ * share one paged cache, in one launch.  The paged page's module docstring
+ * describes four such streams per layer (K, V, attention output, MLP output),
+ * each occupying its own D sub-range [off_s, off_s + ws) of every head of the
+ * same cache; every stream computes exactly what sconv_paged_fused computes
+ * for it, with the shared positions, slot_mapping, query_start_loc and
+ * block_table.  The streams share the per-token metadata work of the launch.
+ *
+ * num_streams  1..SCONV_MAX_PAGED_STREAMS.
+ * x, x_stride_tok, weight, w_stride_dim, off_s, ws, out, o_stride_tok:
+ *              HOST arrays of num_streams entries holding what
+ *              sconv_paged_fused takes for one stream (device pointers and
+ *              element strides; stream i has C_i = num_heads * ws[i]
+ *              channels).
+ * bias         NULL (no stream has a bias) or a HOST array of num_streams
+ *              device pointers, each NULL or [C_i] bf16.
+ * cache ... use_residual: as for sconv_paged_fused, shared by all streams.
+ * The D sub-ranges must be pairwise disjoint (else SCONV_ERR_ALIAS: two
+ * streams would insert into the same cache elements); no output may overlap
+ * any input, another output or the cache.  Other errors as for
+ * sconv_paged_fused; a NULL host array -> SCONV_ERR_NULL.
+ */
+int sconv_paged_fused_multi(int32_t num_streams,
+                            const void *const *x, const int64_t *x_stride_tok,
+                            const void *const *weight, const int64_t *w_stride_dim,
+                            const void *const *bias,
+                            const int32_t *off_s, const int32_t *ws,
+                            void *const *out, const int64_t *o_stride_tok,
+                            void *cache, int64_t c_stride_blk, int64_t c_stride_head,
+                            int64_t c_stride_slot, int64_t num_blocks,
+                            int32_t num_heads, int32_t block_size, int32_t head_dim,
+                            const int64_t *positions, const int64_t *slot_mapping,
+                            const int32_t *query_start_loc, int32_t num_reqs,
+                            const int32_t *block_table, int64_t bt_stride_req,
+                            int32_t max_blocks, int64_t num_tokens, int32_t width,
+                            int32_t activation, int32_t use_residual,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -37,6 +37,7 @@ SPEC_DECODE = dict(batch=64, dim=8192, width=4, seqlen=4, num_lines=256, n_pad=4
 PAGED_MIXED = dict(H=32, ws=128, N=16, D=512, off_s=128, num_blocks=4096,
                    width=4, n_decode=32, n_prefill=8, chunk=512, max_pos=8191,
                    pad_frac=0.05)
+PAGED_MULTI_OFFSETS = (0, 128, 256, 384)      # four streams filling D = 512
 
 
 def seed_for(config: int, variant: int = 0) -> int:
@@ -310,3 +311,25 @@ def paged_batch(H: int = 32, ws: int = 128, N: int = 16, D: int = 512,
         block_table=bt.to(torch.int32).to(device),
         off_s=off_s, ws=ws, block_size=N, requests=reqs,
     )
+
+
+def paged_multi_batch(offsets=PAGED_MULTI_OFFSETS, seed: int = 0, device="cpu",
+                      values: str = "normal", with_bias: bool = False, **paged_kw) -> dict:
+    """Several conv streams sharing one paged step (the paged page's module
+    docstring: K, V, attention output and MLP output at their own D
+    sub-ranges of the same cache).  The shared metadata, the cache and the
+    first stream come from paged_batch (with off_s = offsets[0]); every
+    further stream gets its own x, weight and (optionally) bias, drawn from
+    a generator seeded with seed + 2.  Returns the paged_batch dict plus
+    lists xs, weights, biases, offs."""
+    base = paged_batch(off_s=offsets[0], seed=seed, device=device, values=values,
+                       with_bias=with_bias, **paged_kw)
+    T, C = base["x"].shape
+    width = base["weight"].shape[1]
+    g = _gen(seed + 2, device)
+    xs, weights, biases = [base["x"]], [base["weight"]], [base["bias"]]
+    for _ in offsets[1:]:
+        xs.append(_draw((T, C), g, device, values))
+        weights.append(_draw((C, width), g, device, values))
+        biases.append(_draw((C,), g, device, values) if with_bias else None)
+    return dict(base, xs=xs, weights=weights, biases=biases, offs=list(offsets))
