@@ -37,7 +37,7 @@ namespace {
 constexpr int kChunksPerWave = kWaveSize * kTokRounds;
 constexpr uint32_t kWaveElems = kChunksPerWave * kVec;
 constexpr int kShortMinT = 16;                    // shortest row of the short-row kernel
-constexpr int kShortBigChunks = 256 * 16 * 2 * kWaveSize;  // 2 rounds from here on
+constexpr int kShortWaves = 256 * 8;             // waves that keep ~8 per CU busy
 
 // Weights of one channel for the dot2 path: taps as packed bf16 pairs
 // (w[2p], w[2p+1]), the odd last tap and the bias as fp32.
@@ -427,19 +427,33 @@ __device__ __forceinline__ PairTaps<W> buf_pair_taps(Rsrc wr, Rsrc br, uint32_t 
     return t;
 }
 
+// Lane `src`'s PairTaps (a cross-lane permute per value).
+template <int W>
+__device__ __forceinline__ PairTaps<W> shfl_taps(const PairTaps<W> &t, int src) {
+    PairTaps<W> r;
+#pragma unroll
+    for (int q = 0; q < W / 2; ++q) r.wp[q] = uint32_t(__shfl(int(t.wp[q]), src));
+    r.wl = (W & 1) ? __shfl(t.wl, src) : 0.0f;
+    r.b = __shfl(t.b, src);
+    return r;
+}
+
 // One sequence whose rows are short (kShortMinT <= T < one wave): a chunk
 // holds at most one row start, and every element of a chunk before that
 // start has its whole window inside its own row (T >= 16 > 8 + width-1).
-// The lane whose chunk holds a row start owns that row's history: together
-// with its chunk it loads the cached state, the row's first width-1 inputs
-// and its last width-1 inputs; it computes the chunk (head_chunk), the head
-// outputs that spill into the next chunk, and writes the new state, while
-// the next chunk leaves those spilled outputs alone.
-// Latency decides this kernel (a few waves per CU at most), so every load of
-// a lane -- its chunk, the taps of its row and of the next, and the owner's
-// history / head / tail inputs -- is issued up front and unconditionally,
-// through descriptors based at the wave's own rows (out-of-range offsets read
-// 0): one memory round trip per wave.
+//
+// The rows a wave touches (at most ROUNDS*512/T + 2 <= 64) are handled by
+// "row lanes": lane j loads, once per wave, the taps of row c_first + j and,
+// when that row starts inside the wave, its cached history, its first
+// width-1 inputs and its last width-1 inputs -- and writes the row's new
+// state, so the one reader of a history is also its one writer.  A chunk
+// lane takes its row's taps, and for a row start inside its chunk the
+// history and head inputs, from the row lane with cross-lane permutes; it
+// computes that chunk with head_chunk and the head outputs that spill into
+// the next chunk, which leaves them alone.  A wave thus issues ROUNDS chunk
+// loads plus a fixed handful of row loads, all up front and unconditional
+// (through descriptors based at the wave's own rows; out-of-range offsets
+// read 0): one memory round trip per wave.
 template <int W, bool SILU, int ROUNDS>
 __global__ __launch_bounds__(kWaveSize) void fwd_tok_short_kernel(FwdTokParams p) {
     constexpr int H = W - 1;
@@ -452,18 +466,18 @@ __global__ __launch_bounds__(kWaveSize) void fwd_tok_short_kernel(FwdTokParams p
     const uint32_t n_full = p.n_elems / kVec;
     const SeqInfo s0 = seq_info(p.sb, p.sb.qsl, 0);      // used after the loads are issued
 
-    // The wave's reach: its elements [e0, e_end) and, for a row starting in
-    // them, that row's last width-1 inputs (less than T past e_end).
+    // The wave's elements [e0, e_end) and rows [c_first, c_last]; a row that
+    // starts in a full chunk of the wave is owned by the wave.
     const uint32_t e0 = wbase * kVec;
     const uint32_t e_end = e0 + uint32_t(ROUNDS * kWaveSize * kVec) < p.n_elems
                                ? e0 + uint32_t(ROUNDS * kWaveSize * kVec) : p.n_elems;
+    const uint32_t own_end = e_end < n_full * kVec ? e_end : n_full * kVec;
+    const uint32_t c_first = p.divT.div(e0);
+    const uint32_t c_last = p.divT.div(e_end - 1);
+    const uint32_t n_rows = c_last - c_first + 1;
     const uint32_t xb0 = e0 >= uint32_t(kVec) ? e0 - kVec : 0;      // keeps the halo in range
     const uint32_t x_hi = uint64_t(e_end) + T < p.n_elems ? e_end + T : p.n_elems;
     const Rsrc xr = make_rsrc(p.x + xb0, int64_t(x_hi - xb0) * 2);
-    const uint32_t c_first = p.divT.div(e0);
-    const uint32_t c_last = p.divT.div(e_end - 1) + 1 < uint32_t(p.dim) ? p.divT.div(e_end - 1) + 1
-                                                                         : uint32_t(p.dim) - 1;
-    const uint32_t n_rows = c_last - c_first + 1;
     const Rsrc wr = make_rsrc(p.w + int64_t(c_first) * p.w_sd, int64_t(n_rows) * p.w_sd * 2);
     const Rsrc br = make_rsrc(p.bias ? p.bias + c_first : p.x, p.bias ? int64_t(n_rows) * 2 : 0);
     const bool state_ok = p.sb.cs != nullptr && !s0.skip;
@@ -472,44 +486,35 @@ __global__ __launch_bounds__(kWaveSize) void fwd_tok_short_kernel(FwdTokParams p
                               state_ok ? (int64_t(n_rows - 1) * p.sb.cs_sd + int64_t(H - 1) * p.sb.cs_st + 1) * 2
                                        : 0);
 
+    // chunk loads
     u32x4 v[ROUNDS];
-    uint32_t hpos[ROUNDS], lead[ROUNDS];
-    uint32_t hb[ROUNDS][H], xh[ROUNDS][H], nb[ROUNDS][H];
-    PairTaps<W> ta[ROUNDS], tb[ROUNDS];
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
         const uint32_t chunk = wbase + r * kWaveSize + lane;
-        const bool full = chunk < n_full;
-        const uint32_t i0 = (full ? chunk : wbase) * kVec;
-        v[r] = buf_ld128<kNt>(xr, full ? (i0 - xb0) * 2 : kOob);
-        const uint32_t c = p.divT.div(i0);
-        const uint32_t t0 = i0 - c * T;
-        uint32_t hp = kNone, hrow = c;
-        lead[r] = 0;
-        if (full) {
-            if (t0 == 0) hp = i0;
-            else if (t0 + kVec > T) { hp = i0 + (T - t0); hrow = c + 1; }   // next row starts inside
-            else if (t0 < uint32_t(H)) lead[r] = H - t0;   // those outputs belong to the row's owner
-        }
-        hpos[r] = hp;
-        const bool own = hp != kNone;
-        ta[r] = buf_pair_taps<W>(wr, br, c - c_first, p.w_sd);
-        tb[r] = buf_pair_taps<W>(wr, br, hrow - c_first, p.w_sd);
-#pragma unroll
-        for (int k = 0; k < H; ++k) {
-            hb[r][k] = buf_ld16(sr, own ? uint32_t(int64_t(hrow - c_first) * p.sb.cs_sd +
-                                                   int64_t(k) * p.sb.cs_st) * 2
-                                        : kOob);
-            xh[r][k] = buf_ld16(xr, own ? (hp + k - xb0) * 2 : kOob);
-            nb[r][k] = buf_ld16(xr, own ? (hp + T - H + k - xb0) * 2 : kOob);
-        }
+        v[r] = buf_ld128<kNt>(xr, chunk < n_full ? (chunk * kVec - xb0) * 2 : kOob);
     }
     const u32x2 prev = __builtin_bit_cast(
         u32x2, __builtin_amdgcn_raw_buffer_load_b64(xr, lane == 0 && wbase > 0 ? (e0 - 4 - xb0) * 2
                                                                                 : kOob, 0, 0));
+    // row loads: lane j <-> row c_first + j
+    const uint32_t my_row = c_first + uint32_t(lane);
+    const bool row_in = uint32_t(lane) < n_rows;
+    const uint32_t my_hp = my_row * T;
+    const bool row_own = row_in && my_hp >= e0 && my_hp < own_end;
+    const PairTaps<W> rt = buf_pair_taps<W>(wr, br, row_in ? uint32_t(lane) : 0x7fffu, p.w_sd);
+    uint32_t rh[H], rx[H], rn[H];
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+        rh[k] = buf_ld16(sr, row_own ? uint32_t(int64_t(lane) * p.sb.cs_sd + int64_t(k) * p.sb.cs_st) * 2
+                                     : kOob);
+        rx[k] = buf_ld16(xr, row_own ? (my_hp + k - xb0) * 2 : kOob);
+        rn[k] = buf_ld16(xr, row_own ? (my_hp + T - H + k - xb0) * 2 : kOob);
+    }
 
     if (s0.skip) return;                                // padded sequence: nothing to do
-    if (s0.start != 0 || s0.end != int64_t(T)) {        // the sequence is not the whole row
+    // the sequence is not the whole row, or (never, with the host's choice of
+    // ROUNDS) the wave spans more rows than it has lanes: element path
+    if (s0.start != 0 || s0.end != int64_t(T) || n_rows > uint32_t(kWaveSize)) {
 #pragma unroll 1
         for (int r = 0; r < ROUNDS; ++r) {
             const uint32_t chunk = wbase + r * kWaveSize + lane;
@@ -518,73 +523,86 @@ __global__ __launch_bounds__(kWaveSize) void fwd_tok_short_kernel(FwdTokParams p
         return;
     }
     const bool init = s0.init;
-    uint16_t *cs_line = p.sb.cs ? p.sb.cs + s0.line * p.sb.cs_sl : nullptr;
+    // packed per-row history and head inputs, to be permuted to chunk lanes
+    uint32_t hpk[(H + 1) / 2], xpk[(H + 1) / 2];
+#pragma unroll
+    for (int k = 0; k < (H + 1) / 2; ++k) {
+        const uint32_t h0 = init ? rh[2 * k] : 0u;
+        const uint32_t h1 = (2 * k + 1 < H && init) ? rh[2 * k + 1 < H ? 2 * k + 1 : 0] : 0u;
+        hpk[k] = (h0 & 0xffffu) | (h1 << 16);
+        xpk[k] = (rx[2 * k] & 0xffffu) | ((2 * k + 1 < H ? rx[2 * k + 1 < H ? 2 * k + 1 : 0] : 0u) << 16);
+    }
 
     uint32_t prev_z = prev.x, prev_w = prev.y;
     const int src_lane = (lane + kWaveSize - 1) & (kWaveSize - 1);
-    uint32_t hz[ROUNDS], hw[ROUNDS];
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
         const uint32_t rz = uint32_t(__shfl(int(v[r].z), src_lane));
         const uint32_t rw = uint32_t(__shfl(int(v[r].w), src_lane));
-        hz[r] = lane == 0 ? prev_z : rz;
-        hw[r] = lane == 0 ? prev_w : rw;
-        prev_z = rz;
-        prev_w = rw;
-    }
-
-#pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
-        const uint32_t chunk = wbase + r * kWaveSize + lane;
-        if (chunk >= n_full) continue;
-        const uint32_t i0 = chunk * kVec;
         Window win;
-        win.d[0] = hz[r];
-        win.d[1] = hw[r];
+        win.d[0] = lane == 0 ? prev_z : rz;
+        win.d[1] = lane == 0 ? prev_w : rw;
         win.d[2] = v[r].x;
         win.d[3] = v[r].y;
         win.d[4] = v[r].z;
         win.d[5] = v[r].w;
-        if (hpos[r] == kNone) {
-            const u32x4 o = fast_chunk<W, SILU>(win, ta[r]);
-            if (lead[r] == 0) {
+        prev_z = rz;
+        prev_w = rw;
+
+        const uint32_t chunk = wbase + r * kWaveSize + lane;
+        const uint32_t i0 = (chunk < n_full ? chunk : wbase) * kVec;
+        const uint32_t c = p.divT.div(i0);
+        const uint32_t t0 = i0 - c * T;
+        uint32_t hp = kNone, hrow = c, lead = 0;
+        if (t0 == 0) hp = i0;
+        else if (t0 + kVec > T) { hp = i0 + (T - t0); hrow = c + 1; }   // next row starts inside
+        else if (t0 < uint32_t(H)) lead = H - t0;      // those outputs belong to the row's owner
+        const PairTaps<W> ta = shfl_taps<W>(rt, int(c - c_first));
+        const PairTaps<W> tb = shfl_taps<W>(rt, int(hrow - c_first));
+        uint32_t h2[(H + 1) / 2], x2[(H + 1) / 2];
+#pragma unroll
+        for (int k = 0; k < (H + 1) / 2; ++k) {
+            h2[k] = uint32_t(__shfl(int(hpk[k]), int(hrow - c_first)));
+            x2[k] = uint32_t(__shfl(int(xpk[k]), int(hrow - c_first)));
+        }
+        if (chunk >= n_full) continue;                 // ragged tail: element path below
+
+        if (hp == kNone) {
+            const u32x4 o = fast_chunk<W, SILU>(win, ta);
+            if (lead == 0) {
                 st16_stream(p.out + size_t(i0), o);
             } else {
 #pragma unroll
                 for (int j = 0; j < kVec; ++j)
-                    if (j >= int(lead[r])) p.out[size_t(i0) + j] = lane_elem(o, j);
+                    if (j >= int(lead)) p.out[size_t(i0) + j] = lane_elem(o, j);
             }
             continue;
         }
-        const uint32_t hp = hpos[r];
         uint32_t h[H];
 #pragma unroll
-        for (int k = 0; k < H; ++k) h[k] = init ? hb[r][k] : 0u;
-        st16_stream(p.out + size_t(i0), head_chunk<W, SILU>(win, i0, hp, ta[r], tb[r], h));
+        for (int k = 0; k < H; ++k) h[k] = (h2[k >> 1] >> ((k & 1) * 16)) & 0xffffu;
+        st16_stream(p.out + size_t(i0), head_chunk<W, SILU>(win, i0, hp, ta, tb, h));
         // head outputs past the chunk: u = history ++ row, output j uses u[j .. j+H]
 #pragma unroll
         for (int j = 0; j < H; ++j) {
             if (hp + j < i0 + kVec) continue;
-            float acc = tb[r].b;
+            float acc = tb.b;
 #pragma unroll
             for (int k = 0; k < W; ++k) {
                 const int m = j + k;                   // index into history ++ row
-                uint32_t bits = 0;
-#pragma unroll
-                for (int q = 0; q < H; ++q) {
-                    if (m == q) bits = h[q];
-                    if (m == H + q) bits = xh[r][q];
-                }
-                acc = __builtin_fmaf(tap_of<W>(tb[r], k), bf_one(uint16_t(bits)), acc);
+                const uint32_t bits = m < H ? (h2[m >> 1] >> ((m & 1) * 16))
+                                            : (x2[(m - H) >> 1] >> (((m - H) & 1) * 16));
+                acc = __builtin_fmaf(tap_of<W>(tb, k), bf_one(uint16_t(bits & 0xffffu)), acc);
             }
             p.out[size_t(hp) + j] = to_bf16(act<SILU>(acc));
         }
-        if (cs_line) {
-            const uint32_t hrow = hp == i0 ? p.divT.div(i0) : p.divT.div(i0) + 1;
+    }
+    // the row lanes write the new states of the rows this wave owns
+    if (row_own && p.sb.cs) {
+        uint16_t *cs_line = p.sb.cs + s0.line * p.sb.cs_sl;
 #pragma unroll
-            for (int k = 0; k < H; ++k)
-                cs_line[int64_t(hrow) * p.sb.cs_sd + k * p.sb.cs_st] = uint16_t(nb[r][k]);
-        }
+        for (int k = 0; k < H; ++k)
+            cs_line[int64_t(my_row) * p.sb.cs_sd + k * p.sb.cs_st] = uint16_t(rn[k]);
     }
 #pragma unroll 1
     for (int r = 0; r < ROUNDS; ++r) {
@@ -767,8 +785,15 @@ hipError_t launch_ws(const FwdTokParams &p, hipStream_t s) {
     } else if (p.T >= kWaveElems) {
         fwd_tok_long_kernel<W, SILU><<<grid, block, 0, s>>>(p);
     } else if (p.T >= uint32_t(kShortMinT)) {
-        // two rounds per wave once that still leaves ~16 waves per CU
-        if (p.n_chunks >= uint32_t(kShortBigChunks)) {
+        // Rounds per wave, measured on gfx950: one round (the most waves in
+        // flight) up to 512K chunks, two from there, four from 2M, where a
+        // wave's row loads are worth amortising; a wave's rows
+        // (ROUNDS*512/T + 2) must fit its 64 lanes.
+        const uint32_t T = p.T;
+        if (T >= 64 && p.n_chunks >= uint32_t(16 * kShortWaves * kWaveSize)) {
+            const dim3 g((p.n_chunks + 4 * kWaveSize - 1) / (4 * kWaveSize));
+            fwd_tok_short_kernel<W, SILU, 4><<<g, dim3(kWaveSize), 0, s>>>(p);
+        } else if (T >= 32 && p.n_chunks >= uint32_t(4 * kShortWaves * kWaveSize)) {
             const dim3 g((p.n_chunks + 2 * kWaveSize - 1) / (2 * kWaveSize));
             fwd_tok_short_kernel<W, SILU, 2><<<g, dim3(kWaveSize), 0, s>>>(p);
         } else {

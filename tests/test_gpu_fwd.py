@@ -130,6 +130,17 @@ def test_short_rows_every_head_position(T, width):
     check_full(g, activation=None, exact=True, label=f"short rows T{T} W{width} no init")
 
 
+@pytest.mark.parametrize("T,dim", [(33, 130000), (47, 96000), (1000, 4200), (100, 170000),
+                                   (2047, 8200)])
+def test_short_rows_two_and_four_rounds(T, dim):
+    """Sizes that select the two- and four-round short-row variants (a wave
+    spans up to 64 rows), ragged row lengths, every output compared."""
+    d = W.single_sequence(dim=dim, T=T, width=4, seed=T + dim, values="exact", device=DEV)
+    say(f"[fwd] short rows T{T} dim{dim}")
+    check_full(d, activation=None, exact=True, label=f"short rows T{T} dim{dim}")
+    check_full(d, activation="silu", label=f"short rows T{T} dim{dim} silu")
+
+
 @pytest.mark.parametrize("T", list(range(1, 16)))
 @pytest.mark.parametrize("width", [2, 3, 4, 5])
 def test_very_short_rows(T, width):
