@@ -487,8 +487,43 @@ def summarize(argv):
     print("\n".join(lines))
 
 
+def summarize_trace(argv):
+    """Kernel-only durations of every libsconv dispatch in a rocprofv3
+    --kernel-trace run, grouped by (kernel, grid size) in first-launch order:
+
+        python bench.py summarize-trace TRACE_DIR OUT_TXT TITLE CMDLINE
+
+    Each group is one workload of the run (the benchmark launches its
+    workloads one after another, each with its own grid)."""
+    import csv
+    import glob
+    import re
+    trace_dir, out_txt, title, cmdline = argv[:4]
+    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not f:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    rows = sorted(csv.DictReader(open(f[0])), key=lambda r: int(r["Start_Timestamp"]))
+    groups = {}
+    for r in rows:
+        if "sconv::" not in r["Kernel_Name"]:
+            continue
+        name = re.sub(r"\(.*", "", r["Kernel_Name"].replace("(anonymous namespace)::", "")
+                      .replace("void ", ""))
+        key = (name, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"# rocprofv3 kernel trace summary: {title}", f"# command: {cmdline}", "",
+             "kernel | grid (threads) | workgroup | calls | median us | min us | max us"]
+    for (name, grid, wg), d in groups.items():
+        lines.append(f"{name} | {grid} | {wg} | {len(d)} | {statistics.median(d):.2f} | "
+                     f"{min(d):.2f} | {max(d):.2f}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "summarize":
         summarize(sys.argv[2:])
+    elif len(sys.argv) > 1 and sys.argv[1] == "summarize-trace":
+        summarize_trace(sys.argv[2:])
     else:
         main()
