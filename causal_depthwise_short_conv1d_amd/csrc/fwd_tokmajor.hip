@@ -38,6 +38,8 @@ constexpr int kChunksPerWave = kWaveSize * kTokRounds;
 constexpr uint32_t kWaveElems = kChunksPerWave * kVec;
 constexpr int kShortMinT = 16;                    // shortest row of the short-row kernel
 constexpr int kShortWaves = 256 * 8;             // waves that keep ~8 per CU busy
+constexpr int kLongWaves = 4;                     // waves per long-row block (fewer, larger
+                                                  // workgroups dispatch faster at 10^5 waves)
 
 // Weights of one channel for the dot2 path: taps as packed bf16 pairs
 // (w[2p], w[2p+1]), the odd last tap and the bias as fp32.
@@ -274,13 +276,12 @@ __device__ void slow_chunk(const FwdTokParams &p, const int32_t *qsl, uint32_t i
 // next wave (its owner computes them element by element and the next wave's
 // first chunk skips them).
 template <int W, bool SILU>
-__global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tok_long_kernel(FwdTokParams p) {
+__global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(FwdTokParams p) {
     constexpr int H = W - 1;
     constexpr uint32_t kNone = 0xffffffffu;
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wave = threadIdx.x / kWaveSize;
-    const uint32_t tile = blockIdx.x;
-    const uint32_t wbase = (tile * kTokWavesPerBlock + wave) * uint32_t(kChunksPerWave);
+    const uint32_t wbase = (blockIdx.x * kLongWaves + wave) * uint32_t(kChunksPerWave);
     if (wbase >= p.n_chunks) return;
     const SeqInfo s0 = seq_info(p.sb, p.sb.qsl, 0);
     if (s0.skip) return;                                    // padded sequence: nothing to do
@@ -655,6 +656,238 @@ __global__ __launch_bounds__(kRowsBlock) void fwd_tok_rows_kernel(FwdTokParams p
     }
 }
 
+// A batch of sequences in rows of at least one wave (total tokens T >=
+// 2048), in one launch of two kinds of workgroups:
+//   * chunk workgroups stream x as the long kernel does (a wave spans at most
+//     two rows, so the row and its taps are wave-uniform) and compute every
+//     chunk from the plain window; an element is stored only when it is at
+//     least width-1 tokens into an unpadded sequence, because only then do
+//     all its taps lie inside its own sequence.  They never touch a state.
+//   * head workgroups give one lane to each (sequence, channel): it reads the
+//     cached history (when the sequence continues from it), computes the
+//     first width-1 outputs, and writes the new state -- the single reader
+//     and writer of that history.
+// The two write disjoint elements, so no ordering between them is needed.
+// query_start_loc and the per-sequence lines and flags are staged in LDS.
+constexpr int kVarWaves = 4;                      // waves per block sharing the staged tables
+
+template <int W, bool SILU>
+__global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(FwdTokParams p,
+                                                                                uint32_t chunk_blocks) {
+    constexpr int H = W - 1;
+    __shared__ int32_t qsl[kQslLdsMax];                 // the host guarantees batch + 1 fits
+    __shared__ uint8_t skip_of[kQslLdsMax];
+    const int32_t B = p.sb.batch;
+    const uint32_t T = p.T;
+
+    // A chunk wave issues its x loads before the tables are staged, so the
+    // staging's round trip and barrier overlap them.  Every load of a whole
+    // wave is unconditional (a load under a branch would wait for the ones
+    // before it); only the last wave checks its chunks.
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wave = threadIdx.x / kWaveSize;
+    const uint32_t wbase = (blockIdx.x * kVarWaves + wave) * uint32_t(kChunksPerWave);
+    const uint32_t n_full = p.n_elems / kVec;
+    const bool chunk_wave = blockIdx.x < chunk_blocks && wbase < p.n_chunks;
+    u32x4 v[kTokRounds];
+    uint32_t prev_z = 0, prev_w = 0;
+    if (chunk_wave) {
+        if (wbase + kChunksPerWave <= n_full) {
+#pragma unroll
+            for (int r = 0; r < kTokRounds; ++r)
+                v[r] = ld16_stream(p.x + size_t(wbase + r * kWaveSize + lane) * kVec);
+        } else {
+#pragma unroll
+            for (int r = 0; r < kTokRounds; ++r) {
+                const uint32_t ch = wbase + r * kWaveSize + lane;
+                if (ch < n_full) v[r] = ld16_stream(p.x + size_t(ch) * kVec);
+                else if (ch < p.n_chunks) v[r] = ld8_partial(p.x + size_t(ch) * kVec, int(p.n_elems - ch * kVec));
+                else v[r] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        if (lane == 0 && wbase > 0) {
+            const u32x2 t2 = *reinterpret_cast<const u32x2 *>(p.x + size_t(wbase) * kVec - 4);
+            prev_z = t2.x;
+            prev_w = t2.y;
+        }
+    }
+
+    for (int i = threadIdx.x; i <= B; i += kVarWaves * kWaveSize) {
+        qsl[i] = p.sb.qsl[i];
+        if (i < B) {
+            const int64_t line = p.sb.cache_idx ? int64_t(p.sb.cache_idx[i]) : int64_t(i);
+            skip_of[i] = (p.sb.cache_idx && line == p.sb.pad_slot_id) ||
+                         (p.sb.cs && (line < 0 || line >= p.sb.num_lines));
+        }
+    }
+    __syncthreads();
+
+    if (blockIdx.x >= chunk_blocks) {
+        // ---- head lanes: (sequence, channel) = divmod(g, dim)
+        const uint64_t g = uint64_t(blockIdx.x - chunk_blocks) * (kVarWaves * kWaveSize) + threadIdx.x;
+        const int32_t sq = int32_t(g / uint64_t(p.dim));
+        const uint32_t c = uint32_t(g - uint64_t(sq) * uint64_t(p.dim));
+        if (sq >= B) return;
+        const int64_t st = qsl[sq] < 0 ? 0 : (qsl[sq] > int32_t(T) ? int64_t(T) : int64_t(qsl[sq]));
+        const int64_t en = qsl[sq + 1] < st ? st : (qsl[sq + 1] > int32_t(T) ? int64_t(T) : int64_t(qsl[sq + 1]));
+        const int64_t L = en - st;
+        if (L <= 0 || skip_of[sq]) return;
+        const int64_t line = p.sb.cache_idx ? int64_t(p.sb.cache_idx[sq]) : int64_t(sq);
+        const bool init = p.sb.cs && p.sb.has_init && p.sb.has_init[sq] != 0;
+        // every load at once, from addresses valid whether or not the value is
+        // wanted (the values are selected afterwards)
+        const size_t row0 = size_t(c) * T;
+        const uint16_t *hbase = init ? p.sb.cs + line * p.sb.cs_sl + int64_t(c) * p.sb.cs_sd : p.x + row0;
+        const Taps<W> tp = load_taps<W>(p, c);
+        uint32_t h[H], xh[H], nb[H];
+#pragma unroll
+        for (int q = 0; q < H; ++q) {
+            const uint16_t hv = hbase[init ? q * p.sb.cs_st : 0];
+            const uint16_t xv = p.x[row0 + size_t(st) + (q < L ? q : 0)];
+            const uint16_t nv = p.x[row0 + size_t(L >= H ? en - H + q : st)];
+            h[q] = init ? hv : 0u;
+            xh[q] = q < L ? xv : 0u;
+            nb[q] = nv;
+        }
+        // outputs j < min(L, H): u = history ++ sequence, output j uses u[j .. j+H]
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+            if (j >= L) break;
+            float acc = tp.b;
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int m = j + k;                   // compile-time: a register, not an index
+                const uint32_t bits = m < H ? h[m < H ? m : 0] : xh[m - H < H ? m - H : 0];
+                acc = __builtin_fmaf(tp.w[k], bf_one(uint16_t(bits)), acc);
+            }
+            p.out[row0 + size_t(st) + j] = to_bf16(act<SILU>(acc));
+        }
+        if (p.sb.cs) {
+            // new state: the last H entries of history ++ sequence
+#pragma unroll
+            for (int q = 0; q < H; ++q) {
+                uint32_t bits = nb[q];
+#pragma unroll
+                for (int e = 0; e < H; ++e) {
+                    if (L + q == e) bits = h[e];
+                    if (L < H && L + q == H + e) bits = xh[e];
+                }
+                p.sb.cs[line * p.sb.cs_sl + int64_t(c) * p.sb.cs_sd + q * p.sb.cs_st] = uint16_t(bits);
+            }
+        }
+        return;
+    }
+
+    // ---- chunk lanes
+    if (!chunk_wave) return;
+
+    // sequence bounds clamped into [0, T], as the head lanes see them
+    auto bounds = [&](int32_t q, int64_t &st, int64_t &en) {
+        st = qsl[q] < 0 ? 0 : (qsl[q] > int32_t(T) ? int64_t(T) : int64_t(qsl[q]));
+        en = qsl[q + 1] < st ? st : (qsl[q + 1] > int32_t(T) ? int64_t(T) : int64_t(qsl[q + 1]));
+    };
+    // wave-uniform rows (at most two) and their taps
+    const uint32_t e_first = wbase * kVec;
+    const uint32_t cA = p.divT.div(e_first);
+    const uint32_t row_a = cA * T, row_end = row_a + T;
+    const PairTaps<W> tA = uniform(load_pair_taps<W>(p, cA));
+    const PairTaps<W> tB = (cA + 1 < uint32_t(p.dim)) ? uniform(load_pair_taps<W>(p, cA + 1)) : tA;
+    // the sequence of the wave's first element; lanes of the first row walk
+    // forward from it (a wave spans a few sequences), the second row searches
+    const int32_t s_wave = __builtin_amdgcn_readfirstlane(seq_search(qsl, B, int64_t(e_first - row_a)));
+
+    const int src_lane = (lane + kWaveSize - 1) & (kWaveSize - 1);
+    uint32_t hz[kTokRounds], hw[kTokRounds];
+#pragma unroll
+    for (int r = 0; r < kTokRounds; ++r) {
+        const uint32_t rz = uint32_t(__shfl(int(v[r].z), src_lane));
+        const uint32_t rw = uint32_t(__shfl(int(v[r].w), src_lane));
+        hz[r] = lane == 0 ? prev_z : rz;
+        hw[r] = lane == 0 ? prev_w : rw;
+        prev_z = rz;
+        prev_w = rw;
+    }
+
+#pragma unroll
+    for (int r = 0; r < kTokRounds; ++r) {
+        const uint32_t chunk = wbase + r * kWaveSize + lane;
+        if (chunk >= p.n_chunks) continue;
+        const uint32_t i0 = chunk * kVec;
+        const uint32_t n = chunk < n_full ? uint32_t(kVec) : p.n_elems - i0;   // elements present
+        const bool in_b = i0 >= row_end;
+        const int64_t t0 = int64_t(i0) - int64_t(in_b ? row_end : row_a);
+        // the sequence of the first element, and whether the chunk is plain:
+        // one row, one unpadded sequence, every element past its head
+        int32_t sq = in_b ? seq_search(qsl, B, t0) : s_wave;
+        if (!in_b)
+            while (sq + 1 < B && qsl[sq + 1] <= t0) ++sq;
+        int64_t st, en;
+        bounds(sq, st, en);
+        const bool row_cross = !in_b && i0 + n > row_end;
+        const bool plain = n == uint32_t(kVec) && !row_cross && t0 >= st + H && t0 + kVec <= en &&
+                           !skip_of[sq];
+        uint32_t keep = 0;                             // bit j: store element j
+        if (plain) {
+            keep = 0xffu;
+        } else {
+            // segment by segment (a run of elements of one sequence of one
+            // row): keep those at least H into an unpadded sequence
+            int64_t row_base = in_b ? int64_t(row_end) : int64_t(row_a);
+            uint32_t j = 0;
+            while (j < n) {
+                int64_t t = int64_t(i0) + j - row_base;
+                if (t >= int64_t(T)) {                 // crossed into the next row
+                    row_base += T;
+                    t -= T;
+                    sq = seq_search(qsl, B, t);
+                    bounds(sq, st, en);
+                } else if (t >= en) {
+                    while (sq + 1 < B && qsl[sq + 1] <= t) ++sq;
+                    bounds(sq, st, en);
+                }
+                if (t < st || t >= en) {               // a token no sequence covers
+                    ++j;
+                    continue;
+                }
+                const uint32_t jend = uint32_t(en - t) < n - j ? j + uint32_t(en - t) : n;
+                const int64_t skip_n = st + H - t;    // head elements of the run, owned by a head lane
+                const uint32_t jkeep = skip_n <= 0 ? j : (uint64_t(skip_n) < jend - j ? j + uint32_t(skip_n) : jend);
+                if (!skip_of[sq]) keep |= ((1u << jend) - 1u) & ~((1u << jkeep) - 1u);
+                j = jend;
+            }
+        }
+        if (!keep) continue;
+        Window win;
+        win.d[0] = hz[r];
+        win.d[1] = hw[r];
+        win.d[2] = v[r].x;
+        win.d[3] = v[r].y;
+        win.d[4] = v[r].z;
+        win.d[5] = v[r].w;
+        u32x4 o = fast_chunk<W, SILU>(win, in_b ? tB : tA);
+        if (row_cross) {                               // elements from row_end on use the next row's taps
+            const u32x4 ob = fast_chunk<W, SILU>(win, tB);
+            const uint32_t kb = row_end - i0;
+            const uint32_t av[4] = {o.x, o.y, o.z, o.w}, bv[4] = {ob.x, ob.y, ob.z, ob.w};
+            uint32_t rr[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t lo = (2 * d < int(kb) ? av[d] : bv[d]) & 0xffffu;
+                const uint32_t hi = (2 * d + 1 < int(kb) ? av[d] : bv[d]) & 0xffff0000u;
+                rr[d] = lo | hi;
+            }
+            o = u32x4{rr[0], rr[1], rr[2], rr[3]};
+        }
+        if (keep == 0xffu) {
+            st16_stream(p.out + size_t(i0), o);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kVec; ++j)
+                if (keep & (1u << j)) p.out[size_t(i0) + j] = lane_elem(o, j);
+        }
+    }
+}
+
 template <int W, bool SILU, bool VARLEN>
 __global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tokmajor_kernel(FwdTokParams p) {
     constexpr int H = W - 1;
@@ -780,10 +1013,18 @@ hipError_t launch_ws(const FwdTokParams &p, hipStream_t s) {
     const uint32_t blocks = (p.n_chunks + kTokWavesPerBlock * kChunksPerWave - 1) /
                             (kTokWavesPerBlock * kChunksPerWave);
     const dim3 grid(blocks), block(kTokWavesPerBlock * kWaveSize);
-    if (p.sb.batch > 1) {
+    if (p.sb.batch > 1 && p.T >= kWaveElems && p.sb.batch + 1 <= kQslLdsMax) {
+        const uint32_t waves = (p.n_chunks + kChunksPerWave - 1) / kChunksPerWave;
+        const uint32_t chunk_blocks = (waves + kVarWaves - 1) / kVarWaves;
+        const uint64_t heads = uint64_t(p.sb.batch) * uint64_t(p.dim);
+        const uint32_t head_blocks = uint32_t((heads + kVarWaves * kWaveSize - 1) / (kVarWaves * kWaveSize));
+        fwd_tok_varlen_kernel<W, SILU><<<dim3(chunk_blocks + head_blocks), dim3(kVarWaves * kWaveSize), 0, s>>>(
+            p, chunk_blocks);
+    } else if (p.sb.batch > 1) {
         fwd_tokmajor_kernel<W, SILU, true><<<grid, block, 0, s>>>(p);
     } else if (p.T >= kWaveElems) {
-        fwd_tok_long_kernel<W, SILU><<<grid, block, 0, s>>>(p);
+        const uint32_t lb = (p.n_chunks + kLongWaves * kChunksPerWave - 1) / (kLongWaves * kChunksPerWave);
+        fwd_tok_long_kernel<W, SILU><<<dim3(lb), dim3(kLongWaves * kWaveSize), 0, s>>>(p);
     } else if (p.T >= uint32_t(kShortMinT)) {
         // Rounds per wave, measured on gfx950: one round (the most waves in
         // flight) up to 512K chunks, two from there, four from 2M, where a

@@ -222,6 +222,27 @@ def test_varlen_batch(width, layout):
             assert torch.all(g_out[:, qsl[s]:qsl[s + 1]] == -7.0)
 
 
+@pytest.mark.parametrize("width", [2, 3, 4, 5])
+@pytest.mark.parametrize("seed,dim", [(0, 24), (1, 37)])
+def test_varlen_long_rows_token_contiguous(width, seed, dim):
+    """A batch in token-contiguous rows of at least one wave: hundreds of
+    sequences of 0..24 tokens (starts at every chunk offset, two and more
+    starts per chunk, heads shorter than the window) plus a few long ones,
+    pads, mixed initial state, and (dim 37) a ragged last chunk; every output
+    and state compared bit for bit with exact values."""
+    g = torch.Generator().manual_seed(800 + 10 * width + seed)
+    lens = torch.randint(0, 25, (300,), generator=g).tolist() + [300, 1000, 7, 0, 513]
+    perm = torch.randperm(len(lens), generator=g).tolist()
+    lens = [lens[i] for i in perm]
+    d = W.varlen_batch(lengths=lens, dim=dim, width=width, seed=810 + width + seed,
+                       num_lines=len(lens) + 8, n_pad=12, layout="dim_tok", values="exact")
+    assert int(d["query_start_loc"][-1]) >= 2048
+    say(f"[fwd] varlen long rows W{width} T={int(d['query_start_loc'][-1])}")
+    gd = to_dev(d)
+    check_full(gd, activation=None, exact=True, label=f"varlen long rows W{width}")
+    check_full(gd, activation="silu", label=f"varlen long rows W{width} silu")
+
+
 # ------------------------------------------------------------ small cases --
 
 SMALL_CASES = []
