@@ -311,10 +311,13 @@ def extras(torch, S, W, dev):
         f"{warm*1e3:.2f} us/launch in a graph")
     del d, so
 
-    # varlen continuous batch, widths 2..5, channel-contiguous
+    # varlen continuous batch, widths 2..5, channel-contiguous (T, dim) storage;
+    # then width 4 token-contiguous (dim, T)
     vl = {}
-    for width in (2, 3, 4, 5):
-        d = W.varlen_batch(dim=8192, width=width, seed=W.seed_for(4, width), device=dev)
+    for width, layout in ((2, "tok_dim"), (3, "tok_dim"), (4, "tok_dim"), (5, "tok_dim"),
+                          (4, "dim_tok")):
+        d = W.varlen_batch(dim=8192, width=width, seed=W.seed_for(4, width), device=dev,
+                           layout=layout)
         out = torch.empty_like(d["x"])
         lens = d["lengths"].tolist()
         lines = d["cache_indices"].tolist()
@@ -330,9 +333,10 @@ def extras(torch, S, W, dev):
                                          has_initial_state=d["has_initial_state"], out=out)
         fn()
         ms = event_time_ms(fn, 10, flush)
-        vl[f"W{width}"] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
-                           "tokens": sum(kept), "tokens_per_s": round(sum(kept) / ms * 1e3, 1)}
-        log(f"[bench] varlen W{width}: {ms*1e3:.1f} us {nb/ms/1e6:.0f} GB/s")
+        key = f"W{width}" if layout == "tok_dim" else f"W{width}_{layout}"
+        vl[key] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
+                   "tokens": sum(kept), "tokens_per_s": round(sum(kept) / ms * 1e3, 1)}
+        log(f"[bench] varlen {key}: {ms*1e3:.1f} us {nb/ms/1e6:.0f} GB/s")
         del d, out, cs
     ex["varlen_64seq_dim8192"] = vl
 
