@@ -895,7 +895,8 @@ __global__ __launch_bounds__(kTokWavesPerBlock * kWaveSize) void fwd_tokmajor_ke
     const int32_t *qsl = p.sb.qsl;
     if constexpr (VARLEN) {
         if (p.sb.batch + 1 <= kQslLdsMax) {
-            for (int i = threadIdx.x; i <= p.sb.batch; i += blockDim.x) s_qsl[i] = p.sb.qsl[i];
+            for (int i = threadIdx.x; i <= p.sb.batch; i += kTokWavesPerBlock * kWaveSize)
+                s_qsl[i] = p.sb.qsl[i];
             __syncthreads();
             qsl = s_qsl;
         }

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     __shared__ int32_t s_qsl[kQslLdsMax];
     const bool use_lds = p.num_reqs + 1 <= kQslLdsMax;
     if (use_lds) {
-        for (int i = threadIdx.x; i <= p.num_reqs; i += blockDim.x) s_qsl[i] = p.qsl[i];
+        for (int i = threadIdx.x; i <= p.num_reqs; i += kPagedWavesPerBlock * kWaveSize) s_qsl[i] = p.qsl[i];
         __syncthreads();
     }
     const int32_t *qsl = use_lds ? s_qsl : p.qsl;
