@@ -243,6 +243,36 @@ def test_varlen_long_rows_token_contiguous(width, seed, dim):
     check_full(gd, activation="silu", label=f"varlen long rows W{width} silu")
 
 
+@pytest.mark.parametrize("layout", ["dim_tok", "tok_dim"])
+@pytest.mark.parametrize("nseq", [2047, 2048])
+def test_varlen_batch_size_at_lds_table_limit(nseq, layout):
+    """2047 sequences fill the LDS copy of query_start_loc exactly; 2048 take
+    the kernels' global-table path.  Lengths 0..3 (most sequences shorter
+    than the window), pads, mixed initial state; every output and state
+    compared bit for bit with exact values."""
+    g = torch.Generator().manual_seed(nseq)
+    lens = torch.randint(0, 4, (nseq,), generator=g).tolist()
+    dim = 5 if layout == "dim_tok" else 8              # (T, dim) rows: a multiple of 8
+    d = W.varlen_batch(lengths=lens, dim=dim, width=4, seed=nseq + 1, num_lines=nseq + 3,
+                       n_pad=40, layout=layout, values="exact")
+    assert int(d["query_start_loc"][-1]) >= 2048
+    say(f"[fwd] varlen {nseq} sequences {layout}")
+    check_full(to_dev(d), activation=None, exact=True, label=f"varlen {nseq} seqs {layout}")
+
+
+@pytest.mark.parametrize("layout", ["dim_tok", "tok_dim"])
+@pytest.mark.parametrize("total", [2047, 2048])
+def test_varlen_total_tokens_at_wave_limit(total, layout):
+    """A batch whose rows are one wave (2048 tokens) long, and one token
+    shorter: the two sides of the token-contiguous varlen dispatch."""
+    lens = [700, 3, 0, 1, 900, 2, total - 1606]
+    d = W.varlen_batch(lengths=lens, dim=67 if layout == "dim_tok" else 72, width=4, seed=total,
+                       num_lines=12, n_pad=1, layout=layout, values="exact")
+    assert int(d["query_start_loc"][-1]) == total
+    check_full(to_dev(d), activation=None, exact=True, label=f"varlen T={total} {layout}")
+    check_full(to_dev(d), activation="silu", label=f"varlen T={total} {layout} silu")
+
+
 # ------------------------------------------------------------ small cases --
 
 SMALL_CASES = []
