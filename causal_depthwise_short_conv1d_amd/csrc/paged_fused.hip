@@ -60,9 +60,9 @@ typedef unsigned int ui32x2 __attribute__((ext_vector_type(2)));
 // A buffer descriptor over `bytes` bytes from `base` (offsets past the end
 // read 0 / drop the write).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0),
-                                             int(bytes < 0x7fffffff ? bytes : 0x7fffffff),
-                                             0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(base), short(0),
+        int(bytes < 0 ? 0 : (bytes < 0x7fffffff ? bytes : 0x7fffffff)), 0x00020000);
 }
 template <int AUX>
 __device__ __forceinline__ u32x2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff, int64_t soff) {
@@ -78,20 +78,12 @@ template <int W, bool SILU, bool RESID>
 __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_kernel(PagedParams p) {
     constexpr int H = W - 1;
     __shared__ int32_t s_qsl[kQslLdsMax];
-    const bool use_lds = p.num_reqs + 1 <= kQslLdsMax;
-    if (use_lds) {
-        for (int i = threadIdx.x; i <= p.num_reqs; i += kPagedWavesPerBlock * kWaveSize) s_qsl[i] = p.qsl[i];
-        __syncthreads();
-    }
-    const int32_t *qsl = use_lds ? s_qsl : p.qsl;
-
     const int lane = threadIdx.x & (kWaveSize - 1);
     // wave index within the block: uniform, and marked so for the compiler
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
     const uint32_t wt = blockIdx.x * kPagedWavesPerBlock + wave;
     const int32_t gslab = int32_t(wt % uint32_t(p.total_slabs));
     const int32_t tt = int32_t(wt / uint32_t(p.total_slabs));
-    if (tt >= p.n_tiles) return;
     // the wave's stream: the last one whose first slab is at or below gslab
     int si = 0;
 #pragma unroll
@@ -106,6 +98,35 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     // byte offsets of the lane's 4 channels inside a block and inside a row
     const uint32_t coff = uint32_t((int64_t(c0 / st.ws) * p.c_sh + (st.off_s + c0 % st.ws)) * 2);
     const uint32_t xoff = uint32_t(c0) * 2;
+
+    // What depends only on the tile is issued before the query_start_loc
+    // staging and the metadata round trips: the token's slot and position
+    // (lane = token) and the width-1 rows before the tile.  A wave past the
+    // last tile reads clamped addresses and zeros, and stops after the
+    // barrier.  (Issuing the tile's own rows here as well was measured: it
+    // raises registers and was slower.)
+    const int64_t tile_start = int64_t(tt) * kPagedBT;
+    const int64_t xbase = tile_start >= H ? tile_start - H : 0;
+    const __amdgpu_buffer_rsrc_t xr =
+        rsrc(st.x + xbase * st.x_st, (p.T - xbase - 1) * st.x_st * 2 + int64_t(st.C) * 2);
+    u32x2 win[H];
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+        const int64_t row = tile_start - H + k;
+        win[k] = ld8<kNt>(xr, xoff, row >= 0 ? (row - xbase) * st.x_st * 2 : int64_t(kOob));
+    }
+    const int64_t t_lane = tile_start + (lane < kPagedBT ? lane : 0);
+    const int64_t t_safe = t_lane < p.T ? t_lane : p.T - 1;
+    const int64_t slot_l = p.slot[t_safe];
+    const int64_t pos_l = p.pos[t_safe];
+
+    const bool use_lds = p.num_reqs + 1 <= kQslLdsMax;
+    if (use_lds) {
+        for (int i = threadIdx.x; i <= p.num_reqs; i += kPagedWavesPerBlock * kWaveSize) s_qsl[i] = p.qsl[i];
+        __syncthreads();
+    }
+    const int32_t *qsl = use_lds ? s_qsl : p.qsl;
+    if (tt >= p.n_tiles) return;
 
     // taps: pair q of channel ch is (w[ch][2q], w[ch][2q+1]); odd last tap fp32
     uint32_t wp[W / 2 > 0 ? W / 2 : 1][kPCpl];
@@ -128,7 +149,6 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
         }
     }
 
-    const int64_t tile_start = int64_t(tt) * kPagedBT;
     const int n_tok = int((p.T - tile_start) < kPagedBT ? (p.T - tile_start) : kPagedBT);
     int64_t actual = p.num_reqs > 0 ? int64_t(qsl[p.num_reqs]) : 0;
     actual = actual < 0 ? 0 : (actual > p.T ? p.T : actual);
@@ -150,8 +170,8 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     }
     if (lane < n_tok) {
         const int64_t t = tile_start + lane;
-        const int64_t slot = p.slot[t];
-        const int64_t pos = p.pos[t];
+        const int64_t slot = slot_l;
+        const int64_t pos = pos_l;
         m_pad = (slot < 0 || t >= actual) ? 1 : 0;
         if (!m_pad) {
             const int64_t sb = slot / p.block_size;
@@ -177,23 +197,15 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
         }
     }
 
-    // x rows of the tile (and its width-1 predecessors), out rows of the tile
-    const int64_t xbase = tile_start >= H ? tile_start - H : 0;
-    const __amdgpu_buffer_rsrc_t xr =
-        rsrc(st.x + xbase * st.x_st, (p.T - xbase - 1) * st.x_st * 2 + int64_t(st.C) * 2);
     const __amdgpu_buffer_rsrc_t orr =
         rsrc(st.out + tile_start * st.o_st, (p.T - tile_start - 1) * st.o_st * 2 + int64_t(st.C) * 2);
 
     // Previous width-1 rows of x for the tile's first tokens; rows before
     // the first token's request are never an intra tap of this tile.
     const int64_t qs0 = readlane64(m_qs, 0);
-    u32x2 win[H];
 #pragma unroll
-    for (int k = 0; k < H; ++k) {
-        const int64_t row = tile_start - H + k;
-        win[k] = (row >= 0 && row >= qs0) ? ld8<kNt>(xr, xoff, (row - xbase) * st.x_st * 2)
-                                          : u32x2{0u, 0u};
-    }
+    for (int k = 0; k < H; ++k)
+        if (tile_start - H + k < qs0) win[k] = u32x2{0u, 0u};
 
     for (int u0 = 0; u0 < n_tok; u0 += kPagedUnroll) {
         u32x2 xv[kPagedUnroll];
