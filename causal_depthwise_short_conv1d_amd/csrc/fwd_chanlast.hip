@@ -85,8 +85,9 @@ __device__ __forceinline__ Rows make_rows(const uint16_t *t, int64_t base, int64
     Rows r;
     r.base = base;
     r.pitch = stride * 2;
-    // last row's channels end the extent (the row stride may be 0 when T == 1)
-    const int64_t bytes = (rows_total - base - 1) * r.pitch + int64_t(dim) * 2;
+    // last row's channels end the extent (the row stride may be 0 when T == 1);
+    // a base past the last row gives an empty descriptor
+    const int64_t bytes = base < rows_total ? (rows_total - base - 1) * r.pitch + int64_t(dim) * 2 : 0;
     r.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(t + base * stride), short(0),
                                                int(bytes < 0x7fffffff ? bytes : 0x7fffffff),
                                                0x00020000);
@@ -233,23 +234,10 @@ __device__ __forceinline__ void run_segment(const FwdClParams &p, const SeqInfo 
     }
 }
 
-template <int W, bool SILU, bool FULL>
-__global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_chanlast_kernel(FwdClParams p) {
-    const int lane = threadIdx.x & (kWaveSize - 1);
-    // wave index within the block: uniform, and marked so for the compiler
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
-    const uint32_t wt = blockIdx.x * kClWavesPerBlock + wave;
-    const int32_t slab = int32_t(wt % uint32_t(p.n_slabs));
-    const int32_t tt = int32_t(wt / uint32_t(p.n_slabs));
-    if (tt >= p.n_tiles) return;
-
-    int32_t c0 = slab * kClSlab + lane * kCpl;
-    int nv = p.dim - c0;
-    nv = nv < 0 ? 0 : (nv > kCpl ? kCpl : nv);
-    if (nv == 0) c0 = 0;                   // idle lane: in-range reads, no writes
-
-    // taps of the lane's channels, loaded without branches (channels past
-    // dim, and a missing bias, read 0)
+// Taps of a lane's channels (slab `slab`, lane channels from c0), loaded
+// without branches: channels past dim, and a missing bias, read 0.
+template <int W, bool FULL>
+__device__ __forceinline__ LaneTaps<W> lane_taps(const FwdClParams &p, int32_t slab, int lane) {
     const int32_t c_lo = slab * kClSlab;
     const int32_t n_ch = p.dim - c_lo < kClSlab ? p.dim - c_lo : kClSlab;
     const Rsrc wr = make_rsrc(p.w + int64_t(c_lo) * p.w_sd, int64_t(n_ch) * p.w_sd * 2);
@@ -275,10 +263,15 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_chanlast_ker
             tp.b[ch] = bf_one(buf_ld16(br, lc < n_ch ? uint32_t(lc) * 2 : kOob));
         }
     }
+    return tp;
+}
 
-    const int64_t T = p.sb.total_T;
-    const int64_t tile_start = int64_t(tt) * p.bt;
-    const int64_t tile_end = (tile_start + p.bt) < T ? (tile_start + p.bt) : T;
+// Tokens [tile_start, tile_end) of one slab, sequence by sequence: each
+// sequence's stretch inside the tile is a segment; a sequence's first
+// width-1 tokens belong to the tile that holds its first token.
+template <int W, bool SILU, bool FULL>
+__device__ __forceinline__ void run_tile(const FwdClParams &p, int64_t tile_start, int64_t tile_end,
+                                         int32_t c0, int nv, const LaneTaps<W> &tp) {
     int32_t s = seq_search(p.sb.qsl, p.sb.batch, tile_start);
     int64_t t = tile_start;
     while (t < tile_end) {
@@ -312,12 +305,153 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_chanlast_ker
     }
 }
 
+template <int W, bool SILU, bool FULL>
+__global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_chanlast_kernel(FwdClParams p) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    // wave index within the block: uniform, and marked so for the compiler
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+    const uint32_t wt = blockIdx.x * kClWavesPerBlock + wave;
+    const int32_t slab = int32_t(wt % uint32_t(p.n_slabs));
+    const int32_t tt = int32_t(wt / uint32_t(p.n_slabs));
+    if (tt >= p.n_tiles) return;
+
+    int32_t c0 = slab * kClSlab + lane * kCpl;
+    int nv = p.dim - c0;
+    nv = nv < 0 ? 0 : (nv > kCpl ? kCpl : nv);
+    if (nv == 0) c0 = 0;                   // idle lane: in-range reads, no writes
+    const LaneTaps<W> tp = lane_taps<W, FULL>(p, slab, lane);
+
+    const int64_t T = p.sb.total_T;
+    const int64_t tile_start = int64_t(tt) * p.bt;
+    const int64_t tile_end = (tile_start + p.bt) < T ? (tile_start + p.bt) : T;
+    run_tile<W, SILU, FULL>(p, tile_start, tile_end, c0, nv, tp);
+}
+
+// One sequence in (T, dim) storage, whole lanes (dim % 4 == 0), T >= 64.
+// A workgroup owns four consecutive 8-row tiles of one 256-channel slab.
+// Each wave issues its 8 rows at once; wave 0 also issues the width-1 rows
+// before the group.  Every other wave takes its history from the previous
+// wave's last width-1 rows, passed through LDS, so a halo costs no second
+// HBM read.  (With 8-row tiles, reading every tile's halo from memory costs
+// 7% of a copy of the same bytes.)  Group 0's wave 0 holds the sequence's
+// head: it reads the cached history and writes the new state (the last
+// width-1 rows), and is the only reader and writer of that line.  When the
+// sequence does not cover exactly [0, T) (query_start_loc is only known on
+// the device), every wave runs the general tile routine on its 8-row tile,
+// with the same tiles as fwd_chanlast_kernel at bt = 8.
+constexpr int kOneRows = 8;                      // rows per wave
+constexpr int kOneGroup = kClWavesPerBlock * kOneRows;   // rows per workgroup
+
+template <int W, bool SILU>
+__global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_cl_one_kernel(FwdClParams p,
+                                                                                  int32_t n_groups) {
+    constexpr int H = W - 1;
+    __shared__ u32x2 edge[kClWavesPerBlock][H][kWaveSize];   // each wave's last H rows
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+    const int32_t slab = int32_t(blockIdx.x % uint32_t(p.n_slabs));
+    const int32_t grp = int32_t(blockIdx.x / uint32_t(p.n_slabs));
+    if (grp >= n_groups) return;                     // the whole workgroup
+
+    int32_t c0 = slab * kClSlab + lane * kCpl;
+    const int nv = c0 < p.dim ? kCpl : 0;            // whole lanes
+    if (nv == 0) c0 = 0;                             // idle lane: in-range reads, no writes
+    const uint32_t voff = uint32_t(c0) * 2;
+    const int64_t T = p.sb.total_T;
+    const int64_t g0 = int64_t(grp) * kOneGroup;
+    const int64_t t0 = g0 + int64_t(wave) * kOneRows;
+    const LaneTaps<W> tp = lane_taps<W, true>(p, slab, lane);
+    const SeqInfo si = seq_info(p.sb, p.sb.qsl, 0);
+    if (!(si.start == 0 && si.end == T)) {           // uniform across the launch
+        const int64_t te = t0 + kOneRows < T ? t0 + kOneRows : T;
+        if (t0 < T) run_tile<W, SILU, true>(p, t0, te, c0, nv, tp);
+        return;
+    }
+    if (si.skip) return;                             // padded sequence: nothing to write
+
+    // the group's rows and the H before it, through one descriptor based at
+    // the first of them (rows past T read 0)
+    const int64_t base = g0 >= H ? g0 - H : 0;
+    const Rows xr = make_rows(p.x, base, p.x_st, T, p.dim);
+    u32x2 xv[kOneRows];
+#pragma unroll
+    for (int u = 0; u < kOneRows; ++u) xv[u] = ld_rows(xr, t0 + u, voff);
+    u32x2 win[H];
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+        const int64_t row = g0 - H + k;
+        const bool mine = wave == 0 && row >= 0;
+        win[k] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                     xr.rsrc, mine ? voff : kOob, mine ? int((row - base) * xr.pitch) : 0, kNt));
+    }
+#pragma unroll
+    for (int k = 0; k < H; ++k) edge[wave][k][lane] = xv[kOneRows - H + k];
+    __syncthreads();
+    if (wave > 0) {
+#pragma unroll
+        for (int k = 0; k < H; ++k) win[k] = edge[wave - 1][k][lane];
+    } else if (grp == 0) {
+        // the sequence head: cached history (or zeros), then the new state
+        // = rows T-H .. T-1 (T >= 64 > H), written after the history is read
+        const bool has_cs = p.sb.cs != nullptr;
+        const Rsrc cs = make_rsrc(has_cs ? p.sb.cs + si.line * p.sb.cs_sl : p.x,
+                                  has_cs ? 0x7fffffff : 0);
+        const Rsrc hist = make_rsrc(has_cs ? p.sb.cs + si.line * p.sb.cs_sl : p.x,
+                                    has_cs && si.init ? 0x7fffffff : 0);
+        uint32_t coff[kCpl];
+#pragma unroll
+        for (int ch = 0; ch < kCpl; ++ch)
+            coff[ch] = nv > 0 ? uint32_t(int64_t(c0 + ch) * p.sb.cs_sd * 2) : kOob;
+        const Rows tr = make_rows(p.x, T - H, p.x_st, T, p.dim);
+        u32x2 tail[H];
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            uint32_t d[2] = {0u, 0u};
+#pragma unroll
+            for (int ch = 0; ch < kCpl; ++ch)
+                d[ch >> 1] |= uint32_t(__builtin_amdgcn_raw_buffer_load_b16(
+                                  hist, coff[ch], int(k * p.sb.cs_st * 2), 0))
+                              << (16 * (ch & 1));
+            win[k] = u32x2{d[0], d[1]};
+            tail[k] = ld_rows(tr, T - H + k, voff);
+        }
+        if (has_cs) {
+#pragma unroll
+            for (int k = 0; k < H; ++k)
+#pragma unroll
+                for (int ch = 0; ch < kCpl; ++ch)
+                    __builtin_amdgcn_raw_buffer_store_b16(row_elem(tail[k], ch), cs, coff[ch],
+                                                          int(k * p.sb.cs_st * 2), 0);
+        }
+    }
+
+    const Rows orr = make_rows(p.out, t0, p.o_st, T, p.dim);
+#pragma unroll
+    for (int u = 0; u < kOneRows; ++u) {
+        const u32x2 o = conv_row<W, SILU>(tp, win, xv[u]);
+        if (nv > 0) st_rows(orr, t0 + u, voff, o);     // rows past T: dropped
+#pragma unroll
+        for (int k = 0; k + 1 < H; ++k) win[k] = win[k + 1];
+        win[H - 1] = xv[u];
+    }
+}
+
 template <int W>
 hipError_t launch_w(const FwdClParams &p, bool silu, hipStream_t s) {
     const uint64_t waves = uint64_t(p.n_tiles) * uint64_t(p.n_slabs);
     const uint32_t blocks = uint32_t((waves + kClWavesPerBlock - 1) / kClWavesPerBlock);
     const dim3 grid(blocks), block(kClWavesPerBlock * kWaveSize);
     const bool full = p.dim % kCpl == 0;
+    const int64_t pitch = (p.x_st > p.o_st ? p.x_st : p.o_st) * 2;
+    if (p.sb.batch <= 1 && full && p.bt == kOneRows && p.sb.total_T >= 64 &&
+        int64_t(kOneGroup + W) * pitch + int64_t(p.dim) * 2 < kMaxDescriptorSpan) {
+        // one sequence: four 8-row tiles per workgroup, halos through LDS
+        const int32_t n_groups = int32_t((p.sb.total_T + kOneGroup - 1) / kOneGroup);
+        const dim3 g(uint32_t(n_groups) * uint32_t(p.n_slabs));
+        if (silu) fwd_cl_one_kernel<W, true><<<g, block, 0, s>>>(p, n_groups);
+        else fwd_cl_one_kernel<W, false><<<g, block, 0, s>>>(p, n_groups);
+        return hipGetLastError();
+    }
     if (silu && full) fwd_chanlast_kernel<W, true, true><<<grid, block, 0, s>>>(p);
     else if (silu) fwd_chanlast_kernel<W, true, false><<<grid, block, 0, s>>>(p);
     else if (full) fwd_chanlast_kernel<W, false, true><<<grid, block, 0, s>>>(p);

@@ -182,6 +182,47 @@ def test_long_prefill_channel_contiguous():
     assert_bits(g_cs[0], d["x"][:, T - 3:], "T4195 (T,dim) state")
 
 
+# One sequence in (T, dim) rows: four 8-row tiles per workgroup with the
+# halos passed on chip; cases for partial last groups (waves past T), idle
+# lanes, every width, with and without history or state, a padded sequence,
+# row pitches wider than dim (one of them with dim % 4 != 0, which takes the
+# general kernel), and sequences that do not cover [0, T) (the general tile
+# routine inside the same launch).
+ONE_CL_CASES = [
+    (64, 256, 4, "plain"), (65, 264, 2, "plain"), (95, 8, 3, "plain"), (97, 520, 5, "plain"),
+    (100, 1032, 4, "no_init"), (1000, 264, 4, "no_state"), (333, 256, 5, "pad"),
+    (257, 256, 4, "pitch"), (301, 13, 3, "pitch"), (4096, 200, 3, "plain"),
+    (130, 8, 2, "start5"), (130, 16, 4, "end_short"), (63, 256, 4, "plain"),
+]
+
+
+@pytest.mark.parametrize("T,dim,width,variant", ONE_CL_CASES)
+def test_one_sequence_channel_contiguous(T, dim, width, variant):
+    d = W.single_sequence(dim=dim, T=T, width=width, seed=T * 7 + dim + width,
+                          layout="tok_dim" if variant != "pitch" else "dim_tok", values="exact")
+    if variant == "no_init":
+        d["has_initial_state"] = torch.zeros(1, dtype=torch.bool)
+    elif variant == "no_state":
+        d["conv_states"] = None
+        d["has_initial_state"] = None
+    elif variant == "pad":
+        d["cache_indices"] = torch.tensor([-1], dtype=torch.int32)
+    elif variant == "start5":
+        d["query_start_loc"] = torch.tensor([5, T], dtype=torch.int32)
+    elif variant == "end_short":
+        d["query_start_loc"] = torch.tensor([0, T - 3], dtype=torch.int32)
+    gd = to_dev(d)
+    if variant == "pitch":                     # rows wider than dim, built on the device
+        pitch = (dim + 7) // 8 * 8 + 8
+        wide = torch.zeros(T, pitch, dtype=BF, device=DEV)
+        wide[:, :dim] = gd["x"].t()
+        gd["x"] = wide[:, :dim].t()
+    assert gd["x"].stride(0) == 1
+    say(f"[fwd] one sequence (T,dim) T{T} dim{dim} W{width} {variant}")
+    check_full(gd, activation=None, exact=True, label=f"one seq T{T} dim{dim} W{width} {variant}")
+    check_full(gd, activation="silu", label=f"one seq T{T} dim{dim} W{width} {variant} silu")
+
+
 def varlen_state_property(d, g_cs, width):
     """New state of every channel of every processed line: the last width-1
     entries of (history ++ sequence); untouched lines unchanged."""
