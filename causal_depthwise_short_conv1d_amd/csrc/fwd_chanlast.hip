@@ -23,7 +23,7 @@ namespace sconv {
 
 namespace {
 
-constexpr int kUnroll = 8;                     // token rows in flight per lane
+constexpr int kUnroll = 8;                     // token rows per batch (two batches in flight)
 
 // A lane's taps for its 4 channels, packed for dot2: pair q of channel ch is
 // (w[ch][2q], w[ch][2q+1]); an odd last tap and the bias are fp32.
@@ -209,13 +209,25 @@ __device__ __forceinline__ void run_segment(const FwdClParams &p, const SeqInfo 
                           : ld_row<FULL>(p.x + (b - H + k) * p.x_st + c0, nv);
     }
 
+    // Software-pipelined rows: the next kUnroll rows are issued before the
+    // current ones are computed (rows past the segment read 0), which keeps a
+    // wave's loads in flight through its arithmetic.
+    u32x2 xn[kUnroll];
+    if constexpr (FULL) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) xn[u] = ld_rows(xr, b + u, voff);
+    }
     for (int64_t t = b; t < e; t += kUnroll) {
         const int n = (e - t) < kUnroll ? int(e - t) : kUnroll;
         u32x2 xv[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            if constexpr (FULL) xv[u] = ld_rows(xr, t + u, voff);     // past the segment: 0
-            else if (u < n) xv[u] = ld_row<FULL>(p.x + (t + u) * p.x_st + c0, nv);
+            if constexpr (FULL) {
+                xv[u] = xn[u];
+                xn[u] = ld_rows(xr, t + kUnroll + u, voff);          // next batch; past the segment: 0
+            } else if (u < n) {
+                xv[u] = ld_row<FULL>(p.x + (t + u) * p.x_st + c0, nv);
+            }
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
