@@ -29,6 +29,9 @@
 // (possibly spilling into the next chunk) and writes the new state, so no
 // other lane can read a state that has already been overwritten.
 #include "sconv_device.h"
+#ifndef SCONV_LONG_ROUNDS
+#define SCONV_LONG_ROUNDS 4
+#endif
 
 namespace sconv {
 
@@ -38,7 +41,10 @@ constexpr int kChunksPerWave = kWaveSize * kTokRounds;
 constexpr uint32_t kWaveElems = kChunksPerWave * kVec;
 constexpr int kShortMinT = 16;                    // shortest row of the short-row kernel
 constexpr int kShortWaves = 256 * 8;             // waves that keep ~8 per CU busy
-constexpr int kLongWaves = 4;                     // waves per long-row block (fewer, larger
+#ifndef SCONV_LONG_WAVES
+#define SCONV_LONG_WAVES 4
+#endif
+constexpr int kLongWaves = SCONV_LONG_WAVES;                     // waves per long-row block (fewer, larger
                                                   // workgroups dispatch faster at 10^5 waves)
 
 // Weights of one channel for the dot2 path: taps as packed bf16 pairs
@@ -138,11 +144,11 @@ __device__ __forceinline__ uint32_t hist_bits(uint64_t hv, int l) {
 // chunk twice: once on the window as loaded with the previous row's taps
 // (right for elements before hp), once on a copy whose positions in
 // [hp-H, hp) hold the cached history h, with the head row's taps (right for
-// elements from hp on); the two are merged element by element.
+// elements from hp on); the two are merged element by element.  head_merge
+// takes the first of the two, `a`, already computed.
 template <int W, bool SILU>
-__device__ __forceinline__ u32x4 head_chunk(const Window &win, uint32_t i0, uint32_t hp,
-                                            const PairTaps<W> &t_prev, const PairTaps<W> &t_head,
-                                            const uint32_t (&h)[W - 1]) {
+__device__ __forceinline__ u32x4 head_merge(const u32x4 &a, const Window &win, uint32_t i0, uint32_t hp,
+                                            const PairTaps<W> &t_head, const uint32_t (&h)[W - 1]) {
     constexpr int H = W - 1;
     const uint64_t hv = pack_hist<H>(h);
     Window wh = win;
@@ -154,7 +160,6 @@ __device__ __forceinline__ u32x4 head_chunk(const Window &win, uint32_t i0, uint
         if (l0 + 1 >= -H && l0 + 1 < 0) hi = hist_bits<H>(hv, l0 + 1);
         wh.d[d] = lo | (hi << 16);
     }
-    const u32x4 a = fast_chunk<W, SILU>(win, t_prev);
     const u32x4 b = fast_chunk<W, SILU>(wh, t_head);
     const uint32_t k = hp > i0 ? hp - i0 : 0;              // elements [0, k) end the previous row
     const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
@@ -166,6 +171,12 @@ __device__ __forceinline__ u32x4 head_chunk(const Window &win, uint32_t i0, uint
         r[d] = lo | hi;
     }
     return u32x4{r[0], r[1], r[2], r[3]};
+}
+template <int W, bool SILU>
+__device__ __forceinline__ u32x4 head_chunk(const Window &win, uint32_t i0, uint32_t hp,
+                                            const PairTaps<W> &t_prev, const PairTaps<W> &t_head,
+                                            const uint32_t (&h)[W - 1]) {
+    return head_merge<W, SILU>(fast_chunk<W, SILU>(win, t_prev), win, i0, hp, t_head, h);
 }
 
 // Scalar weights for the element-by-element path.
@@ -266,51 +277,72 @@ __device__ void slow_chunk(const FwdTokParams &p, const int32_t *qsl, uint32_t i
     }
 }
 
+// Channel c's taps and bias through the scalar cache (with no bias the
+// stand-in read is masked to 0).
+template <int W>
+__device__ __forceinline__ PairTaps<W> sload_pair_taps(const FwdTokParams &p, uint32_t c) {
+    const U16Run<W> w = sld_run<W>(p.w + int64_t(c) * p.w_sd);
+    PairTaps<W> r;
+#pragma unroll
+    for (int q = 0; q < W / 2; ++q) r.wp[q] = w.d[q];
+    r.wl = (W & 1) ? bf_one(uint16_t(w.elem(W - 1))) : 0.0f;
+    r.b = bf_one(uint16_t(sld_u16(p.bias_rd + c) & p.bias_mask));
+    return r;
+}
+
 // One sequence whose rows are at least one wave long (T >= 2048): every
 // wave spans at most two rows and contains at most one row head.  The head's
 // history (state), the row's last width-1 inputs (the new state) and both
-// rows' taps are wave-uniform values loaded with the wave's x; the head
-// chunks are computed in registers and one lane writes the new state after
-// the wave's reads.  Only three rare cases fall back to the element path:
-// the ragged last chunk, and a head whose first width-1 tokens cross into the
-// next wave (its owner computes them element by element and the next wave's
-// first chunk skips them).
-template <int W, bool SILU>
+// rows' taps are wave-uniform values read with scalar loads issued right
+// after the wave's x loads, so they complete under them; the head chunks are
+// computed in registers and one lane writes the new state after the wave's
+// reads.  Only three rare cases fall back to the element path: the ragged
+// last chunk, and a head whose first width-1 tokens cross into the next wave
+// (its owner computes them element by element and the next wave's first
+// chunk skips them).
+template <int W, bool SILU, int ROUNDS>
 __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(FwdTokParams p) {
+    constexpr uint32_t kCPW = ROUNDS * kWaveSize;           // chunks per wave
+    constexpr uint32_t kWE = kCPW * kVec;                   // elements per wave
     constexpr int H = W - 1;
     constexpr uint32_t kNone = 0xffffffffu;
     const int lane = threadIdx.x & (kWaveSize - 1);
-    const int wave = threadIdx.x / kWaveSize;
-    const uint32_t wbase = (blockIdx.x * kLongWaves + wave) * uint32_t(kChunksPerWave);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+    const uint32_t wbase = (blockIdx.x * kLongWaves + wave) * kCPW;
     if (wbase >= p.n_chunks) return;
-    const SeqInfo s0 = seq_info(p.sb, p.sb.qsl, 0);
-    if (s0.skip) return;                                    // padded sequence: nothing to do
 
+    // The wave's x goes out first.  Everything else it needs is wave-uniform
+    // and read with scalar loads that complete under the x loads, so a wave
+    // waits for one memory round trip before it computes.  Full chunks go
+    // through a descriptor that ends at the last one, so the loads need no
+    // branch (the ragged last chunk reads 0 here).
     const uint32_t T = p.T;
     const uint32_t n_full = p.n_elems / kVec;
-    u32x4 v[kTokRounds];
-    if (wbase + kChunksPerWave <= n_full) {
+    constexpr int kNt = 2;                                  // non-temporal cache policy bit
+    const uint32_t n_mine = wbase < n_full ? (n_full - wbase < kCPW ? n_full - wbase : kCPW) : 0u;
+    const Rsrc xr = make_rsrc(p.x + size_t(wbase) * kVec, int64_t(n_mine) * 16);
+    const Rsrc outr = make_rsrc(p.out + size_t(wbase) * kVec, int64_t(n_mine) * 16);
+    u32x4 v[ROUNDS];
 #pragma unroll
-        for (int r = 0; r < kTokRounds; ++r)
-            v[r] = ld16_stream(p.x + size_t(wbase + r * kWaveSize + lane) * kVec);
-    } else {
-#pragma unroll
-        for (int r = 0; r < kTokRounds; ++r) {
-            const uint32_t ch = wbase + r * kWaveSize + lane;
-            v[r] = ch < n_full ? ld16_stream(p.x + size_t(ch) * kVec) : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-    uint32_t prev_z = 0, prev_w = 0;
-    if (lane == 0 && wbase > 0) {
-        const u32x2 t2 = *reinterpret_cast<const u32x2 *>(p.x + size_t(wbase) * kVec - 4);
-        prev_z = t2.x;
-        prev_w = t2.y;
-    }
+    for (int r = 0; r < ROUNDS; ++r) v[r] = buf_ld128<kNt>(xr, uint32_t(r * kWaveSize + lane) * 16u);
+    // the 4 elements before the wave: lane 0's halo in round 0
+    const uint16_t *pp = p.x + (wbase > 0 ? size_t(wbase) * kVec - 4 : 0);
+    uint32_t prev_z = sld_u32(pp), prev_w = sld_u32(pp + 2);
+    if (wbase == 0) prev_z = prev_w = 0;
+
+    // Sequence 0: its token range, cache line and whether it has a history.
+    const int64_t q0 = int32_t(sld_u32(p.sb.qsl)), q1 = int32_t(sld_u32(p.sb.qsl + 1));
+    const int32_t ci = int32_t(sld_u32(p.ci_rd));
+    const uint32_t hiv = sld_u8(p.hi_rd);
+    const int64_t line = p.sb.cache_idx ? int64_t(ci) : 0;
+    const bool skip = (p.sb.cache_idx && line == p.sb.pad_slot_id) ||
+                      (p.sb.cs && (line < 0 || line >= p.sb.num_lines));
+    const bool init = p.sb.cs && p.sb.has_init && hiv != 0;
+    const bool simple = q0 <= 0 && q1 >= int64_t(T);       // the sequence covers every token
 
     // Wave-uniform rows, head and history.
-    const bool simple = s0.start == 0 && s0.end == int64_t(T);
     const uint32_t e_first = wbase * kVec;
-    const uint32_t e_last = (e_first + kWaveElems <= p.n_elems ? e_first + kWaveElems : p.n_elems) - 1;
+    const uint32_t e_last = (e_first + kWE <= p.n_elems ? e_first + kWE : p.n_elems) - 1;
     const uint32_t cA = p.divT.div(e_first);
     const uint32_t row_a = cA * T, row_end = row_a + T;
     uint32_t hp = kNone, R = 0;
@@ -318,15 +350,39 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
     else if (row_end <= e_last) { hp = row_end; R = cA + 1; }
     const bool cross = hp != kNone && uint64_t(hp) + (H - 1) > e_last;
     const bool lead_owned = H >= 2 && e_first > row_a && e_first - row_a <= uint32_t(H - 1);
-    const PairTaps<W> tA = uniform(load_pair_taps<W>(p, cA));
-    const PairTaps<W> tB = (cA + 1 < uint32_t(p.dim)) ? uniform(load_pair_taps<W>(p, cA + 1)) : tA;
-    const bool own_head = simple && hp != kNone && !cross;
+    const PairTaps<W> tA = sload_pair_taps<W>(p, cA);
+    const PairTaps<W> tB = sload_pair_taps<W>(p, cA + 1 < uint32_t(p.dim) ? cA + 1 : cA);
+    const bool own_head = simple && hp != kNone && !cross && !skip;
+    const PairTaps<W> &t_head = (R == cA) ? tA : tB;
+    // Waves that hold a row head also read its history (the cached state,
+    // read by this wave only) and the row's last width-1 inputs (the new
+    // state).  The loads still go out before the wave waits for its x.
+    uint32_t hb[H];
+    U16Run<H> nh;
+#pragma unroll
+    for (int k = 0; k < H; ++k) hb[k] = 0;
+#pragma unroll
+    for (int i = 0; i < H / 2 + 1; ++i) nh.d[i] = 0;
+    if (own_head) {
+        asm volatile("");                                   // keeps this a branch
+        nh = sld_run<H>(p.x + size_t(R) * T + (T - H));
+        if (init) {
+#pragma unroll
+            for (int k = 0; k < H; ++k)
+                hb[k] = sld_u16(p.sb.cs + (line * p.sb.cs_sl + int64_t(R) * p.sb.cs_sd + k * p.sb.cs_st));
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < H; ++k) pin_sgpr(hb[k]);
+#pragma unroll
+    for (int i = 0; i < H / 2 + 1; ++i) pin_sgpr(nh.d[i]);
+    const bool live = !skip;                                // padded sequence: nothing to do
 
     // Halo of every round first (each permute waits only for its own load).
     const int src_lane = (lane + kWaveSize - 1) & (kWaveSize - 1);
-    uint32_t hz[kTokRounds], hw[kTokRounds];
+    uint32_t hz[ROUNDS], hw[ROUNDS];
 #pragma unroll
-    for (int r = 0; r < kTokRounds; ++r) {
+    for (int r = 0; r < ROUNDS; ++r) {
         const uint32_t rz = uint32_t(__shfl(int(v[r].z), src_lane));
         const uint32_t rw = uint32_t(__shfl(int(v[r].w), src_lane));
         hz[r] = lane == 0 ? prev_z : rz;
@@ -335,74 +391,46 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
         prev_w = rw;
     }
 
-    // Interior chunks: computed and stored round by round.  Head chunks and
-    // element-path chunks are only marked here, which keeps this loop (and
-    // the register budget that sets the occupancy) small.
-    uint32_t head = 0, slow = 0;
+    // Chunks computed and stored round by round; the (at most two) chunks of
+    // the row head take the history in place of the previous row's inputs.
+    // Element-path chunks are only marked here.
+    uint32_t slow = 0;
 #pragma unroll
-    for (int r = 0; r < kTokRounds; ++r) {
+    for (int r = 0; r < ROUNDS; ++r) {
         const uint32_t chunk = wbase + r * kWaveSize + lane;
-        if (chunk >= p.n_chunks) continue;
         const uint32_t i0 = chunk * kVec;
         const bool at_head = hp != kNone && i0 + kVec > hp && i0 <= hp + (H - 1);
-        if (!simple || chunk >= n_full || (lead_owned && r == 0 && lane == 0) ||
-            (at_head && cross)) {
-            slow |= 1u << r;
-        } else if (at_head) {
-            head |= 1u << r;
-        } else {
-            Window win;
-            win.d[0] = hz[r];
-            win.d[1] = hw[r];
-            win.d[2] = v[r].x;
-            win.d[3] = v[r].y;
-            win.d[4] = v[r].z;
-            win.d[5] = v[r].w;
-            st16_stream(p.out + size_t(i0), fast_chunk<W, SILU>(win, select(i0 >= row_end, tB, tA)));
+        const bool is_slow = !simple || chunk >= n_full || (lead_owned && r == 0 && lane == 0) ||
+                             (at_head && cross);
+        Window win;
+        win.d[0] = hz[r];
+        win.d[1] = hw[r];
+        win.d[2] = v[r].x;
+        win.d[3] = v[r].y;
+        win.d[4] = v[r].z;
+        win.d[5] = v[r].w;
+        // Every lane computes its chunk and stores it through a descriptor
+        // (a lane with nothing to store writes past its end): no branch
+        // stands between the wave's loads and the taps' first use.
+        u32x4 o = fast_chunk<W, SILU>(win, select(i0 >= row_end, tB, tA));
+        const bool mine = live && chunk < p.n_chunks;
+        if (mine && is_slow) slow |= 1u << r;
+        if (own_head) {                                     // wave-uniform: a row head is here
+            asm volatile("");                               // keeps this a branch, not a select
+            if (at_head) o = head_merge<W, SILU>(o, win, i0, hp, t_head, hb);
         }
+        __builtin_amdgcn_raw_buffer_store_b128(o, outr, mine && !is_slow ? uint32_t(r * kWaveSize + lane) * 16u : kOob,
+                                               0, kNt);
     }
-
-    // The row head of this wave (at most two chunks, usually one lane): its
-    // history is the cached state, read once, uniformly, by this wave only;
-    // afterwards one lane replaces it with the row's last width-1 inputs.
-    if (own_head) {
-        uint32_t hb[H];
-        uint16_t nh[H];
+    // One lane replaces the history this wave read with the row's last
+    // width-1 inputs.
+    if (own_head && p.sb.cs && lane == 0) {
 #pragma unroll
-        for (int k = 0; k < H; ++k) {
-            const uint16_t b = s0.init
-                ? p.sb.cs[s0.line * p.sb.cs_sl + int64_t(R) * p.sb.cs_sd + k * p.sb.cs_st]
-                : uint16_t(0);
-            hb[k] = __builtin_amdgcn_readfirstlane(uint32_t(b));
-            nh[k] = uint16_t(__builtin_amdgcn_readfirstlane(p.x[size_t(R) * T + (T - H) + k]));
-        }
-        const PairTaps<W> &t_head = (R == cA) ? tA : tB;
-#pragma unroll 1
-        for (int r = 0; r < kTokRounds; ++r) {
-            if (!(head & (1u << r))) continue;
-            const uint32_t i0 = (wbase + r * kWaveSize + lane) * kVec;
-            Window win;
-            // elements 4..7 of the previous chunk (none before the tensor start,
-            // where every tap before the head comes from the history)
-            const u32x2 t2 = i0 >= kVec ? *reinterpret_cast<const u32x2 *>(p.x + size_t(i0) - 4)
-                                        : u32x2{0u, 0u};
-            const u32x4 cv = ld16(p.x + size_t(i0));
-            win.d[0] = t2.x;
-            win.d[1] = t2.y;
-            win.d[2] = cv.x;
-            win.d[3] = cv.y;
-            win.d[4] = cv.z;
-            win.d[5] = cv.w;
-            st16_stream(p.out + size_t(i0), head_chunk<W, SILU>(win, i0, hp, tA, t_head, hb));
-        }
-        if (p.sb.cs && lane == 0) {
-#pragma unroll
-            for (int k = 0; k < H; ++k)
-                p.sb.cs[s0.line * p.sb.cs_sl + int64_t(R) * p.sb.cs_sd + k * p.sb.cs_st] = nh[k];
-        }
+        for (int k = 0; k < H; ++k)
+            p.sb.cs[line * p.sb.cs_sl + int64_t(R) * p.sb.cs_sd + k * p.sb.cs_st] = uint16_t(nh.elem(k));
     }
 #pragma unroll 1
-    for (int r = 0; r < kTokRounds; ++r)
+    for (int r = 0; r < ROUNDS; ++r)
         if (slow & (1u << r)) slow_chunk<W, SILU>(p, p.sb.qsl, (wbase + r * kWaveSize + lane) * kVec);
 }
 
@@ -1024,8 +1052,9 @@ hipError_t launch_ws(const FwdTokParams &p, hipStream_t s) {
     } else if (p.sb.batch > 1) {
         fwd_tokmajor_kernel<W, SILU, true><<<grid, block, 0, s>>>(p);
     } else if (p.T >= kWaveElems) {
-        const uint32_t lb = (p.n_chunks + kLongWaves * kChunksPerWave - 1) / (kLongWaves * kChunksPerWave);
-        fwd_tok_long_kernel<W, SILU><<<dim3(lb), dim3(kLongWaves * kWaveSize), 0, s>>>(p);
+        constexpr uint32_t kLB = kLongWaves * SCONV_LONG_ROUNDS * kWaveSize;
+        const uint32_t lb = (p.n_chunks + kLB - 1) / kLB;
+        fwd_tok_long_kernel<W, SILU, SCONV_LONG_ROUNDS><<<dim3(lb), dim3(kLongWaves * kWaveSize), 0, s>>>(p);
     } else if (p.T >= uint32_t(kShortMinT)) {
         // Rounds per wave, measured on gfx950: one round (the most waves in
         // flight) up to 512K chunks, two from there, four from 2M, where a

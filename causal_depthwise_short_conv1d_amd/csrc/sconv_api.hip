@@ -188,6 +188,10 @@ int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
         p.n_elems = uint32_t(n);
         p.n_chunks = uint32_t((n + kVec - 1) / kVec);
         p.dim = dim;
+        p.bias_rd = bias ? p.bias : p.w;
+        p.bias_mask = bias ? 0xffffu : 0u;
+        p.ci_rd = sb.cache_idx ? sb.cache_idx : sb.qsl;
+        p.hi_rd = sb.has_init ? sb.has_init : reinterpret_cast<const uint8_t *>(sb.qsl);
         return launch_status(launch_fwd_tokmajor(p, width, silu, stream));
     }
     return SCONV_ERR_STRIDE;

@@ -162,6 +162,60 @@ __device__ __forceinline__ void load_taps4(Rsrc wr, uint32_t off, Rsrc br, uint3
     b[0] = bf_lo(bv.x); b[1] = bf_hi(bv.x); b[2] = bf_lo(bv.y); b[3] = bf_hi(bv.y);
 }
 
+// -------------------------------------------------- wave-uniform loads --
+// Reads of read-only, wave-uniform data through the scalar cache (constant
+// address space): they take no vector-memory issue slots and land directly
+// in scalar registers.  Only whole dwords that hold a wanted byte are read,
+// so no access leaves the dword-aligned span of the data.
+typedef const __attribute__((address_space(4))) uint32_t KU32;
+
+__device__ __forceinline__ KU32 *kptr(uintptr_t a) { return reinterpret_cast<KU32 *>(a); }
+
+__device__ __forceinline__ uint32_t sld_u32(const void *p) {
+    return *kptr(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ uint32_t sld_u16(const uint16_t *p) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return (*kptr(a & ~uintptr_t(3)) >> ((a & 2) * 8)) & 0xffffu;
+}
+__device__ __forceinline__ uint32_t sld_u8(const uint8_t *p) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return (*kptr(a & ~uintptr_t(3)) >> ((a & 3) * 8)) & 0xffu;
+}
+
+// K consecutive 16-bit values from p (wave-uniform, 2-byte aligned) as
+// dwords: value k is bits [16(k&1), 16(k&1)+16) of d[k/2], so d[q] is the
+// pair (2q, 2q+1) whatever the alignment of p.
+// Marks a wave-uniform value as used at this point: its load completes here
+// instead of being sunk into the (branch) block that first reads it.
+__device__ __forceinline__ void pin_sgpr(uint32_t v) { asm volatile("" ::"s"(v)); }
+
+template <int K>
+struct U16Run {
+    uint32_t d[K / 2 + 1];
+    __device__ __forceinline__ uint32_t elem(int k) const { return (d[k >> 1] >> (16 * (k & 1))) & 0xffffu; }
+};
+template <int K>
+__device__ __forceinline__ U16Run<K> sld_run(const uint16_t *p) {
+    constexpr int N = K / 2 + 1;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uintptr_t q = a & ~uintptr_t(3);
+    const uint32_t m = uint32_t(a >> 1) & 1u;             // 1 when p is not dword aligned
+    // The run spans dwords 0..K/2 except for an even K at an aligned p, which
+    // ends at dword K/2 - 1; that dword is then read twice instead.
+    uint32_t raw[N];
+#pragma unroll
+    for (int i = 0; i < N - 1; ++i) raw[i] = kptr(q)[i];
+    raw[N - 1] = (K & 1) ? kptr(q)[N - 1] : kptr(q + 4 * (N - 2 + m))[0];
+    U16Run<K> r;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint64_t hi = i + 1 < N ? uint64_t(raw[i + 1]) << 32 : 0;
+        r.d[i] = uint32_t((hi | raw[i]) >> (16 * m));
+    }
+    return r;
+}
+
 // -------------------------------------------------- varlen sequence lookup --
 // Largest j in [0, n) with qsl[j] <= t (the token -> sequence search of the
 // Inkling page's metadata kernel).  Works for any qsl contents: the result

@@ -61,6 +61,13 @@ struct FwdTokParams {          // token-contiguous (dim, T) storage
     uint32_t n_elems;          // dim * T
     uint32_t n_chunks;         // ceil(n_elems / 8)
     int32_t dim;
+    // Always-readable stand-ins, so wave-uniform reads need no branch: the
+    // bias (or the weights, masked to 0 when there is no bias), the cache
+    // indices and has_initial_state (or query_start_loc when absent).
+    const uint16_t *bias_rd;
+    uint32_t bias_mask;        // 0xffff with a bias, else 0
+    const int32_t *ci_rd;
+    const uint8_t *hi_rd;
 };
 
 struct FwdClParams {           // channel-contiguous (T, dim) storage

@@ -152,6 +152,42 @@ def test_very_short_rows(T, width):
     check_full(g, activation=None, exact=True, label=f"very short rows T{T} W{width} no init")
 
 
+# One sequence in token-contiguous rows of at least 2048 tokens (the long-row
+# kernel): every way of describing the sequence -- a cache line other than 0,
+# a pad, no history, no state, no bias, no has_initial_state array, and a
+# sequence that ends before T -- at every width.
+ONE_TOK_CASES = [
+    (2051, 40, 4, "line5"), (2500, 24, 2, "pad"), (3000, 33, 3, "no_init"),
+    (2049, 16, 5, "no_state"), (4099, 20, 4, "no_bias"), (2100, 36, 5, "no_has_init"),
+    (2048, 8, 3, "end_short"), (4096, 12, 2, "line5"),
+]
+
+
+@pytest.mark.parametrize("T,dim,width,variant", ONE_TOK_CASES)
+def test_one_sequence_long_rows_variants(T, dim, width, variant):
+    d = W.single_sequence(dim=dim, T=T, width=width, seed=T * 3 + dim + width, values="exact")
+    if variant == "line5":
+        d["conv_states"] = W._draw((8, dim, width - 1), W._gen(T, "cpu"), "cpu", "exact")
+        d["cache_indices"] = torch.tensor([5], dtype=torch.int32)
+    elif variant == "pad":
+        d["cache_indices"] = torch.tensor([-1], dtype=torch.int32)
+    elif variant == "no_init":
+        d["has_initial_state"] = torch.zeros(1, dtype=torch.bool)
+    elif variant == "no_state":
+        d["conv_states"] = None
+        d["has_initial_state"] = None
+    elif variant == "no_bias":
+        d["bias"] = None
+    elif variant == "no_has_init":
+        d["has_initial_state"] = None
+    elif variant == "end_short":
+        d["query_start_loc"] = torch.tensor([0, T - 3], dtype=torch.int32)
+    say(f"[fwd] one sequence (dim,T) long rows T{T} dim{dim} W{width} {variant}")
+    g = to_dev(d)
+    check_full(g, activation=None, exact=True, label=f"long one seq T{T} dim{dim} W{width} {variant}")
+    check_full(g, activation="silu", label=f"long one seq T{T} dim{dim} W{width} {variant} silu")
+
+
 @pytest.mark.parametrize("T,start", [(100, 5), (10, 3), (3000, 2)])
 def test_single_sequence_not_starting_at_zero(T, start):
     """query_start_loc [start, T] (outside the documented contract, which
