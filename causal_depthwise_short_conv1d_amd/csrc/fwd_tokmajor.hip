@@ -709,36 +709,37 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     const uint32_t T = p.T;
 
     // A chunk wave issues its x loads before the tables are staged, so the
-    // staging's round trip and barrier overlap them.  Every load of a whole
-    // wave is unconditional (a load under a branch would wait for the ones
-    // before it); only the last wave checks its chunks.
+    // staging's round trip and barrier overlap them.  Full chunks go through
+    // a descriptor that ends at the last one (no branch); only the last wave
+    // reads a ragged last chunk element by element.  The wave-uniform rows'
+    // taps and the 4 elements before the wave are scalar loads issued next.
     const int lane = threadIdx.x & (kWaveSize - 1);
-    const int wave = threadIdx.x / kWaveSize;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
     const uint32_t wbase = (blockIdx.x * kVarWaves + wave) * uint32_t(kChunksPerWave);
     const uint32_t n_full = p.n_elems / kVec;
     const bool chunk_wave = blockIdx.x < chunk_blocks && wbase < p.n_chunks;
+    constexpr int kNt = 2;                                  // non-temporal cache policy bit
+    const uint32_t n_mine = chunk_wave && wbase < n_full
+                                ? (n_full - wbase < uint32_t(kChunksPerWave) ? n_full - wbase : uint32_t(kChunksPerWave))
+                                : 0u;
+    const Rsrc xr = make_rsrc(p.x + size_t(chunk_wave ? wbase : 0) * kVec, int64_t(n_mine) * 16);
     u32x4 v[kTokRounds];
-    uint32_t prev_z = 0, prev_w = 0;
-    if (chunk_wave) {
-        if (wbase + kChunksPerWave <= n_full) {
 #pragma unroll
-            for (int r = 0; r < kTokRounds; ++r)
-                v[r] = ld16_stream(p.x + size_t(wbase + r * kWaveSize + lane) * kVec);
-        } else {
+    for (int r = 0; r < kTokRounds; ++r) v[r] = buf_ld128<kNt>(xr, uint32_t(r * kWaveSize + lane) * 16u);
+    if (chunk_wave && n_mine < uint32_t(kChunksPerWave) && n_full < p.n_chunks) {
 #pragma unroll
-            for (int r = 0; r < kTokRounds; ++r) {
-                const uint32_t ch = wbase + r * kWaveSize + lane;
-                if (ch < n_full) v[r] = ld16_stream(p.x + size_t(ch) * kVec);
-                else if (ch < p.n_chunks) v[r] = ld8_partial(p.x + size_t(ch) * kVec, int(p.n_elems - ch * kVec));
-                else v[r] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-        if (lane == 0 && wbase > 0) {
-            const u32x2 t2 = *reinterpret_cast<const u32x2 *>(p.x + size_t(wbase) * kVec - 4);
-            prev_z = t2.x;
-            prev_w = t2.y;
+        for (int r = 0; r < kTokRounds; ++r) {
+            const uint32_t ch = wbase + r * kWaveSize + lane;
+            if (ch == n_full) v[r] = ld8_partial(p.x + size_t(ch) * kVec, int(p.n_elems - ch * kVec));
         }
     }
+    const uint16_t *pp = p.x + (chunk_wave && wbase > 0 ? size_t(wbase) * kVec - 4 : 0);
+    uint32_t prev_z = sld_u32(pp), prev_w = sld_u32(pp + 2);
+    if (!chunk_wave || wbase == 0) prev_z = prev_w = 0;
+    const uint32_t e_first = wbase * kVec;
+    const uint32_t cA = chunk_wave ? p.divT.div(e_first) : 0u;
+    const PairTaps<W> tA = sload_pair_taps<W>(p, cA);
+    const PairTaps<W> tB = sload_pair_taps<W>(p, cA + 1 < uint32_t(p.dim) ? cA + 1 : cA);
 
     for (int i = threadIdx.x; i <= B; i += kVarWaves * kWaveSize) {
         qsl[i] = p.sb.qsl[i];
@@ -814,12 +815,8 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         st = qsl[q] < 0 ? 0 : (qsl[q] > int32_t(T) ? int64_t(T) : int64_t(qsl[q]));
         en = qsl[q + 1] < st ? st : (qsl[q + 1] > int32_t(T) ? int64_t(T) : int64_t(qsl[q + 1]));
     };
-    // wave-uniform rows (at most two) and their taps
-    const uint32_t e_first = wbase * kVec;
-    const uint32_t cA = p.divT.div(e_first);
+    // wave-uniform rows (at most two); their taps were read above
     const uint32_t row_a = cA * T, row_end = row_a + T;
-    const PairTaps<W> tA = uniform(load_pair_taps<W>(p, cA));
-    const PairTaps<W> tB = (cA + 1 < uint32_t(p.dim)) ? uniform(load_pair_taps<W>(p, cA + 1)) : tA;
     // the sequence of the wave's first element; lanes of the first row walk
     // forward from it (a wave spans a few sequences), the second row searches
     const int32_t s_wave = __builtin_amdgcn_readfirstlane(seq_search(qsl, B, int64_t(e_first - row_a)));
