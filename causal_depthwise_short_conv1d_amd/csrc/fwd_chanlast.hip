@@ -372,8 +372,13 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_cl_one_kerne
     const int64_t T = p.sb.total_T;
     const int64_t g0 = int64_t(grp) * kOneGroup;
     const int64_t t0 = g0 + int64_t(wave) * kOneRows;
+
+    // The sequence's description comes through the scalar cache (a query
+    // every wave of a CU shares).  Whether the sequence covers [0, T) is
+    // decided before the rows are issued: rows in flight across the general
+    // routine would keep their registers and cost occupancy.
+    const SeqInfo si = seq_info_scalar(p.sb, 0);
     const LaneTaps<W> tp = lane_taps<W, true>(p, slab, lane);
-    const SeqInfo si = seq_info(p.sb, p.sb.qsl, 0);
     if (!(si.start == 0 && si.end == T)) {           // uniform across the launch
         const int64_t te = t0 + kOneRows < T ? t0 + kOneRows : T;
         if (t0 < T) run_tile<W, SILU, true>(p, t0, te, c0, nv, tp);

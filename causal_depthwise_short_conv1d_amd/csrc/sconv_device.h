@@ -251,4 +251,23 @@ __device__ __forceinline__ SeqInfo seq_info(const SeqBatch &sb, const int32_t *q
     return si;
 }
 
+// seq_info() of sequence s (wave-uniform) with every read a scalar load at
+// an address that is always readable (a null array reads query_start_loc
+// instead), so the reads need no branch and can overlap earlier loads.
+__device__ __forceinline__ SeqInfo seq_info_scalar(const SeqBatch &sb, int32_t s) {
+    SeqInfo si;
+    int64_t a = int32_t(sld_u32(sb.qsl + s)), b = int32_t(sld_u32(sb.qsl + s + 1));
+    a = a < 0 ? 0 : (a > sb.total_T ? sb.total_T : a);
+    b = b < a ? a : (b > sb.total_T ? sb.total_T : b);
+    si.start = a;
+    si.end = b;
+    const int32_t ci = int32_t(sld_u32(sb.cache_idx ? sb.cache_idx + s : sb.qsl));
+    const uint32_t hi = sld_u8(sb.has_init ? sb.has_init + s : reinterpret_cast<const uint8_t *>(sb.qsl));
+    si.line = sb.cache_idx ? int64_t(ci) : int64_t(s);
+    si.skip = (sb.cache_idx && si.line == sb.pad_slot_id) ||
+              (sb.cs && (si.line < 0 || si.line >= sb.num_lines));
+    si.init = sb.cs && sb.has_init && hi != 0;
+    return si;
+}
+
 }  // namespace sconv
