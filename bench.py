@@ -225,7 +225,7 @@ def main():
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "fwd_tok_long_kernel<4,true>",
+                     "traffic": traffic, "kernel": "fwd_tok_long_kernel<4,true,4>",
                      "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_us": round(kern_ms * 1e3, 2)},
     }

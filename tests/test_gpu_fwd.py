@@ -188,6 +188,42 @@ def test_one_sequence_long_rows_variants(T, dim, width, variant):
     check_full(g, activation="silu", label=f"long one seq T{T} dim{dim} W{width} {variant} silu")
 
 
+def strided_taps(g, width):
+    """The weights as a (dim, width) view with row stride width + 3 that starts
+    one element into its storage, and the bias one element in: taps whose
+    rows start at every 2-byte alignment, read through each kernel's general
+    path."""
+    dim = g["weight"].shape[0]
+    wide = torch.zeros(dim, width + 3, dtype=BF, device=DEV)
+    wide[:, 1:1 + width] = g["weight"]
+    g["weight"] = wide[:, 1:1 + width]
+    if g.get("bias") is not None:
+        b = torch.zeros(dim + 1, dtype=BF, device=DEV)
+        b[1:] = g["bias"]
+        g["bias"] = b[1:]
+    assert g["weight"].stride() == (width + 3, 1)
+    return g
+
+
+@pytest.mark.parametrize("width", [2, 3, 4, 5])
+@pytest.mark.parametrize("case", ["long_dim_tok", "varlen_dim_tok", "varlen_tok_dim", "one_tok_dim"])
+def test_strided_misaligned_weights(width, case):
+    if case == "long_dim_tok":
+        d = W.single_sequence(dim=24, T=2300, width=width, seed=900 + width, values="exact")
+    elif case == "one_tok_dim":
+        d = W.single_sequence(dim=264, T=300, width=width, seed=910 + width, values="exact",
+                              layout="tok_dim")
+    else:
+        lens = [700, 1, 2, 3, 2500, 9, 1200]
+        d = W.varlen_batch(lengths=lens, dim=40, width=width, seed=920 + width, num_lines=12,
+                           n_pad=1, values="exact",
+                           layout="dim_tok" if case == "varlen_dim_tok" else "tok_dim")
+    g = strided_taps(to_dev(d), width)
+    say(f"[fwd] strided weights {case} W{width}")
+    check_full(g, activation=None, exact=True, label=f"strided weights {case} W{width}")
+    check_full(g, activation="silu", label=f"strided weights {case} W{width} silu")
+
+
 @pytest.mark.parametrize("T,start", [(100, 5), (10, 3), (3000, 2)])
 def test_single_sequence_not_starting_at_zero(T, start):
     """query_start_loc [start, T] (outside the documented contract, which
