@@ -29,9 +29,6 @@
 // (possibly spilling into the next chunk) and writes the new state, so no
 // other lane can read a state that has already been overwritten.
 #include "sconv_device.h"
-#ifndef SCONV_LONG_ROUNDS
-#define SCONV_LONG_ROUNDS 4
-#endif
 
 namespace sconv {
 
@@ -41,11 +38,10 @@ constexpr int kChunksPerWave = kWaveSize * kTokRounds;
 constexpr uint32_t kWaveElems = kChunksPerWave * kVec;
 constexpr int kShortMinT = 16;                    // shortest row of the short-row kernel
 constexpr int kShortWaves = 256 * 8;             // waves that keep ~8 per CU busy
-#ifndef SCONV_LONG_WAVES
-#define SCONV_LONG_WAVES 4
-#endif
-constexpr int kLongWaves = SCONV_LONG_WAVES;                     // waves per long-row block (fewer, larger
+constexpr int kLongWaves = 4;                     // waves per long-row block (fewer, larger
                                                   // workgroups dispatch faster at 10^5 waves)
+constexpr int kLongRounds = 4;                    // 64-chunk rounds per long-row wave (measured:
+                                                  // 1 and 2 repeat the wave setup too often)
 
 // Weights of one channel for the dot2 path: taps as packed bf16 pairs
 // (w[2p], w[2p+1]), the odd last tap and the bias as fp32.
@@ -1049,9 +1045,9 @@ hipError_t launch_ws(const FwdTokParams &p, hipStream_t s) {
     } else if (p.sb.batch > 1) {
         fwd_tokmajor_kernel<W, SILU, true><<<grid, block, 0, s>>>(p);
     } else if (p.T >= kWaveElems) {
-        constexpr uint32_t kLB = kLongWaves * SCONV_LONG_ROUNDS * kWaveSize;
+        constexpr uint32_t kLB = kLongWaves * kLongRounds * kWaveSize;
         const uint32_t lb = (p.n_chunks + kLB - 1) / kLB;
-        fwd_tok_long_kernel<W, SILU, SCONV_LONG_ROUNDS><<<dim3(lb), dim3(kLongWaves * kWaveSize), 0, s>>>(p);
+        fwd_tok_long_kernel<W, SILU, kLongRounds><<<dim3(lb), dim3(kLongWaves * kWaveSize), 0, s>>>(p);
     } else if (p.T >= uint32_t(kShortMinT)) {
         // Rounds per wave, measured on gfx950: one round (the most waves in
         // flight) up to 512K chunks, two from there, four from 2M, where a

@@ -485,6 +485,30 @@ def test_split_sequence_bit_identical(layout):
         assert_bits(cs, st_full, f"split state at {k}")
 
 
+@pytest.mark.parametrize("width", [2, 4, 5])
+def test_split_long_rows_chain(width):
+    """A (dim, T) sequence cut into pieces of at least 2048 tokens, each run
+    by the long-row kernel with the state the previous call wrote (read back
+    through the scalar cache by the next launch): outputs and the final
+    state bit-identical to one call."""
+    T, dim = 7000, 96
+    d = to_dev(W.single_sequence(dim=dim, T=T, width=width, seed=830 + width))
+    full, st_full = run_gpu(d)
+    for cuts in ((2500,), (2048, 4096), (2400, 4700)):
+        cs = d["conv_states"].clone()
+        parts = []
+        bounds = (0,) + cuts + (T,)
+        for lo, hi in zip(bounds[:-1], bounds[1:]):
+            assert hi - lo >= 2048
+            o = S.conv1d_fwd_varlen(d["x"][:, lo:hi].contiguous(), d["weight"], d["bias"], cs,
+                                    torch.tensor([0, hi - lo], dtype=torch.int32, device=DEV),
+                                    has_initial_state=torch.ones(1, dtype=torch.bool, device=DEV))
+            parts.append(o)
+        torch.cuda.synchronize()
+        assert_bits(torch.cat(parts, dim=1), full, f"W{width} cuts {cuts}")
+        assert_bits(cs, st_full, f"W{width} cuts {cuts} state")
+
+
 def test_repeat_is_deterministic():
     d = W.varlen_batch(dim=2048, nseq=16, max_len=600, width=4, seed=901, device=DEV)
     a, sa = run_gpu(d, out_fill=0.0)      # pad rows are left untouched
