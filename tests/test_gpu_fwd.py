@@ -48,11 +48,12 @@ def run_oracle(d, activation="silu", pad_slot_id=-1, out_fill=None, channels=Non
     """Oracle on CPU copies; with `channels`, only those channels (all tokens)."""
     def cpu(t):
         return None if t is None else t.cpu()
-    x, w, b, cs = cpu(d["x"]), cpu(d["weight"]), cpu(d.get("bias")), cpu(d.get("conv_states"))
-    if channels is not None:
-        x, w = x[channels], w[channels]
-        b = b[channels] if b is not None else None
-        cs = cs[:, channels] if cs is not None else None
+    x, w, b, cs = d["x"], d["weight"], d.get("bias"), d.get("conv_states")
+    if channels is not None:                   # select on the device: only those rows move
+        x, w = x[channels.to(x.device)], w[channels.to(w.device)]
+        b = b[channels.to(b.device)] if b is not None else None
+        cs = cs[:, channels.to(cs.device)] if cs is not None else None
+    x, w, b, cs = cpu(x), cpu(w), cpu(b), cpu(cs)
     cs = cs.clone() if cs is not None else None
     out = torch.full(x.shape, 0.0 if out_fill is None else out_fill, dtype=BF)
     oracle.fwd_varlen(x, w, b, cs, cpu(d["query_start_loc"]), out,
@@ -252,6 +253,46 @@ def test_long_prefill_channel_contiguous():
     r_out, r_cs = run_oracle(d, channels=ch)
     assert_close(g_out[ch.to(DEV)], r_out, "T4195 (T,dim) sampled out")
     assert_bits(g_cs[0], d["x"][:, T - 3:], "T4195 (T,dim) state")
+
+
+@pytest.mark.parametrize("layout,T", [("dim_tok", (2 ** 32 - 1) // 8192), ("tok_dim", 300000)])
+def test_largest_single_sequence(layout, T):
+    """The largest (dim, T) sequence the 32-bit element indexing of the
+    token-contiguous kernels accepts (dim 8192, T 524287: 2^32 - 8192
+    elements, 8.6 GB per tensor), and a (T, dim) sequence past 2^31 elements:
+    sampled channels against the oracle, every state value against the
+    sequence's last width-1 inputs."""
+    dim = 8192
+    d = W.single_sequence(dim=dim, T=T, width=4, seed=W.seed_for(3, 77), device=DEV, layout=layout)
+    say(f"[fwd] largest single sequence {layout} dim{dim} T{T}")
+    g_out, g_cs = run_gpu(d)
+    ch = sample_channels(dim, 24, seed=T % 1000)
+    r_out, r_cs = run_oracle(d, channels=ch)
+    assert_close(g_out[ch.to(DEV)], r_out, f"{layout} T{T} sampled out")
+    assert_bits(g_cs[0], d["x"][:, T - 3:], f"{layout} T{T} state")
+    del d, g_out, g_cs
+    torch.cuda.empty_cache()
+
+
+def test_largest_varlen_token_contiguous():
+    """A 64-sequence batch in token-contiguous rows at the 32-bit element
+    limit (dim 8192, 524287 tokens): pads, mixed history, sampled channels
+    against the oracle in every sequence and the state property of every
+    line."""
+    dim, total = 8192, (2 ** 32 - 1) // 8192
+    g = torch.Generator().manual_seed(4242)
+    cuts = torch.sort(torch.randperm(total - 1, generator=g)[:63] + 1).values
+    lens = torch.diff(torch.cat([torch.tensor([0]), cuts, torch.tensor([total])])).tolist()
+    d = W.varlen_batch(lengths=lens, dim=dim, width=4, seed=W.seed_for(4, 77), layout="dim_tok",
+                       device=DEV)
+    say(f"[fwd] largest varlen (dim,T) dim{dim} total_T {total}")
+    g_out, g_cs = run_gpu(d, out_fill=-3.0)
+    ch = sample_channels(dim, 16, seed=11)
+    r_out, r_cs = run_oracle(d, out_fill=-3.0, channels=ch)
+    assert_close(g_out[ch.to(DEV)], r_out, "largest varlen sampled out")
+    assert_bits(g_cs[:, ch.to(DEV)], r_cs, "largest varlen sampled state")
+    del d, g_out, g_cs
+    torch.cuda.empty_cache()
 
 
 # One sequence in (T, dim) rows: four 8-row tiles per workgroup with the
