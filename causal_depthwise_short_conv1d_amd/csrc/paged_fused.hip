@@ -6,8 +6,9 @@
 // own D sub-range): they share the per-token metadata and differ only in
 // their rows of x / out, taps and D offsets.
 //
-// Decomposition: a wave owns [kPagedBT tokens x 256 channels of one stream]
-// (the slabs of all streams are numbered consecutively); each lane owns
+// Decomposition: a wave owns [BT tokens x 256 channels of one stream]
+// (the slabs of all streams are numbered consecutively; BT is 16, or 8 for
+// a step that would not fill the chip once with 16); each lane owns
 // 4 adjacent channels, which lie in one head (ws % 8 == 0), so every cache
 // access of a lane is one 8-byte vector at D offset off_s + c % ws.
 // Latency, not bandwidth, is the hazard here (decode rows are pure gathers
@@ -74,7 +75,7 @@ __device__ __forceinline__ void st8(__amdgpu_buffer_rsrc_t r, uint32_t voff, int
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(ui32x2, v), r, voff, int(soff), AUX);
 }
 
-template <int W, bool SILU, bool RESID>
+template <int W, bool SILU, bool RESID, int BT>
 __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_kernel(PagedParams p) {
     constexpr int H = W - 1;
     __shared__ int32_t s_qsl[kQslLdsMax];
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     // last tile reads clamped addresses and zeros, and stops after the
     // barrier.  (Issuing the tile's own rows here as well was measured: it
     // raises registers and was slower.)
-    const int64_t tile_start = int64_t(tt) * kPagedBT;
+    const int64_t tile_start = int64_t(tt) * BT;
     const int64_t xbase = tile_start >= H ? tile_start - H : 0;
     const __amdgpu_buffer_rsrc_t xr =
         rsrc(st.x + xbase * st.x_st, (p.T - xbase - 1) * st.x_st * 2 + int64_t(st.C) * 2);
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
         const int64_t row = tile_start - H + k;
         win[k] = ld8<kNt>(xr, xoff, row >= 0 ? (row - xbase) * st.x_st * 2 : int64_t(kOob));
     }
-    const int64_t t_lane = tile_start + (lane < kPagedBT ? lane : 0);
+    const int64_t t_lane = tile_start + (lane < BT ? lane : 0);
     const int64_t t_safe = t_lane < p.T ? t_lane : p.T - 1;
     const int64_t slot_l = p.slot[t_safe];
     const int64_t pos_l = p.pos[t_safe];
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
         }
     }
 
-    const int n_tok = int((p.T - tile_start) < kPagedBT ? (p.T - tile_start) : kPagedBT);
+    const int n_tok = int((p.T - tile_start) < BT ? (p.T - tile_start) : BT);
     int64_t actual = p.num_reqs > 0 ? int64_t(qsl[p.num_reqs]) : 0;
     actual = actual < 0 ? 0 : (actual > p.T ? p.T : actual);
 
@@ -159,43 +160,42 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     //   m_sblk / m_sn : physical block / slot of the insert (m_sblk < 0: none)
     //   m_tblk / m_tn : per tap, the block / slot of a cached position, or
     //                   kTapIntra (a row of x) or kTapZero.
-    int32_t m_sblk = -1, m_sn = 0;
-    int32_t m_pad = 1;
-    int64_t m_qs = 0;
-    int32_t m_tblk[H], m_tn[H];
+    // Every lane resolves its token without a branch around a load (a load
+    // under a lane-dependent branch would wait before the branch joins, and
+    // the block-table reads of a tile's taps would become a chain of round
+    // trips): lanes past the tile, pads and taps without a table entry read
+    // valid stand-in addresses and their values are discarded.
+    const int64_t tl = tile_start + lane;      // the lane's token
+    const bool tok = lane < n_tok;
+    const int64_t slot = slot_l;
+    const int64_t pos = pos_l;
+    const int32_t m_pad = (!tok || slot < 0 || tl >= actual) ? 1 : 0;
+    const bool ins = !m_pad && slot < p.slot_lim;
+    const uint32_t s32 = ins ? uint32_t(slot) : 0u;
+    const uint32_t sblk = p.div_n.div(s32);
+    const int32_t m_sblk = ins ? int32_t(sblk) : -1;
+    const int32_t m_sn = int32_t(s32 - sblk * uint32_t(p.block_size));
+    const int32_t r = seq_search(qsl, p.num_reqs, tok ? tl : tile_start);
+    const int64_t qs_r = qsl[r];
+    const int64_t m_qs = m_pad ? 0 : qs_r;
+    int32_t m_tblk[H], m_tn[H], bt_v[H];
+    bool need[H];
 #pragma unroll
     for (int j = 0; j < H; ++j) {
-        m_tblk[j] = kTapZero;
-        m_tn[j] = 0;
+        const int64_t src = pos - H + j;
+        const int64_t row = tl - H + j;
+        const bool live = !m_pad && src >= 0;
+        const bool intra = live && row >= qs_r;
+        need[j] = live && !intra && src < p.src_lim;
+        const uint32_t c32 = need[j] ? uint32_t(src) : 0u;
+        const uint32_t lb = p.div_n.div(c32);
+        m_tn[j] = int32_t(c32 - lb * uint32_t(p.block_size));
+        bt_v[j] = *(need[j] ? p.bt + (int64_t(r) * p.bt_sr + lb) : p.bt_rd);
+        m_tblk[j] = intra ? kTapIntra : kTapZero;
     }
-    if (lane < n_tok) {
-        const int64_t t = tile_start + lane;
-        const int64_t slot = slot_l;
-        const int64_t pos = pos_l;
-        m_pad = (slot < 0 || t >= actual) ? 1 : 0;
-        if (!m_pad) {
-            const int64_t sb = slot / p.block_size;
-            if (sb < p.num_blocks) {
-                m_sblk = int32_t(sb);
-                m_sn = int32_t(slot % p.block_size);
-            }
-            const int32_t r = seq_search(qsl, p.num_reqs, t);
-            m_qs = qsl[r];
 #pragma unroll
-            for (int j = 0; j < H; ++j) {
-                const int64_t src = pos - H + j;
-                const int64_t row = t - H + j;
-                if (src < 0) continue;
-                if (row >= m_qs) { m_tblk[j] = kTapIntra; continue; }
-                const int64_t lblk = src / p.block_size;
-                if (lblk >= p.max_blocks) continue;
-                const int64_t blk = p.bt[int64_t(r) * p.bt_sr + lblk];
-                if (blk < 0 || blk >= p.num_blocks) continue;
-                m_tblk[j] = int32_t(blk);
-                m_tn[j] = int32_t(src % p.block_size);
-            }
-        }
-    }
+    for (int j = 0; j < H; ++j)
+        if (need[j] && bt_v[j] >= 0 && bt_v[j] < p.num_blocks) m_tblk[j] = bt_v[j];
 
     const __amdgpu_buffer_rsrc_t orr =
         rsrc(st.out + tile_start * st.o_st, (p.T - tile_start - 1) * st.o_st * 2 + int64_t(st.C) * 2);
@@ -287,8 +287,13 @@ hipError_t launch_ws(const PagedParams &p, bool residual, hipStream_t s) {
     const uint64_t waves = uint64_t(p.n_tiles) * uint64_t(p.total_slabs);
     const uint32_t blocks = uint32_t((waves + kPagedWavesPerBlock - 1) / kPagedWavesPerBlock);
     const dim3 grid(blocks), block(kPagedWavesPerBlock * kWaveSize);
-    if (residual) paged_fused_kernel<W, SILU, true><<<grid, block, 0, s>>>(p);
-    else paged_fused_kernel<W, SILU, false><<<grid, block, 0, s>>>(p);
+    if (p.tile_bt == kPagedBTSmall) {
+        if (residual) paged_fused_kernel<W, SILU, true, kPagedBTSmall><<<grid, block, 0, s>>>(p);
+        else paged_fused_kernel<W, SILU, false, kPagedBTSmall><<<grid, block, 0, s>>>(p);
+    } else {
+        if (residual) paged_fused_kernel<W, SILU, true, kPagedBT><<<grid, block, 0, s>>>(p);
+        else paged_fused_kernel<W, SILU, false, kPagedBT><<<grid, block, 0, s>>>(p);
+    }
     return hipGetLastError();
 }
 

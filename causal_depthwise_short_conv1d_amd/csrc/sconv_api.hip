@@ -371,6 +371,10 @@ int sconv_paged_fused_multi(int32_t num_streams, const void *const *x,
         !aligned(query_start_loc, 4) || !aligned(block_table, 4))
         return SCONV_ERR_ALIGN;
     if (c_stride_blk * 2 >= kMaxDescriptorSpan) return SCONV_ERR_SHAPE;
+    // slots and block-table positions are resolved in 32-bit arithmetic
+    if (num_blocks * int64_t(block_size) >= (int64_t(1) << 31) ||
+        int64_t(max_blocks) * block_size >= (int64_t(1) << 31))
+        return SCONV_ERR_SHAPE;
     const Span sc = span_of(cache, {num_blocks, num_heads, block_size, head_dim},
                             {c_stride_blk, c_stride_head, c_stride_slot, 1});
 
@@ -437,8 +441,16 @@ int sconv_paged_fused_multi(int32_t num_streams, const void *const *x,
     p.bt = block_table;
     p.bt_sr = bt_stride_req;
     p.max_blocks = block_table ? max_blocks : 0;
+    p.div_n = FastDivU32::make(uint32_t(block_size));
+    p.slot_lim = num_blocks * int64_t(block_size);
+    p.src_lim = int64_t(p.max_blocks) * block_size;
+    p.bt_rd = (block_table && num_reqs > 0 && max_blocks > 0) ? block_table : query_start_loc;
     p.T = num_tokens;
-    p.n_tiles = int32_t((num_tokens + kPagedBT - 1) / kPagedBT);
+    // A step that would not fill the chip once with 16-token tiles takes
+    // 8-token tiles: twice the waves, each with half the chain of round trips.
+    const int64_t tiles16 = (num_tokens + kPagedBT - 1) / kPagedBT;
+    p.tile_bt = tiles16 * total_slabs < kPagedFillWaves ? kPagedBTSmall : kPagedBT;
+    p.n_tiles = int32_t((num_tokens + p.tile_bt - 1) / p.tile_bt);
     if (uint64_t(p.n_tiles) * uint64_t(total_slabs) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;
     p.total_slabs = int32_t(total_slabs);
     return launch_status(launch_paged_fused(p, width, activation == SCONV_ACT_SILU,

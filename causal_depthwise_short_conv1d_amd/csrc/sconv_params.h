@@ -136,7 +136,15 @@ struct PagedParams {
     int64_t bt_sr;
     int32_t max_blocks;
     int64_t T;
-    int32_t n_tiles;
+    int32_t tile_bt;           // tokens per tile: kPagedBT or kPagedBTSmall
+    int32_t n_tiles;           // ceil(T / tile_bt)
+    // Slot and position arithmetic in 32 bits: the host bounds every valid
+    // slot (slot_lim = num_blocks * block_size) and every position with a
+    // block-table entry (src_lim = max_blocks * block_size) below 2^31.
+    FastDivU32 div_n;          // division by block_size
+    int64_t slot_lim;
+    int64_t src_lim;
+    const int32_t *bt_rd;      // the block table, or query_start_loc when it is empty
 };
 
 // Launchers: each enqueues one kernel and returns hipGetLastError().
@@ -159,7 +167,9 @@ constexpr int kClWavesPerBlock = 4;
 constexpr int kCpl = 4;                          // channels per lane, channel-contiguous
 constexpr int kClSlab = kWaveSize * kCpl;        // channels per wave there (256)
 constexpr int kPagedWavesPerBlock = 4;
-constexpr int kPagedBT = 16;                     // tokens per paged wave tile
+constexpr int kPagedBT = 16;                     // tokens per paged wave tile (the larger size)
+constexpr int kPagedBTSmall = 8;                 // tile for steps of under one generation of waves
+constexpr int64_t kPagedFillWaves = 256 * 32;    // waves that fill the chip once
 constexpr int kPagedSlab = 256;                  // channels per paged wave (4 per lane)
 // Buffer-descriptor offsets are 32-bit: rows, state lines and cache blocks
 // reached through one descriptor must span less than this many bytes.

@@ -291,7 +291,10 @@ int sconv_seq_metadata(const int32_t *query_start_loc, int32_t num_reqs,
  *              every absolute position: position p of request r lives in
  *              block block_table[r*bt_stride_req + p / block_size], slot
  *              p % block_size, D range [off_s, off_s + ws).
- *              Requires ws % 8 == 0, off_s % 8 == 0, off_s + ws <= head_dim.
+ *              Requires ws % 8 == 0, off_s % 8 == 0, off_s + ws <= head_dim,
+ *              and num_blocks * block_size and max_blocks * block_size
+ *              below 2^31 (slots and positions are resolved in 32-bit
+ *              arithmetic), else SCONV_ERR_SHAPE.
  * positions    [num_tokens] int64 absolute position of each row.
  * slot_mapping [num_tokens] int64 flat slot block*block_size + offset of
  *              each row; < 0 marks a pad row.

@@ -242,6 +242,8 @@ def test_paged_validation(lib):
     assert paged(lib, off=4) == EALIGN
     assert paged(lib, csn=500) == EALIGN
     assert paged(lib, x=ctypes.c_void_p(BASE + GB + 8)) == EALIGN
+    assert paged(lib, nb=1 << 27) == ESHAPE       # 2^31 slots: beyond 32-bit slot arithmetic
+    assert paged(lib, mb=1 << 27, btsr=1 << 27) == ESHAPE   # positions past 2^31 in the table
     assert paged(lib, out=addr(1)) == EALIAS
     assert paged(lib, out=ctypes.c_void_p(BASE + 3 * GB + 1024)) == EALIAS   # out inside cache
 

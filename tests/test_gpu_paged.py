@@ -68,6 +68,23 @@ def test_paged_exact_values(width):
     run_both(d, activation=None, residual=True, exact=True, label=f"exact W{width}")
 
 
+@pytest.mark.parametrize("width", [3, 4])
+def test_paged_sixteen_token_tiles_exact(width):
+    """A step large enough (8232 tokens x 16 slabs) for the 16-token tiles
+    (smaller steps take 8-token tiles): decode tokens, prefill chunks with
+    cached taps, interior and trailing pads, exact values, bit-exact against
+    the oracle."""
+    cfg = dict(H=32, ws=128, N=16, D=256, off_s=64, num_blocks=1024, n_decode=40,
+               n_prefill=16, chunk=512, max_pos=4000)
+    d2 = W.paged_batch(**cfg, width=width, pad_frac=0.05, trailing_pad=5, seed=450 + width,
+                       values="exact", with_bias=True, device=DEV)
+    assert d2["x"].shape[0] // 16 * (cfg["H"] * cfg["ws"] // 256) >= 8192
+    host = {k: (v.cpu() if isinstance(v, torch.Tensor) and k != "cache" else v)
+            for k, v in d2.items()}
+    run_both(host, activation=None, residual=True, exact=True, cache_dev=d2["cache"],
+             label=f"16-token tiles W{width}")
+
+
 def test_paged_idempotent_on_gpu():
     d = W.paged_batch(**SMALL, width=4, pad_frac=0.1, seed=300)
     out1, cache1 = run_both(d, label="first")
