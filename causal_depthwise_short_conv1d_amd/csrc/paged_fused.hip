@@ -271,9 +271,11 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
                         o[ch] += (ch & 1) ? bf_hi(d) : bf_lo(d);
                     }
                 }
+                // a temporal store: the L2 gathers each output row from the
+                // pieces the waves of its other slabs write
                 if (active)
-                    st8<kNt>(orr, xoff, (t - tile_start) * st.o_st * 2,
-                             u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
+                    st8<0>(orr, xoff, (t - tile_start) * st.o_st * 2,
+                           u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
 #pragma unroll
                 for (int k = 0; k + 1 < H; ++k) win[k] = win[k + 1];
                 win[H - 1] = xv[u];
