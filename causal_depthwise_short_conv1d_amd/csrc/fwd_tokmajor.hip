@@ -489,7 +489,6 @@ __global__ __launch_bounds__(kWaveSize) void fwd_tok_short_kernel(FwdTokParams p
     if (wbase >= p.n_chunks) return;
     const uint32_t T = p.T;
     const uint32_t n_full = p.n_elems / kVec;
-    const SeqInfo s0 = seq_info(p.sb, p.sb.qsl, 0);      // used after the loads are issued
 
     // The wave's elements [e0, e_end) and rows [c_first, c_last]; a row that
     // starts in a full chunk of the wave is owned by the wave.
@@ -505,13 +504,8 @@ __global__ __launch_bounds__(kWaveSize) void fwd_tok_short_kernel(FwdTokParams p
     const Rsrc xr = make_rsrc(p.x + xb0, int64_t(x_hi - xb0) * 2);
     const Rsrc wr = make_rsrc(p.w + int64_t(c_first) * p.w_sd, int64_t(n_rows) * p.w_sd * 2);
     const Rsrc br = make_rsrc(p.bias ? p.bias + c_first : p.x, p.bias ? int64_t(n_rows) * 2 : 0);
-    const bool state_ok = p.sb.cs != nullptr && !s0.skip;
-    const Rsrc sr = make_rsrc(state_ok ? p.sb.cs + s0.line * p.sb.cs_sl + int64_t(c_first) * p.sb.cs_sd
-                                       : p.x,
-                              state_ok ? (int64_t(n_rows - 1) * p.sb.cs_sd + int64_t(H - 1) * p.sb.cs_st + 1) * 2
-                                       : 0);
 
-    // chunk loads
+    // chunk loads first: they depend on the launch arguments alone
     u32x4 v[ROUNDS];
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
@@ -530,11 +524,21 @@ __global__ __launch_bounds__(kWaveSize) void fwd_tok_short_kernel(FwdTokParams p
     uint32_t rh[H], rx[H], rn[H];
 #pragma unroll
     for (int k = 0; k < H; ++k) {
-        rh[k] = buf_ld16(sr, row_own ? uint32_t(int64_t(lane) * p.sb.cs_sd + int64_t(k) * p.sb.cs_st) * 2
-                                     : kOob);
         rx[k] = buf_ld16(xr, row_own ? (my_hp + k - xb0) * 2 : kOob);
         rn[k] = buf_ld16(xr, row_own ? (my_hp + T - H + k - xb0) * 2 : kOob);
     }
+    // the sequence's description through the scalar cache, then the owned
+    // rows' cached histories (their line is known only now)
+    const SeqInfo s0 = seq_info_scalar(p.sb, 0);
+    const bool state_ok = p.sb.cs != nullptr && !s0.skip;
+    const Rsrc sr = make_rsrc(state_ok ? p.sb.cs + s0.line * p.sb.cs_sl + int64_t(c_first) * p.sb.cs_sd
+                                       : p.x,
+                              state_ok ? (int64_t(n_rows - 1) * p.sb.cs_sd + int64_t(H - 1) * p.sb.cs_st + 1) * 2
+                                       : 0);
+#pragma unroll
+    for (int k = 0; k < H; ++k)
+        rh[k] = buf_ld16(sr, row_own ? uint32_t(int64_t(lane) * p.sb.cs_sd + int64_t(k) * p.sb.cs_st) * 2
+                                     : kOob);
 
     if (s0.skip) return;                                // padded sequence: nothing to do
     // the sequence is not the whole row, or (never, with the host's choice of
@@ -644,21 +648,48 @@ template <int W, bool SILU>
 __global__ __launch_bounds__(kRowsBlock) void fwd_tok_rows_kernel(FwdTokParams p) {
     constexpr int H = W - 1;
     constexpr int kMaxT = kShortMinT - 1;
-    const int32_t c = int32_t(blockIdx.x) * kRowsBlock + int32_t(threadIdx.x);
+    const uint32_t c0 = blockIdx.x * uint32_t(kRowsBlock);            // the block's first row
+    const int32_t c = int32_t(c0) + int32_t(threadIdx.x);
     if (c >= p.dim) return;
-    const SeqInfo s0 = seq_info(p.sb, p.sb.qsl, 0);
+    // The block's rows and taps go out first, through descriptors based at
+    // the block's first row (wave-uniform), so no load waits on a branch:
+    // a lane reads its whole row (T < 16; past T reads 0).
+    const uint32_t n_rows = uint32_t(p.dim) - c0 < uint32_t(kRowsBlock) ? uint32_t(p.dim) - c0
+                                                                         : uint32_t(kRowsBlock);
+    const uint32_t T = p.T;
+    const Rsrc xr = make_rsrc(p.x + size_t(c0) * T, int64_t(n_rows) * T * 2);
+    const uint32_t xo = uint32_t(threadIdx.x) * T;
+    uint16_t row[kMaxT];
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) row[t] = buf_ld16(xr, uint32_t(t) < T ? (xo + t) * 2 : kOob);
+    const Rsrc wr = make_rsrc(p.w + int64_t(c0) * p.w_sd, int64_t(n_rows) * p.w_sd * 2);
+    const Rsrc br = make_rsrc(p.bias_rd + c0, p.bias ? int64_t(n_rows) * 2 : 0);
+    Taps<W> tp;
+#pragma unroll
+    for (int k = 0; k < W; ++k)
+        tp.w[k] = bf_one(buf_ld16(wr, uint32_t(int64_t(threadIdx.x) * p.w_sd + k) * 2));
+    tp.b = bf_one(buf_ld16(br, uint32_t(threadIdx.x) * 2));
+    const SeqInfo s0 = seq_info_scalar(p.sb, 0);
+    // the cached history: a descriptor over the block's rows of the line
+    const bool rd = s0.init && !s0.skip;
+    const Rsrc hr = make_rsrc(rd ? p.sb.cs + s0.line * p.sb.cs_sl + int64_t(c0) * p.sb.cs_sd : p.x,
+                              rd ? (int64_t(n_rows - 1) * p.sb.cs_sd + int64_t(H - 1) * p.sb.cs_st + 1) * 2 : 0);
+    uint16_t u[H + kMaxT];
+#pragma unroll
+    for (int k = 0; k < H; ++k)
+        u[k] = buf_ld16(hr, uint32_t(int64_t(threadIdx.x) * p.sb.cs_sd + int64_t(k) * p.sb.cs_st) * 2);
     if (s0.skip) return;
     const int32_t a = int32_t(s0.start), L = int32_t(s0.end - s0.start);
     if (L <= 0) return;
-    const uint16_t *xr = p.x + size_t(c) * p.T + a;
-    uint16_t *orow = p.out + size_t(c) * p.T + a;
-    uint16_t *st = p.sb.cs ? p.sb.cs + s0.line * p.sb.cs_sl + int64_t(c) * p.sb.cs_sd : nullptr;
-    uint16_t u[H + kMaxT];
+    if (a == 0) {                                        // uniform: the row from its start
 #pragma unroll
-    for (int k = 0; k < H; ++k) u[k] = s0.init ? st[k * p.sb.cs_st] : uint16_t(0);
+        for (int t = 0; t < kMaxT; ++t) u[H + t] = t < L ? row[t] : uint16_t(0);
+    } else {
+        const uint16_t *xs = p.x + size_t(c) * T + a;
 #pragma unroll
-    for (int t = 0; t < kMaxT; ++t) u[H + t] = t < L ? xr[t] : uint16_t(0);
-    const Taps<W> tp = load_taps<W>(p, uint32_t(c));
+        for (int t = 0; t < kMaxT; ++t) u[H + t] = t < L ? xs[t] : uint16_t(0);
+    }
+    uint16_t *orow = p.out + size_t(c) * T + a;
 #pragma unroll
     for (int t = 0; t < kMaxT; ++t) {
         if (t >= L) break;
@@ -667,8 +698,9 @@ __global__ __launch_bounds__(kRowsBlock) void fwd_tok_rows_kernel(FwdTokParams p
         for (int k = 0; k < W; ++k) acc = __builtin_fmaf(tp.w[k], bf_one(u[t + k]), acc);
         orow[t] = to_bf16(act<SILU>(acc));
     }
-    if (st) {
+    if (p.sb.cs) {
         // new state: u[L .. L+H), picked without dynamic indexing
+        uint16_t *st = p.sb.cs + s0.line * p.sb.cs_sl + int64_t(c) * p.sb.cs_sd;
 #pragma unroll
         for (int k = 0; k < H; ++k) {
             uint16_t hv = 0;

@@ -176,6 +176,11 @@ int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
         tokmajor_ok(o_stride_dim, o_stride_tok, dim, T)) {
         const uint64_t n = uint64_t(dim) * uint64_t(T);
         if (n >= (uint64_t(1) << 32)) return SCONV_ERR_SHAPE;
+        // one descriptor spans a state line's channels
+        const int64_t line_span =
+            conv_states ? ((int64_t(dim) - 1) * cs_stride_dim + int64_t(width - 2) * cs_stride_tok + 1) * 2
+                        : 0;
+        if (line_span >= kMaxDescriptorSpan) return SCONV_ERR_SHAPE;
         FwdTokParams p;
         p.x = static_cast<const uint16_t *>(x);
         p.out = static_cast<uint16_t *>(out);
