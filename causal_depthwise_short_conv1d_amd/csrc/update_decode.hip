@@ -33,21 +33,48 @@ constexpr int kUpdGroup = 4;   // inputs loaded ahead of their outputs
 template <int W, bool SILU>
 __global__ __launch_bounds__(kUpdBlock) void update_kernel(UpdParams p, uint32_t cblocks) {
     constexpr int H = W - 1;
-    const uint32_t b = blockIdx.x / cblocks;
-    const int32_t c = int32_t((blockIdx.x % cblocks) * kUpdBlock + threadIdx.x);
+    const uint32_t b = blockIdx.x / cblocks;            // the entry (workgroup-uniform)
+    const int32_t c0 = int32_t((blockIdx.x % cblocks) * kUpdBlock);
+    const int32_t c = c0 + int32_t(threadIdx.x);
     if (int32_t(b) >= p.batch || c >= p.dim) return;
-    const int64_t line = p.cache_idx ? int64_t(p.cache_idx[b]) : int64_t(b);
+    const int32_t nch = p.dim - c0 < kUpdBlock ? p.dim - c0 : kUpdBlock;
+    const uint32_t lc = uint32_t(threadIdx.x);
+
+    // The first group of inputs, the taps and the bias go out first, through
+    // descriptors based at the workgroup's first channel, with no branch:
+    // they depend on the launch arguments alone.  (Inputs past seqlen, and a
+    // missing bias, read 0.)
+    const int32_t g0 = p.seqlen < kUpdGroup ? p.seqlen : kUpdGroup;
+    const Rsrc xr = make_rsrc(p.x + int64_t(b) * p.x_sb + int64_t(c0) * p.x_sd,
+                              (int64_t(nch - 1) * p.x_sd + int64_t(g0 - 1) * p.x_st + 1) * 2);
+    uint16_t xv0[kUpdGroup];
+#pragma unroll
+    for (int i = 0; i < kUpdGroup; ++i)
+        xv0[i] = buf_ld16(xr, i < g0 ? uint32_t(int64_t(lc) * p.x_sd + int64_t(i) * p.x_st) * 2 : kOob);
+    const Rsrc wr = make_rsrc(p.w + int64_t(c0) * p.w_sd, (int64_t(nch - 1) * p.w_sd + W) * 2);
+    const Rsrc br = make_rsrc(p.bias ? p.bias + c0 : p.w, p.bias ? int64_t(nch) * 2 : 0);
+    float wf[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) wf[k] = bf_one(buf_ld16(wr, uint32_t(int64_t(lc) * p.w_sd + k) * 2));
+    const float b0 = bf_one(buf_ld16(br, lc * 2));
+
+    // The entry's line and option values, read together through the scalar
+    // cache (a missing array reads a stand-in dword of x, discarded).
+    const void *sx = reinterpret_cast<const void *>(reinterpret_cast<uintptr_t>(p.x) & ~uintptr_t(3));
+    const int32_t ci = int32_t(sld_u32(p.cache_idx ? static_cast<const void *>(p.cache_idx + b) : sx));
+    const int32_t na = int32_t(sld_u32(p.num_acc ? static_cast<const void *>(p.num_acc + b) : sx));
+    const int32_t seen = int32_t(sld_u32(p.ring_seen ? static_cast<const void *>(p.ring_seen + b) : sx));
+    const int64_t line = p.cache_idx ? int64_t(ci) : int64_t(b);
     if ((p.cache_idx && line == p.pad_slot_id) || line < 0 || line >= p.num_lines) return;
 
     const int32_t L = p.state_len;
     int32_t off = 0;     // first history column (speculative decoding)
     int32_t rcol = 0;    // ring: column of the next input
     if (p.num_acc) {
-        off = p.num_acc[b] - 1;
+        off = na - 1;
         if (off < 0 || off > L - H) return;
     }
     if (p.ring_seen) {
-        const int32_t seen = p.ring_seen[b];
         if (seen < 0) return;
         rcol = seen % L;
     }
@@ -66,10 +93,6 @@ __global__ __launch_bounds__(kUpdBlock) void update_kernel(UpdParams p, uint32_t
         }
         win[k] = row[int64_t(col) * p.cs_st];
     }
-    float wf[W];
-#pragma unroll
-    for (int k = 0; k < W; ++k) wf[k] = bf_one(p.w[int64_t(c) * p.w_sd + k]);
-    const float b0 = p.bias ? bf_one(p.bias[c]) : 0.0f;
 
     // Speculative roll: the line restarts with the history minus its oldest
     // input (the new inputs follow at columns H-1 onward).
@@ -83,9 +106,14 @@ __global__ __launch_bounds__(kUpdBlock) void update_kernel(UpdParams p, uint32_t
     const int32_t ring_from = p.seqlen - L;    // ring: earlier inputs are overwritten anyway
     for (int32_t t0 = 0; t0 < p.seqlen; t0 += kUpdGroup) {
         uint16_t xv[kUpdGroup];
+        if (t0 == 0) {
 #pragma unroll
-        for (int i = 0; i < kUpdGroup; ++i)
-            xv[i] = t0 + i < p.seqlen ? xp[int64_t(t0 + i) * p.x_st] : uint16_t(0);
+            for (int i = 0; i < kUpdGroup; ++i) xv[i] = xv0[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < kUpdGroup; ++i)
+                xv[i] = t0 + i < p.seqlen ? xp[int64_t(t0 + i) * p.x_st] : uint16_t(0);
+        }
 #pragma unroll
         for (int i = 0; i < kUpdGroup; ++i) {
             const int32_t t = t0 + i;
