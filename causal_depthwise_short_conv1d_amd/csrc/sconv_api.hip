@@ -239,12 +239,6 @@ int conv1d_update(const void *x, int64_t x_stride_seq, int64_t x_stride_dim,
         return SCONV_ERR_ALIGN;
     const uint64_t cblocks = (uint64_t(dim) + 255) / 256;
     if (cblocks * uint64_t(batch) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;
-    // descriptors span a workgroup's 256 channels of one entry's first four
-    // inputs, and of the taps
-    if ((int64_t(255) * x_stride_dim + int64_t((seqlen < 4 ? seqlen : 4) - 1) * x_stride_tok + 1) * 2 >=
-            kMaxDescriptorSpan ||
-        (int64_t(255) * w_stride_dim + width) * 2 >= kMaxDescriptorSpan)
-        return SCONV_ERR_SHAPE;
 
     const Span sx = span_of(x, {batch, dim, seqlen}, {x_stride_seq, x_stride_dim, x_stride_tok});
     const Span so = span_of(out, {batch, dim, seqlen}, {o_stride_seq, o_stride_dim, o_stride_tok});

@@ -40,22 +40,24 @@ __global__ __launch_bounds__(kUpdBlock) void update_kernel(UpdParams p, uint32_t
     const int32_t nch = p.dim - c0 < kUpdBlock ? p.dim - c0 : kUpdBlock;
     const uint32_t lc = uint32_t(threadIdx.x);
 
-    // The first group of inputs, the taps and the bias go out first, through
-    // descriptors based at the workgroup's first channel, with no branch:
-    // they depend on the launch arguments alone.  (Inputs past seqlen, and a
-    // missing bias, read 0.)
+    // The first group of inputs, the taps and the bias go out first, with no
+    // branch: they depend on the launch arguments alone.  An input past
+    // seqlen re-reads the first one and is discarded; the bias comes through
+    // a descriptor based at the workgroup's first channel (none reads 0).
     const int32_t g0 = p.seqlen < kUpdGroup ? p.seqlen : kUpdGroup;
-    const Rsrc xr = make_rsrc(p.x + int64_t(b) * p.x_sb + int64_t(c0) * p.x_sd,
-                              (int64_t(nch - 1) * p.x_sd + int64_t(g0 - 1) * p.x_st + 1) * 2);
+    const uint16_t *xp = p.x + int64_t(b) * p.x_sb + int64_t(c) * p.x_sd;
     uint16_t xv0[kUpdGroup];
 #pragma unroll
-    for (int i = 0; i < kUpdGroup; ++i)
-        xv0[i] = buf_ld16(xr, i < g0 ? uint32_t(int64_t(lc) * p.x_sd + int64_t(i) * p.x_st) * 2 : kOob);
-    const Rsrc wr = make_rsrc(p.w + int64_t(c0) * p.w_sd, (int64_t(nch - 1) * p.w_sd + W) * 2);
-    const Rsrc br = make_rsrc(p.bias ? p.bias + c0 : p.w, p.bias ? int64_t(nch) * 2 : 0);
+    for (int i = 0; i < kUpdGroup; ++i) {
+        const uint16_t v = xp[int64_t(i < g0 ? i : 0) * p.x_st];   // always a valid input
+        xv0[i] = i < g0 ? v : uint16_t(0);
+    }
+    // (plain loads for the taps: the compiler merges a lane's W adjacent
+    // values into one wide load, which a descriptor load would not get)
     float wf[W];
 #pragma unroll
-    for (int k = 0; k < W; ++k) wf[k] = bf_one(buf_ld16(wr, uint32_t(int64_t(lc) * p.w_sd + k) * 2));
+    for (int k = 0; k < W; ++k) wf[k] = bf_one(p.w[int64_t(c) * p.w_sd + k]);
+    const Rsrc br = make_rsrc(p.bias ? p.bias + c0 : p.w, p.bias ? int64_t(nch) * 2 : 0);
     const float b0 = bf_one(buf_ld16(br, lc * 2));
 
     // The entry's line and option values, read together through the scalar
@@ -101,7 +103,6 @@ __global__ __launch_bounds__(kUpdBlock) void update_kernel(UpdParams p, uint32_t
         for (int k = 0; k + 1 < H; ++k) row[int64_t(k) * p.cs_st] = win[k + 1];
     }
 
-    const uint16_t *xp = p.x + int64_t(b) * p.x_sb + int64_t(c) * p.x_sd;
     uint16_t *op = p.out + int64_t(b) * p.o_sb + int64_t(c) * p.o_sd;
     const int32_t ring_from = p.seqlen - L;    // ring: earlier inputs are overwritten anyway
     for (int32_t t0 = 0; t0 < p.seqlen; t0 += kUpdGroup) {
