@@ -877,12 +877,34 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         int64_t st, en;
         bounds(sq, st, en);
         const bool row_cross = !in_b && i0 + n > row_end;
-        const bool plain = n == uint32_t(kVec) && !row_cross && t0 >= st + H && t0 + kVec <= en &&
-                           !skip_of[sq];
+        auto bits = [](int64_t a, int64_t b) {         // elements [a, b) of a chunk, 0 <= a <= b <= 8
+            return ((1u << uint32_t(b)) - 1u) & ~((1u << uint32_t(a)) - 1u);
+        };
+        // The common cases without a loop: a whole chunk inside one row that
+        // starts inside sequence sq and holds at most one more sequence
+        // start.  An element is kept when it is at least H into an unpadded
+        // sequence.  (The next sequence's bounds and pad flag are read with
+        // sq's, in one round of LDS reads.)
         uint32_t keep = 0;                             // bit j: store element j
-        if (plain) {
-            keep = 0xffu;
-        } else {
+        bool done = false;
+        if (n == uint32_t(kVec) && !row_cross && t0 >= st && t0 < en) {
+            const int64_t ea = en - t0 < kVec ? en - t0 : kVec;     // elements of sq: [0, ea)
+            const int64_t ka = st + H - t0 > 0 ? st + H - t0 : 0;    // the first past its head
+            const int32_t s2 = sq + 1 < B ? sq + 1 : sq;
+            int64_t st2, en2;
+            bounds(s2, st2, en2);
+            const bool pad1 = skip_of[sq] != 0, pad2 = skip_of[s2] != 0;
+            if (ka < ea && !pad1) keep = bits(ka, ea);
+            if (ea == kVec) {
+                done = true;
+            } else if (s2 != sq && st2 == en && en2 >= t0 + kVec) {
+                const int64_t kb = st2 + H - t0;                     // > ea
+                if (kb < kVec && !pad2) keep |= bits(kb, kVec);
+                done = true;
+            }
+        }
+        if (!done) {
+            keep = 0;
             // segment by segment (a run of elements of one sequence of one
             // row): keep those at least H into an unpadded sequence
             int64_t row_base = in_b ? int64_t(row_end) : int64_t(row_a);
@@ -934,9 +956,17 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         if (keep == 0xffu) {
             st16_stream(p.out + size_t(i0), o);
         } else {
+            // a pair of kept elements is one 4-byte store, a lone one a
+            // 2-byte store (the chunk is 16-byte aligned)
+            const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
+            uint32_t *o32 = reinterpret_cast<uint32_t *>(p.out + size_t(i0));
 #pragma unroll
-            for (int j = 0; j < kVec; ++j)
-                if (keep & (1u << j)) p.out[size_t(i0) + j] = lane_elem(o, j);
+            for (int d = 0; d < kVec / 2; ++d) {
+                const uint32_t m2 = (keep >> (2 * d)) & 3u;
+                if (m2 == 3u) o32[d] = ov[d];
+                else if (m2 == 1u) p.out[size_t(i0) + 2 * d] = uint16_t(ov[d] & 0xffffu);
+                else if (m2 == 2u) p.out[size_t(i0) + 2 * d + 1] = uint16_t(ov[d] >> 16);
+            }
         }
     }
 }
