@@ -52,7 +52,7 @@ bool chanlast_ok(int64_t sd, int64_t st, int64_t dim, int64_t T) {
 }
 // Token-contiguous storage: a compact (dim, T) array.
 bool tokmajor_ok(int64_t sd, int64_t st, int64_t dim, int64_t T) {
-    return st == 1 && (dim == 1 || sd == T);
+    return (st == 1 || T == 1) && (dim == 1 || sd == T);
 }
 
 // Tokens per channel-contiguous wave tile (measured on gfx950): a single
@@ -145,7 +145,12 @@ int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
     sb.total_T = T;
     const bool silu = activation == SCONV_ACT_SILU;
 
-    if (chanlast_ok(x_stride_dim, x_stride_tok, dim, T) &&
+    // A single token is both layouts at once; the per-row kernel of the
+    // token-contiguous path (one lane per channel) serves it with the
+    // shortest chain of reads.
+    const bool one_token_rows = T == 1 && batch <= 1 && tokmajor_ok(x_stride_dim, x_stride_tok, dim, T) &&
+                                tokmajor_ok(o_stride_dim, o_stride_tok, dim, T);
+    if (!one_token_rows && chanlast_ok(x_stride_dim, x_stride_tok, dim, T) &&
         chanlast_ok(o_stride_dim, o_stride_tok, dim, T)) {
         FwdClParams p;
         p.x = static_cast<const uint16_t *>(x);
