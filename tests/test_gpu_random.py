@@ -1,0 +1,101 @@
+"""Randomised GPU parity sweep: seeded random configurations of every entry
+point, each compared with the oracle -- exact-valued inputs (k/8) bit for
+bit without activation, and within the tolerance with SiLU.
+
+The configurations mix what the fixed cases cover one at a time: batch
+sizes, zero-length and very short sequences, pads, missing state / bias /
+has_initial_state / cache_indices, widths 2..5, ragged channel counts, both
+storages, and, for the single-sequence kernels, every row-length regime
+(per-row, short-row and long-row kernels)."""
+import pytest
+import torch
+
+import causal_depthwise_short_conv1d_amd as S
+import oracle
+import workloads as W
+from tests.parity import assert_bits, assert_close, say
+from tests.test_gpu_fwd import check_full, to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+BF = torch.bfloat16
+
+
+def place_x(g, x, layout):
+    """x (dim, T) on the device in the given storage; channel-contiguous rows
+    get a pitch rounded up to 8 elements (16-byte aligned rows)."""
+    dim, T = x.shape
+    if layout == "tok_dim":
+        pitch = (dim + 7) // 8 * 8
+        buf = torch.zeros(T, pitch, dtype=BF, device=DEV)
+        buf[:, :dim] = x.t().to(DEV)
+        g["x"] = buf[:, :dim].t()
+    else:
+        g["x"] = x.contiguous().to(DEV)
+    return g
+
+
+@pytest.mark.parametrize("case", range(48))
+def test_random_varlen_forward(case):
+    r = torch.Generator().manual_seed(5000 + case)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=r))
+    width = ri(2, 5)
+    layout = ("dim_tok", "tok_dim")[case % 2]
+    single = case % 3 == 0
+    if single:
+        # one sequence: per-row (T < 16), short-row (16..2047) and long-row
+        # (>= 2048) regimes of the token-contiguous path
+        T = (ri(1, 15), ri(16, 2047), ri(2048, 5000))[case % 9 // 3]
+        lens = [T]
+        dim = ri(1, 96)
+    else:
+        nseq = ri(2, 40)
+        lens = [ri(0, 3) if ri(0, 3) == 0 else ri(0, 300) for _ in range(nseq)]
+        if case % 4 == 1:
+            lens.append(ri(2048, 3000))          # rows long enough for the streaming varlen kernel
+        dim = ri(1, 80)
+    n_pad = 0 if len(lens) < 3 else ri(0, 2)
+    d = W.varlen_batch(lengths=lens, dim=dim, width=width, seed=6000 + case,
+                       num_lines=len(lens) + ri(0, 4), n_pad=n_pad, layout="dim_tok",
+                       values="exact", with_bias=ri(0, 1) == 1)
+    if ri(0, 4) == 0:
+        d["has_initial_state"] = None
+    if ri(0, 5) == 0:
+        d["conv_states"] = None
+        d["has_initial_state"] = None
+    elif ri(0, 5) == 0 and n_pad == 0:
+        d["cache_indices"] = None
+        d["conv_states"] = d["conv_states"][:len(lens)].contiguous()
+    x = d.pop("x")
+    g = place_x(to_dev(d), x, layout)
+    label = f"random fwd {case}: {layout} dim {dim} W{width} lens {lens[:6]}{'...' if len(lens) > 6 else ''}"
+    check_full(g, activation=None, exact=True, label=label)
+    check_full(g, activation="silu", label=label + " silu")
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_update(case):
+    """Plain decode update: random batch, channel count, token count, width,
+    pads and bias, bit for bit with exact values."""
+    r = torch.Generator().manual_seed(7000 + case)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=r))
+    width = ri(2, 5)
+    batch, dim, seqlen = ri(1, 12), ri(1, 700), ri(1, 6)
+    n_pad = ri(0, 2) if batch > 2 else 0
+    d = W.decode_batch(batch=batch, dim=dim, width=width, seqlen=seqlen, seed=7100 + case,
+                       num_lines=batch + ri(0, 3), n_pad=n_pad, values="exact",
+                       with_bias=ri(0, 1) == 1)
+    x, ci = d["x"], d["cache_indices"]
+    st_ref = d["conv_state"].clone()
+    out_ref = torch.full(x.shape, -5.0, dtype=BF)
+    oracle.update_decode(x, st_ref, d["weight"], d["bias"], out_ref, cache_indices=ci,
+                         activation=None)
+    st_gpu = d["conv_state"].to(DEV)
+    out = torch.full(x.shape, -5.0, dtype=BF, device=DEV)
+    S.conv1d_update(x.to(DEV), st_gpu, d["weight"].to(DEV),
+                    None if d["bias"] is None else d["bias"].to(DEV), activation=None,
+                    cache_indices=ci.to(DEV), out=out)
+    torch.cuda.synchronize()
+    say(f"[update] random {case}: batch {batch} dim {dim} seqlen {seqlen} W{width} pads {n_pad}")
+    assert_bits(out, out_ref, f"random update {case} out")
+    assert_bits(st_gpu, st_ref, f"random update {case} state")
