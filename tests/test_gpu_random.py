@@ -5,7 +5,8 @@ bit without activation, and within the tolerance with SiLU.
 The configurations mix what the fixed cases cover one at a time: batch
 sizes, zero-length and very short sequences, pads, missing state / bias /
 has_initial_state / cache_indices, widths 2..5, ragged channel counts, both
-storages, and, for the single-sequence kernels, every row-length regime
+storages, paged block sizes, stream offsets and request mixes, and, for
+the single-sequence kernels, every row-length regime
 (per-row, short-row and long-row kernels)."""
 import pytest
 import torch
@@ -99,3 +100,31 @@ def test_random_update(case):
     say(f"[update] random {case}: batch {batch} dim {dim} seqlen {seqlen} W{width} pads {n_pad}")
     assert_bits(out, out_ref, f"random update {case} out")
     assert_bits(st_gpu, st_ref, f"random update {case} state")
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_paged(case):
+    """Paged insert + conv: random heads, stream width and offset, block
+    size, head dim, request mix (decode tokens, prefill chunks), pads, bias,
+    residual and width, bit for bit with exact values and no activation."""
+    from tests.test_gpu_paged import run_both
+    r = torch.Generator().manual_seed(8000 + case)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=r))
+    width = ri(2, 5)
+    H = ri(1, 12)
+    ws = 8 * ri(1, 6)
+    D = ws + 8 * ri(0, 4)
+    off_s = 8 * ri(0, (D - ws) // 8)
+    N = (1, 2, 4, 8, 16)[ri(0, 4)]
+    n_decode, n_prefill, chunk = ri(0, 12), ri(0, 4), ri(1, 70)
+    if n_decode + n_prefill == 0:
+        n_decode = 1
+    max_pos = ri(chunk + width, 400)
+    blocks_needed = n_decode * (width // N + 2) + n_prefill * ((chunk + width) // N + 2)
+    d = W.paged_batch(H=H, ws=ws, N=N, D=D, off_s=off_s, num_blocks=blocks_needed + ri(1, 20),
+                      width=width, n_decode=n_decode, n_prefill=n_prefill, chunk=chunk,
+                      max_pos=max_pos, pad_frac=0.1 * ri(0, 2), trailing_pad=ri(0, 3),
+                      seed=8100 + case, values="exact", with_bias=ri(0, 1) == 1, min_pos=0)
+    run_both(d, activation=None, residual=ri(0, 1) == 1, exact=True,
+             label=f"random paged {case}: H{H} ws{ws} D{D} off{off_s} N{N} W{width} "
+                   f"dec {n_decode} pre {n_prefill}x{chunk}")
