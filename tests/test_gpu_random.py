@@ -128,3 +128,77 @@ def test_random_paged(case):
     run_both(d, activation=None, residual=ri(0, 1) == 1, exact=True,
              label=f"random paged {case}: H{H} ws{ws} D{D} off{off_s} N{N} W{width} "
                    f"dec {n_decode} pre {n_prefill}x{chunk}")
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_spec_and_ring(case):
+    """conv1d_update with the speculative options (state roll, or saved
+    windows and lines in either subset) or ring-buffer states: random batch,
+    channel count, token count, width, state length, pads, bias and state
+    storage, bit for bit with exact values, and with SiLU within the
+    tolerance."""
+    from tests.test_gpu_update import both
+    r = torch.Generator().manual_seed(9000 + case)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=r))
+    width = ri(2, 5)
+    batch, dim, seqlen = ri(1, 12), ri(1, 700), ri(1, 6)
+    n_pad = ri(0, 2) if batch > 2 else 0
+    kind = ("roll", "scatter", "ring")[case % 3]
+    bias = ri(0, 1) == 1
+    if kind == "ring":
+        d = W.ring_decode_batch(batch=batch, dim=dim, width=width, seqlen=seqlen,
+                                state_len=width - 1 + ri(0, 6), num_lines=batch + ri(0, 4),
+                                n_pad=n_pad, max_seen=ri(0, 40), seed=9100 + case,
+                                values="exact", with_bias=bias)
+        use = ("cache_seqlens",)
+    else:
+        layout = ("dim_contig", "tok_contig")[ri(0, 1)]
+        extra = ri(0, 3)
+        state_len = (width - 2 + seqlen if kind == "roll" else width - 1) + extra
+        lines = batch * (seqlen + 1) + ri(0, 5) if kind == "scatter" else batch + ri(0, 4)
+        d = W.spec_decode_batch(batch=batch, dim=dim, width=width, seqlen=seqlen,
+                                state_len=state_len, num_lines=lines, n_pad=n_pad, mode=kind,
+                                seed=9100 + case, values="exact", with_bias=bias,
+                                state_layout=layout)
+        use = ("num_accepted_tokens",) + (
+            (("intermediate", "output_state_indices"), ("intermediate",),
+             ("output_state_indices",))[ri(0, 2)] if kind == "scatter" else ())
+    say(f"[update] random {kind} {case}: batch {batch} dim {dim} seqlen {seqlen} W{width} "
+        f"state_len {d['conv_state'].shape[2]} pads {n_pad} use {use}")
+    both(d, activation=None, exact=True, use=use)
+    both(d, activation="silu", use=use)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_paged_multi(case):
+    """Several streams in one sconv_paged_fused_multi launch: random stream
+    count, order and spacing of the D sub-ranges, block size, request mix,
+    pads, bias, residual and width, bit for bit with exact values."""
+    from tests.test_gpu_paged import run_multi
+    r = torch.Generator().manual_seed(9500 + case)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=r))
+    width = ri(2, 5)
+    k = ri(2, 4)
+    ws = 8 * ri(1, 4)
+    gaps = [8 * ri(0, 2) for _ in range(k)]
+    starts, at = [], 0
+    for gp in gaps:
+        starts.append(at + gp)
+        at += gp + ws
+    D = at + 8 * ri(0, 2)
+    order = torch.randperm(k, generator=r).tolist()
+    offsets = tuple(starts[i] for i in order)
+    N = (1, 2, 4, 8, 16)[ri(0, 4)]
+    n_decode, n_prefill, chunk = ri(0, 10), ri(0, 3), ri(1, 60)
+    if n_decode + n_prefill == 0:
+        n_prefill = 1
+    blocks_needed = n_decode * (width // N + 2) + n_prefill * ((chunk + width) // N + 2)
+    d = W.paged_multi_batch(offsets=offsets, seed=9600 + case, values="exact",
+                            with_bias=ri(0, 1) == 1, H=ri(1, 6), ws=ws, N=N, D=D,
+                            num_blocks=blocks_needed + ri(1, 10), width=width,
+                            n_decode=n_decode, n_prefill=n_prefill, chunk=chunk,
+                            max_pos=ri(chunk + width, 300), pad_frac=0.1 * ri(0, 2),
+                            trailing_pad=ri(0, 2), min_pos=0)
+    run_multi(d, activation=None, residual=ri(0, 1) == 1, exact=True,
+              label=f"random multi {case}: offs {offsets} ws{ws} D{D} N{N} W{width} "
+                    f"dec {n_decode} pre {n_prefill}x{chunk}")
