@@ -357,8 +357,6 @@ def varlen_state_property(d, g_cs, width):
 @pytest.mark.parametrize("width", W.VARLEN_BATCH["widths"])
 @pytest.mark.parametrize("layout", ["tok_dim", "dim_tok"])
 def test_varlen_batch(width, layout):
-    if layout == "dim_tok" and width != 4:
-        pytest.skip("token-contiguous varlen run at width 4 only")
     d = W.varlen_batch(dim=8192, width=width, seed=W.seed_for(4, width), layout=layout,
                        device=DEV)
     total = int(d["query_start_loc"][-1])
