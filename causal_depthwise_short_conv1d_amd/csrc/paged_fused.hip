@@ -178,8 +178,9 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     const int32_t r = seq_search(qsl, p.num_reqs, tok ? tl : tile_start);
     const int64_t qs_r = qsl[r];
     const int64_t m_qs = m_pad ? 0 : qs_r;
-    int32_t m_tblk[H], m_tn[H], bt_v[H];
+    int32_t m_tblk[H], m_tn[H], lb_v[H];
     bool need[H];
+    bool any = false;
 #pragma unroll
     for (int j = 0; j < H; ++j) {
         const int64_t src = pos - H + j;
@@ -187,15 +188,24 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
         const bool live = !m_pad && src >= 0;
         const bool intra = live && row >= qs_r;
         need[j] = live && !intra && src < p.src_lim;
+        any = any || need[j];
         const uint32_t c32 = need[j] ? uint32_t(src) : 0u;
         const uint32_t lb = p.div_n.div(c32);
+        lb_v[j] = int32_t(lb);
         m_tn[j] = int32_t(c32 - lb * uint32_t(p.block_size));
-        bt_v[j] = *(need[j] ? p.bt + (int64_t(r) * p.bt_sr + lb) : p.bt_rd);
         m_tblk[j] = intra ? kTapIntra : kTapZero;
     }
+    // Most tiles of a prefill chunk take every tap from x: their waves skip
+    // the block-table round trip (a wave-uniform branch).
+    if (__builtin_amdgcn_ballot_w64(any) != 0) {
+        asm volatile("");                                   // keeps this a branch
+        int32_t bt_v[H];
 #pragma unroll
-    for (int j = 0; j < H; ++j)
-        if (need[j] && bt_v[j] >= 0 && bt_v[j] < p.num_blocks) m_tblk[j] = bt_v[j];
+        for (int j = 0; j < H; ++j) bt_v[j] = *(need[j] ? p.bt + (int64_t(r) * p.bt_sr + lb_v[j]) : p.bt_rd);
+#pragma unroll
+        for (int j = 0; j < H; ++j)
+            if (need[j] && bt_v[j] >= 0 && bt_v[j] < p.num_blocks) m_tblk[j] = bt_v[j];
+    }
 
     const __amdgpu_buffer_rsrc_t orr =
         rsrc(st.out + tile_start * st.o_st, (p.T - tile_start - 1) * st.o_st * 2 + int64_t(st.C) * 2);
