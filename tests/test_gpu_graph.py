@@ -67,6 +67,21 @@ class Step:
                           n_prefill=3, chunk=37, max_pos=60, width=4, pad_frac=0.1, seed=703)
         self.p = {k: (t.to(DEV) if isinstance(t, torch.Tensor) else t) for k, t in p.items()}
         self.p_out = torch.empty_like(self.p["x"])
+        m = W.paged_multi_batch(offsets=(16, 0), H=3, ws=16, N=4, D=40, num_blocks=96,
+                                n_decode=4, n_prefill=2, chunk=23, max_pos=60, width=3,
+                                pad_frac=0.1, seed=704, with_bias=True)
+        self.m = {k: (t.to(DEV) if isinstance(t, torch.Tensor) else t) for k, t in m.items()}
+        for k in ("xs", "weights", "biases"):
+            self.m[k] = [t.to(DEV) for t in m[k]]
+        self.m_outs = [torch.empty_like(x) for x in self.m["xs"]]
+        r = W.ring_decode_batch(batch=5, dim=200, width=4, seqlen=2, state_len=6, num_lines=8,
+                                n_pad=1, seed=705)
+        self.r = {k: (t.to(DEV) if isinstance(t, torch.Tensor) else t) for k, t in r.items()}
+        self.r_out = torch.empty_like(self.r["x"])
+        c = W.varlen_batch(lengths=[40, 3, 0, 129], dim=264, width=5, seed=706, num_lines=6,
+                           n_pad=1, layout="tok_dim")
+        self.c = {k: (t.to(DEV) if isinstance(t, torch.Tensor) else t) for k, t in c.items()}
+        self.c_out = S.new_output(self.c["x"])
         qsl = self.p["query_start_loc"]
         self.n_req = qsl.numel() - 1
         self.n_tok = self.p["x"].shape[0]
@@ -76,15 +91,19 @@ class Step:
 
     def mutable(self):
         return [self.v["conv_states"], self.d["conv_state"], self.s["conv_state"],
-                self.s["intermediate"], self.p["cache"]]
+                self.s["intermediate"], self.p["cache"], self.m["cache"], self.r["conv_state"],
+                self.c["conv_states"]]
+
+    def bf_outputs(self):
+        return [self.v_out, self.d_out, self.s_out, self.p_out, self.r_out, self.c_out] + self.m_outs
 
     def outputs(self):
-        return [self.v_out, self.d_out, self.s_out, self.p_out, self.si, self.qs] + self.mutable()
+        return self.bf_outputs() + [self.si, self.qs] + self.mutable()
 
     def reset(self):
         for t, p in zip(self.mutable(), self.pristine):
             t.copy_(p)
-        for t in (self.v_out, self.d_out, self.s_out, self.p_out):
+        for t in self.bf_outputs():
             t.fill_(-5.0)
         self.si.fill_(-1)
         self.qs.fill_(-1)
@@ -108,6 +127,18 @@ class Step:
                             activation="silu", use_residual=True, out=self.p_out)
         S.sconv_seq_metadata(p["query_start_loc"], self.n_req, self.n_tok, self.si, self.qs,
                              num_padded_tokens=self.n_tok + 2)
+        m, r, c = self.m, self.r, self.c
+        S.sconv_paged_fused_multi(m["xs"], m["weights"], m["cache"], m["positions"],
+                                  m["slot_mapping"], m["query_start_loc"], m["block_table"],
+                                  m["offs"], m["ws"], activation="silu", use_residual=True,
+                                  biases=m["biases"], outs=self.m_outs)
+        S.conv1d_update(r["x"], r["conv_state"], r["weight"], r["bias"], activation="silu",
+                        cache_indices=r["cache_indices"], cache_seqlens=r["cache_seqlens"],
+                        out=self.r_out)
+        S.conv1d_fwd_varlen(c["x"], c["weight"], c["bias"], c["conv_states"],
+                            c["query_start_loc"], cache_indices=c["cache_indices"],
+                            has_initial_state=c["has_initial_state"], activation="silu",
+                            out=self.c_out)
 
 
 def test_graph_capture_replays_every_entry_point():
