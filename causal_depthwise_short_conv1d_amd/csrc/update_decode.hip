@@ -158,8 +158,171 @@ __global__ __launch_bounds__(kUpdBlock) void update_kernel(UpdParams p, uint32_t
     }
 }
 
+// The same update with four adjacent channels per lane, for x, out, the
+// state lines and the saved windows all unit-stride along dim (the layout a
+// verify step keeps its states in).  Every access is then one 8-byte vector
+// instead of four 2-byte ones: at one lane per channel the address unit,
+// not the bytes, bounds a launch of this size.  The arithmetic and the
+// order of every read and write per channel are those of update_kernel.
+constexpr int kVecCh = 4;
+
+__device__ __forceinline__ u32x2 ld4ch(const uint16_t *p) { return *reinterpret_cast<const u32x2 *>(p); }
+__device__ __forceinline__ void st4ch(uint16_t *p, const u32x2 &v) { *reinterpret_cast<u32x2 *>(p) = v; }
+__device__ __forceinline__ float ch_of(const u32x2 &v, int ch) {
+    const uint32_t d = (ch >> 1) ? v.y : v.x;
+    return (ch & 1) ? bf_hi(d) : bf_lo(d);
+}
+
+template <int W, bool SILU>
+__global__ __launch_bounds__(kUpdBlock) void update_vec_kernel(UpdParams p, uint32_t cblocks) {
+    constexpr int H = W - 1;
+    const uint32_t b = blockIdx.x / cblocks;            // the entry (workgroup-uniform)
+    const int32_t c = int32_t(((blockIdx.x % cblocks) * kUpdBlock + threadIdx.x) * kVecCh);
+    if (int32_t(b) >= p.batch || c >= p.dim) return;
+
+    const int32_t g0 = p.seqlen < kUpdGroup ? p.seqlen : kUpdGroup;
+    const uint16_t *xp = p.x + int64_t(b) * p.x_sb + c;
+    u32x2 xv0[kUpdGroup];
+#pragma unroll
+    for (int i = 0; i < kUpdGroup; ++i) {
+        const u32x2 v = ld4ch(xp + int64_t(i < g0 ? i : 0) * p.x_st);   // always a valid input
+        xv0[i] = i < g0 ? v : u32x2{0u, 0u};
+    }
+    float wf[kVecCh][W];
+#pragma unroll
+    for (int ch = 0; ch < kVecCh; ++ch)
+#pragma unroll
+        for (int k = 0; k < W; ++k) wf[ch][k] = bf_one(p.w[int64_t(c + ch) * p.w_sd + k]);
+    // without a bias the first input stands in and is discarded
+    const u32x2 bv = ld4ch(p.bias ? p.bias + c : xp);
+    float b0[kVecCh];
+#pragma unroll
+    for (int ch = 0; ch < kVecCh; ++ch) b0[ch] = p.bias ? ch_of(bv, ch) : 0.0f;
+
+    const void *sx = reinterpret_cast<const void *>(reinterpret_cast<uintptr_t>(p.x) & ~uintptr_t(3));
+    const int32_t ci = int32_t(sld_u32(p.cache_idx ? static_cast<const void *>(p.cache_idx + b) : sx));
+    const int32_t na = int32_t(sld_u32(p.num_acc ? static_cast<const void *>(p.num_acc + b) : sx));
+    const int32_t seen = int32_t(sld_u32(p.ring_seen ? static_cast<const void *>(p.ring_seen + b) : sx));
+    const int64_t line = p.cache_idx ? int64_t(ci) : int64_t(b);
+    if ((p.cache_idx && line == p.pad_slot_id) || line < 0 || line >= p.num_lines) return;
+
+    const int32_t L = p.state_len;
+    int32_t off = 0;
+    int32_t rcol = 0;
+    if (p.num_acc) {
+        off = na - 1;
+        if (off < 0 || off > L - H) return;
+    }
+    if (p.ring_seen) {
+        if (seen < 0) return;
+        rcol = seen % L;
+    }
+    const bool spec = p.num_acc != nullptr;
+    const bool ring = p.ring_seen != nullptr;
+    const bool saved = p.inter != nullptr || p.out_idx != nullptr;
+
+    uint16_t *row = p.cs + line * p.cs_sl + c;
+    u32x2 win[H];
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+        int32_t col = off + k;
+        if (ring) {
+            col = rcol - H + k;
+            if (col < 0) col += L;
+        }
+        win[k] = ld4ch(row + int64_t(col) * p.cs_st);
+    }
+    if (spec && !saved) {
+#pragma unroll
+        for (int k = 0; k + 1 < H; ++k) st4ch(row + int64_t(k) * p.cs_st, win[k + 1]);
+    }
+
+    uint16_t *op = p.out + int64_t(b) * p.o_sb + c;
+    const int32_t ring_from = p.seqlen - L;
+    for (int32_t t0 = 0; t0 < p.seqlen; t0 += kUpdGroup) {
+        u32x2 xv[kUpdGroup];
+        if (t0 == 0) {
+#pragma unroll
+            for (int i = 0; i < kUpdGroup; ++i) xv[i] = xv0[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < kUpdGroup; ++i)
+                xv[i] = t0 + i < p.seqlen ? ld4ch(xp + int64_t(t0 + i) * p.x_st) : u32x2{0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < kUpdGroup; ++i) {
+            const int32_t t = t0 + i;
+            if (t >= p.seqlen) break;
+            float o[kVecCh];
+#pragma unroll
+            for (int ch = 0; ch < kVecCh; ++ch) {
+                float acc = b0[ch];
+#pragma unroll
+                for (int k = 0; k < H; ++k) acc = __builtin_fmaf(wf[ch][k], ch_of(win[k], ch), acc);
+                acc = __builtin_fmaf(wf[ch][H], ch_of(xv[i], ch), acc);
+                o[ch] = act<SILU>(acc);
+            }
+            st4ch(op + int64_t(t) * p.o_st, u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
+#pragma unroll
+            for (int k = 0; k + 1 < H; ++k) win[k] = win[k + 1];
+            win[H - 1] = xv[i];
+
+            if (p.inter) {
+                uint16_t *ip = p.inter + int64_t(b) * p.i_sb + int64_t(t) * p.i_st + c;
+#pragma unroll
+                for (int k = 0; k < H; ++k) st4ch(ip + int64_t(k) * p.i_sk, win[k]);
+            }
+            if (p.out_idx) {
+                const int64_t dst = p.out_idx[int64_t(b) * p.oi_sb + int64_t(t) * p.oi_st];
+                if (dst >= 0 && dst < p.num_lines) {
+                    uint16_t *dp = p.cs + dst * p.cs_sl + c;
+#pragma unroll
+                    for (int k = 0; k < H; ++k) st4ch(dp + int64_t(k) * p.cs_st, win[k]);
+                }
+            }
+            if (!saved) {
+                if (ring) {
+                    if (t >= ring_from) st4ch(row + int64_t(rcol) * p.cs_st, xv[i]);
+                    rcol = rcol + 1 == L ? 0 : rcol + 1;
+                } else if (spec) {
+                    st4ch(row + int64_t(H - 1 + t) * p.cs_st, xv[i]);
+                }
+            }
+        }
+    }
+    if (!saved && !ring && !spec) {
+#pragma unroll
+        for (int k = 0; k < H; ++k) st4ch(row + int64_t(k) * p.cs_st, win[k]);
+    }
+}
+
+// Whether every tensor the update touches holds four adjacent channels as
+// one aligned 8-byte vector.
+bool vec_layout(const UpdParams &p) {
+    auto al = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 7) == 0; };
+    auto m4 = [](int64_t v) { return (v & 3) == 0; };
+    if (p.dim % kVecCh != 0 || p.x_sd != 1 || p.o_sd != 1 || p.cs_sd != 1) return false;
+    if (!al(p.x) || !al(p.out) || !al(p.cs) || (p.bias && !al(p.bias))) return false;
+    const bool one = p.seqlen == 1;                     // token strides unused
+    if (!m4(p.x_sb) || !m4(p.o_sb) || !m4(p.cs_sl) || !m4(p.cs_st) ||
+        !(one || (m4(p.x_st) && m4(p.o_st))))
+        return false;
+    if (p.inter && (p.i_sd != 1 || !al(p.inter) || !m4(p.i_sb) || !(one || m4(p.i_st)) ||
+                    !m4(p.i_sk)))
+        return false;
+    return true;
+}
+
 template <int W>
 hipError_t launch_w(const UpdParams &p, bool silu, hipStream_t s) {
+    if (vec_layout(p)) {
+        const int32_t lanes = p.dim / kVecCh;
+        const uint32_t cblocks = uint32_t((lanes + kUpdBlock - 1) / kUpdBlock);
+        const dim3 grid(cblocks * uint32_t(p.batch)), block(kUpdBlock);
+        if (silu) update_vec_kernel<W, true><<<grid, block, 0, s>>>(p, cblocks);
+        else update_vec_kernel<W, false><<<grid, block, 0, s>>>(p, cblocks);
+        return hipGetLastError();
+    }
     const uint32_t cblocks = uint32_t((p.dim + kUpdBlock - 1) / kUpdBlock);
     const dim3 grid(cblocks * uint32_t(p.batch)), block(kUpdBlock);
     if (silu) update_kernel<W, true><<<grid, block, 0, s>>>(p, cblocks);

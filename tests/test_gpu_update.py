@@ -20,28 +20,42 @@ def gpu(t):
     return None if t is None else t.to(DEV)
 
 
-def both(d, activation="silu", exact=False, in_place=False, use=OPTS + ("intermediate",)):
+def windows(shape, device, dim_contig):
+    """Saved-window buffer (batch, steps, dim, width-1) filled with 2.5,
+    stored with unit stride along dim when dim_contig."""
+    if not dim_contig:
+        return torch.full(shape, 2.5, dtype=BF, device=device)
+    b, n, dim, h = shape
+    return torch.full((b, n, h, dim), 2.5, dtype=BF, device=device).permute(0, 1, 3, 2)
+
+
+def both(d, activation="silu", exact=False, in_place=False, use=OPTS + ("intermediate",),
+         windows_dim_contig=False, out_like_x=False):
     """Run the oracle and the library on the same inputs with the options of
     `d` named in `use`; compare out (tolerance, or bits when exact), the whole
-    state cache and the intermediate windows (bits)."""
+    state cache and the intermediate windows (bits).  The GPU's out is
+    contiguous, or laid out like x when out_like_x."""
     opts = {k: d[k] for k in OPTS if k in use and d.get(k) is not None}
     inter0 = d.get("intermediate") if "intermediate" in use else None
     x_cpu = d["x"]
     st_ref = d["conv_state"].clone()
     out_ref = torch.full(x_cpu.shape, -3.0, dtype=BF)
-    inter_ref = None if inter0 is None else torch.full(inter0.shape, 2.5, dtype=BF)
+    inter_ref = None if inter0 is None else windows(inter0.shape, "cpu", windows_dim_contig)
     oracle.update_general(x_cpu, st_ref, d["weight"], d["bias"], out_ref,
                           cache_indices=d["cache_indices"], intermediate=inter_ref,
                           activation=activation, **opts)
     x = x_cpu.to(DEV)
     st = d["conv_state"].to(DEV)       # keeps the strides of the CPU tensor
     assert st.stride() == d["conv_state"].stride()
-    inter = None if inter0 is None else torch.full(inter0.shape, 2.5, dtype=BF, device=DEV)
+    inter = None if inter0 is None else windows(inter0.shape, DEV, windows_dim_contig)
     if in_place:
         out = x
         for bi, line in enumerate(d["cache_indices"].tolist()):
             if out_ref[bi].eq(-3.0).all():      # skipped entry keeps x
                 out_ref[bi] = x_cpu[bi]
+    elif out_like_x:
+        out = torch.full_like(x, -3.0)
+        assert out.stride() == x.stride()
     else:
         out = torch.full(x.shape, -3.0, dtype=BF, device=DEV)
     S.conv1d_update(x, st, gpu(d["weight"]), gpu(d["bias"]), activation=activation,
@@ -183,6 +197,48 @@ def test_ring_exact_values_bit_exact():
     d = W.ring_decode_batch(batch=7, dim=100, width=3, seqlen=5, state_len=4, num_lines=9,
                             seed=571, values="exact")
     both(d, activation=None, exact=True)
+
+
+# ------------------------------------------------- channel-contiguous --
+# x, out, the state lines and the saved windows all with unit stride along
+# dim and dim % 4 == 0: the kernel then moves four channels per lane.  Two
+# workgroups of channels (the second partial), one and six tokens (two
+# groups of inputs), every mode.
+
+MODES = ("plain", "roll", "roll_in_place", "scatter_windows", "scatter_lines", "ring")
+
+
+def channel_contiguous_batch(mode, width, seqlen, values):
+    seed = 590 + 10 * width + seqlen + MODES.index(mode) * 100
+    dim, batch = 1156, 7
+    if mode == "ring":
+        return W.ring_decode_batch(batch=batch, dim=dim, width=width, seqlen=seqlen,
+                                   state_len=width + 2, num_lines=10, n_pad=1, seed=seed,
+                                   values=values, state_layout="dim_contig")
+    kind = "scatter" if mode.startswith("scatter") else "roll"
+    lines = batch * (seqlen + 1) + 3 if kind == "scatter" else 10
+    return W.spec_decode_batch(batch=batch, dim=dim, width=width, seqlen=seqlen,
+                               state_len=width - 2 + seqlen + 1 if kind == "roll" else width,
+                               num_lines=lines, n_pad=1, seed=seed, mode=kind, values=values,
+                               state_layout="dim_contig")
+
+
+@pytest.mark.parametrize("seqlen", [1, 6])
+@pytest.mark.parametrize("width", [2, 3, 4, 5])
+@pytest.mark.parametrize("mode", MODES)
+def test_channel_contiguous_layouts(mode, width, seqlen):
+    use = {"plain": (), "roll": ("num_accepted_tokens",),
+           "roll_in_place": ("num_accepted_tokens",),
+           "scatter_windows": ("num_accepted_tokens", "intermediate", "output_state_indices"),
+           "scatter_lines": ("num_accepted_tokens", "output_state_indices"),
+           "ring": ("cache_seqlens",)}[mode]
+    kw = dict(use=use, in_place=mode == "roll_in_place",
+              windows_dim_contig=mode == "scatter_windows", out_like_x=True)
+    d = channel_contiguous_batch(mode, width, seqlen, "exact")
+    assert d["x"].stride(1) == 1 and d["conv_state"].stride(1) == 1
+    both(d, activation=None, exact=True, **kw)
+    d = channel_contiguous_batch(mode, width, seqlen, "normal")
+    both(d, activation="silu", **kw)
 
 
 # ------------------------------------------------------------ plain mode --

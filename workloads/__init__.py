@@ -222,11 +222,13 @@ def ring_decode_batch(batch: int = 64, dim: int = 8192, width: int = 4,
                       seqlen: int = 1, state_len: int = 8, seed: int = 0,
                       num_lines: int = 256, n_pad: int = 0, max_seen: int = 64,
                       device="cpu", values: str = "normal",
-                      with_bias: bool = True) -> dict:
+                      with_bias: bool = True, state_layout: str = "tok_contig") -> dict:
     """A decode step on ring-buffer states (the cache_seqlens option of
     tokenspeed causal_conv1d_update's docstring): each line holds state_len
     inputs, input n of a stream at column n mod state_len, and
-    cache_seqlens counts the inputs seen so far (uniform in [0, max_seen])."""
+    cache_seqlens counts the inputs seen so far (uniform in [0, max_seen]).
+    The state is stored token-contiguous by default, or with unit stride
+    along dim ("dim_contig")."""
     g_host = _gen(seed, "cpu")
     lines = torch.randperm(num_lines, generator=g_host)[:batch].to(torch.int32)
     if n_pad:
@@ -236,7 +238,12 @@ def ring_decode_batch(batch: int = 64, dim: int = 8192, width: int = 4,
     x = _draw((batch, seqlen, dim), g, device, values).permute(0, 2, 1)
     weight = _draw((dim, width), g, device, values)
     bias = _draw((dim,), g, device, values) if with_bias else None
-    state = _draw((num_lines, dim, state_len), g, device, values)
+    if state_layout == "tok_contig":
+        state = _draw((num_lines, dim, state_len), g, device, values)
+    elif state_layout == "dim_contig":
+        state = _draw((num_lines, state_len, dim), g, device, values).permute(0, 2, 1)
+    else:
+        raise ValueError(f"unknown state layout {state_layout!r}")
     return dict(x=x, weight=weight, bias=bias, conv_state=state,
                 cache_indices=lines.to(device), cache_seqlens=seen.to(device),
                 state_len=state_len)
