@@ -134,25 +134,28 @@ def test_random_paged(case):
 def test_random_spec_and_ring(case):
     """conv1d_update with the speculative options (state roll, or saved
     windows and lines in either subset) or ring-buffer states: random batch,
-    channel count, token count, width, state length, pads, bias and state
-    storage, bit for bit with exact values, and with SiLU within the
-    tolerance."""
+    channel count, token count, width, state length, pads, bias, and the
+    storage of the states, the windows and out (channel-contiguous storage
+    with whole four-channel groups takes the four-channel kernel), bit for
+    bit with exact values, and with SiLU within the tolerance."""
     from tests.test_gpu_update import both
     r = torch.Generator().manual_seed(9000 + case)
     ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=r))
     width = ri(2, 5)
     batch, dim, seqlen = ri(1, 12), ri(1, 700), ri(1, 6)
+    if case % 2 == 0:
+        dim = 4 * ri(1, 400)              # whole four-channel groups
     n_pad = ri(0, 2) if batch > 2 else 0
     kind = ("roll", "scatter", "ring")[case % 3]
     bias = ri(0, 1) == 1
+    layout = ("dim_contig", "tok_contig")[ri(0, 1)]
     if kind == "ring":
         d = W.ring_decode_batch(batch=batch, dim=dim, width=width, seqlen=seqlen,
                                 state_len=width - 1 + ri(0, 6), num_lines=batch + ri(0, 4),
                                 n_pad=n_pad, max_seen=ri(0, 40), seed=9100 + case,
-                                values="exact", with_bias=bias)
+                                values="exact", with_bias=bias, state_layout=layout)
         use = ("cache_seqlens",)
     else:
-        layout = ("dim_contig", "tok_contig")[ri(0, 1)]
         extra = ri(0, 3)
         state_len = (width - 2 + seqlen if kind == "roll" else width - 1) + extra
         lines = batch * (seqlen + 1) + ri(0, 5) if kind == "scatter" else batch + ri(0, 4)
@@ -163,10 +166,11 @@ def test_random_spec_and_ring(case):
         use = ("num_accepted_tokens",) + (
             (("intermediate", "output_state_indices"), ("intermediate",),
              ("output_state_indices",))[ri(0, 2)] if kind == "scatter" else ())
+    kw = dict(use=use, out_like_x=ri(0, 1) == 1, windows_dim_contig=ri(0, 1) == 1)
     say(f"[update] random {kind} {case}: batch {batch} dim {dim} seqlen {seqlen} W{width} "
-        f"state_len {d['conv_state'].shape[2]} pads {n_pad} use {use}")
-    both(d, activation=None, exact=True, use=use)
-    both(d, activation="silu", use=use)
+        f"state_len {d['conv_state'].shape[2]} {layout} pads {n_pad} {kw}")
+    both(d, activation=None, exact=True, **kw)
+    both(d, activation="silu", **kw)
 
 
 @pytest.mark.parametrize("case", range(12))
