@@ -173,7 +173,10 @@ __device__ __forceinline__ float ch_of(const u32x2 &v, int ch) {
     return (ch & 1) ? bf_hi(d) : bf_lo(d);
 }
 
-template <int W, bool SILU>
+// WIDE: the weights are packed (row pitch W) and 16-byte aligned, so a lane's
+// four channels' taps are 4W adjacent values, read as W/2 16-byte vectors
+// (W even) or W 8-byte vectors (W odd).
+template <int W, bool SILU, bool WIDE>
 __global__ __launch_bounds__(kUpdBlock) void update_vec_kernel(UpdParams p, uint32_t cblocks) {
     constexpr int H = W - 1;
     const uint32_t b = blockIdx.x / cblocks;            // the entry (workgroup-uniform)
@@ -189,10 +192,36 @@ __global__ __launch_bounds__(kUpdBlock) void update_vec_kernel(UpdParams p, uint
         xv0[i] = i < g0 ? v : u32x2{0u, 0u};
     }
     float wf[kVecCh][W];
+    if constexpr (WIDE) {
+        constexpr int kWD = 2 * W;                      // dwords of the lane's taps
+        uint32_t wd[kWD];
+        const uint16_t *wq = p.w + int64_t(c) * W;
+        if constexpr ((W & 1) == 0) {
 #pragma unroll
-    for (int ch = 0; ch < kVecCh; ++ch)
+            for (int i = 0; i < kWD / 4; ++i) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(wq + 8 * i);
+                wd[4 * i] = v.x; wd[4 * i + 1] = v.y; wd[4 * i + 2] = v.z; wd[4 * i + 3] = v.w;
+            }
+        } else {
 #pragma unroll
-        for (int k = 0; k < W; ++k) wf[ch][k] = bf_one(p.w[int64_t(c + ch) * p.w_sd + k]);
+            for (int i = 0; i < kWD / 2; ++i) {
+                const u32x2 v = ld4ch(wq + 4 * i);
+                wd[2 * i] = v.x; wd[2 * i + 1] = v.y;
+            }
+        }
+#pragma unroll
+        for (int ch = 0; ch < kVecCh; ++ch)
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int e = ch * W + k;
+                wf[ch][k] = (e & 1) ? bf_hi(wd[e >> 1]) : bf_lo(wd[e >> 1]);
+            }
+    } else {
+#pragma unroll
+        for (int ch = 0; ch < kVecCh; ++ch)
+#pragma unroll
+            for (int k = 0; k < W; ++k) wf[ch][k] = bf_one(p.w[int64_t(c + ch) * p.w_sd + k]);
+    }
     // without a bias the first input stands in and is discarded
     const u32x2 bv = ld4ch(p.bias ? p.bias + c : xp);
     float b0[kVecCh];
@@ -319,8 +348,11 @@ hipError_t launch_w(const UpdParams &p, bool silu, hipStream_t s) {
         const int32_t lanes = p.dim / kVecCh;
         const uint32_t cblocks = uint32_t((lanes + kUpdBlock - 1) / kUpdBlock);
         const dim3 grid(cblocks * uint32_t(p.batch)), block(kUpdBlock);
-        if (silu) update_vec_kernel<W, true><<<grid, block, 0, s>>>(p, cblocks);
-        else update_vec_kernel<W, false><<<grid, block, 0, s>>>(p, cblocks);
+        const bool wide = p.w_sd == W && (reinterpret_cast<uintptr_t>(p.w) & 15) == 0;
+        if (silu && wide) update_vec_kernel<W, true, true><<<grid, block, 0, s>>>(p, cblocks);
+        else if (silu) update_vec_kernel<W, true, false><<<grid, block, 0, s>>>(p, cblocks);
+        else if (wide) update_vec_kernel<W, false, true><<<grid, block, 0, s>>>(p, cblocks);
+        else update_vec_kernel<W, false, false><<<grid, block, 0, s>>>(p, cblocks);
         return hipGetLastError();
     }
     const uint32_t cblocks = uint32_t((p.dim + kUpdBlock - 1) / kUpdBlock);

@@ -30,11 +30,12 @@ def windows(shape, device, dim_contig):
 
 
 def both(d, activation="silu", exact=False, in_place=False, use=OPTS + ("intermediate",),
-         windows_dim_contig=False, out_like_x=False):
+         windows_dim_contig=False, out_like_x=False, w_pitch=None):
     """Run the oracle and the library on the same inputs with the options of
     `d` named in `use`; compare out (tolerance, or bits when exact), the whole
     state cache and the intermediate windows (bits).  The GPU's out is
-    contiguous, or laid out like x when out_like_x."""
+    contiguous, or laid out like x when out_like_x; the GPU's weights are
+    packed, or rows of a (dim, w_pitch) buffer."""
     opts = {k: d[k] for k in OPTS if k in use and d.get(k) is not None}
     inter0 = d.get("intermediate") if "intermediate" in use else None
     x_cpu = d["x"]
@@ -58,7 +59,13 @@ def both(d, activation="silu", exact=False, in_place=False, use=OPTS + ("interme
         assert out.stride() == x.stride()
     else:
         out = torch.full(x.shape, -3.0, dtype=BF, device=DEV)
-    S.conv1d_update(x, st, gpu(d["weight"]), gpu(d["bias"]), activation=activation,
+    w = gpu(d["weight"])
+    if w_pitch is not None:
+        buf = torch.zeros(w.shape[0], w_pitch, dtype=BF, device=DEV)
+        buf[:, :w.shape[1]] = w
+        w = buf[:, :w.shape[1]]
+        assert w.stride(0) == w_pitch
+    S.conv1d_update(x, st, w, gpu(d["bias"]), activation=activation,
                     cache_indices=gpu(d["cache_indices"]), intermediate=inter, out=out,
                     **{k: gpu(v) for k, v in opts.items()})
     torch.cuda.synchronize()
@@ -232,8 +239,10 @@ def test_channel_contiguous_layouts(mode, width, seqlen):
            "scatter_windows": ("num_accepted_tokens", "intermediate", "output_state_indices"),
            "scatter_lines": ("num_accepted_tokens", "output_state_indices"),
            "ring": ("cache_seqlens",)}[mode]
+    # six tokens: taps from a pitched weight buffer (the per-channel tap loads)
     kw = dict(use=use, in_place=mode == "roll_in_place",
-              windows_dim_contig=mode == "scatter_windows", out_like_x=True)
+              windows_dim_contig=mode == "scatter_windows", out_like_x=True,
+              w_pitch=width + 3 if seqlen == 6 else None)
     d = channel_contiguous_batch(mode, width, seqlen, "exact")
     assert d["x"].stride(1) == 1 and d["conv_state"].stride(1) == 1
     both(d, activation=None, exact=True, **kw)
