@@ -325,6 +325,100 @@ __global__ __launch_bounds__(kUpdBlock) void update_vec_kernel(UpdParams p, uint
     }
 }
 
+// The plain update (no options) on states stored token-contiguous with
+// exactly width-1 columns, the usual decode cache: four adjacent channels'
+// histories are one run of 4(W-1) values, read and rewritten as W-1
+// 8-byte vectors; x and out as in update_vec_kernel.  The arithmetic is that
+// of update_kernel.
+template <int W, bool SILU>
+__global__ __launch_bounds__(kUpdBlock) void update_run_kernel(UpdParams p, uint32_t cblocks) {
+    constexpr int H = W - 1;
+    const uint32_t b = blockIdx.x / cblocks;
+    const int32_t c = int32_t(((blockIdx.x % cblocks) * kUpdBlock + threadIdx.x) * kVecCh);
+    if (int32_t(b) >= p.batch || c >= p.dim) return;
+
+    const int32_t g0 = p.seqlen < kUpdGroup ? p.seqlen : kUpdGroup;
+    const uint16_t *xp = p.x + int64_t(b) * p.x_sb + c;
+    u32x2 xv0[kUpdGroup];
+#pragma unroll
+    for (int i = 0; i < kUpdGroup; ++i) {
+        const u32x2 v = ld4ch(xp + int64_t(i < g0 ? i : 0) * p.x_st);
+        xv0[i] = i < g0 ? v : u32x2{0u, 0u};
+    }
+    float wf[kVecCh][W];
+#pragma unroll
+    for (int ch = 0; ch < kVecCh; ++ch)
+#pragma unroll
+        for (int k = 0; k < W; ++k) wf[ch][k] = bf_one(p.w[int64_t(c + ch) * p.w_sd + k]);
+    const u32x2 bv = ld4ch(p.bias ? p.bias + c : xp);
+    float b0[kVecCh];
+#pragma unroll
+    for (int ch = 0; ch < kVecCh; ++ch) b0[ch] = p.bias ? ch_of(bv, ch) : 0.0f;
+
+    const void *sx = reinterpret_cast<const void *>(reinterpret_cast<uintptr_t>(p.x) & ~uintptr_t(3));
+    const int32_t ci = int32_t(sld_u32(p.cache_idx ? static_cast<const void *>(p.cache_idx + b) : sx));
+    const int64_t line = p.cache_idx ? int64_t(ci) : int64_t(b);
+    if ((p.cache_idx && line == p.pad_slot_id) || line < 0 || line >= p.num_lines) return;
+
+    // the four histories: value k of channel ch is element ch*H + k of the run
+    uint16_t *run = p.cs + line * p.cs_sl + int64_t(c) * H;
+    uint32_t hd[2 * H];
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        const u32x2 v = ld4ch(run + 4 * i);
+        hd[2 * i] = v.x;
+        hd[2 * i + 1] = v.y;
+    }
+    uint32_t win[kVecCh][H];                           // bf16 bits, oldest first
+#pragma unroll
+    for (int ch = 0; ch < kVecCh; ++ch)
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            const int e = ch * H + k;
+            win[ch][k] = (hd[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        }
+
+    uint16_t *op = p.out + int64_t(b) * p.o_sb + c;
+    for (int32_t t0 = 0; t0 < p.seqlen; t0 += kUpdGroup) {
+        u32x2 xv[kUpdGroup];
+        if (t0 == 0) {
+#pragma unroll
+            for (int i = 0; i < kUpdGroup; ++i) xv[i] = xv0[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < kUpdGroup; ++i)
+                xv[i] = t0 + i < p.seqlen ? ld4ch(xp + int64_t(t0 + i) * p.x_st) : u32x2{0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < kUpdGroup; ++i) {
+            const int32_t t = t0 + i;
+            if (t >= p.seqlen) break;
+            float o[kVecCh];
+#pragma unroll
+            for (int ch = 0; ch < kVecCh; ++ch) {
+                float acc = b0[ch];
+#pragma unroll
+                for (int k = 0; k < H; ++k) acc = __builtin_fmaf(wf[ch][k], bf_one(uint16_t(win[ch][k])), acc);
+                acc = __builtin_fmaf(wf[ch][H], ch_of(xv[i], ch), acc);
+                o[ch] = act<SILU>(acc);
+                const uint32_t d = (ch >> 1) ? xv[i].y : xv[i].x;
+#pragma unroll
+                for (int k = 0; k + 1 < H; ++k) win[ch][k] = win[ch][k + 1];
+                win[ch][H - 1] = (d >> (16 * (ch & 1))) & 0xffffu;
+            }
+            st4ch(op + int64_t(t) * p.o_st, u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
+        }
+    }
+    // the new histories, written back as the same run
+#pragma unroll
+    for (int i = 0; i < 2 * H; ++i) {
+        const int e0 = 2 * i, e1 = 2 * i + 1;
+        hd[i] = win[e0 / H][e0 % H] | (win[e1 / H][e1 % H] << 16);
+    }
+#pragma unroll
+    for (int i = 0; i < H; ++i) st4ch(run + 4 * i, u32x2{hd[2 * i], hd[2 * i + 1]});
+}
+
 // Whether every tensor the update touches holds four adjacent channels as
 // one aligned 8-byte vector.
 bool vec_layout(const UpdParams &p) {
@@ -342,8 +436,29 @@ bool vec_layout(const UpdParams &p) {
     return true;
 }
 
+// Whether the update is the plain one on (lines, dim, width-1) token-
+// contiguous states, with x and out as vec_layout requires.
+bool run_layout(const UpdParams &p, int width) {
+    auto al = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 7) == 0; };
+    auto m4 = [](int64_t v) { return (v & 3) == 0; };
+    const bool one = p.seqlen == 1;
+    if (p.num_acc || p.ring_seen || p.inter || p.out_idx) return false;
+    if (p.state_len != width - 1 || p.cs_st != 1 || p.cs_sd != width - 1) return false;
+    if (p.dim % kVecCh != 0 || p.x_sd != 1 || p.o_sd != 1) return false;
+    if (!al(p.x) || !al(p.out) || !al(p.cs) || (p.bias && !al(p.bias))) return false;
+    return m4(p.x_sb) && m4(p.o_sb) && m4(p.cs_sl) && (one || (m4(p.x_st) && m4(p.o_st)));
+}
+
 template <int W>
 hipError_t launch_w(const UpdParams &p, bool silu, hipStream_t s) {
+    if (run_layout(p, W)) {
+        const int32_t lanes = p.dim / kVecCh;
+        const uint32_t cblocks = uint32_t((lanes + kUpdBlock - 1) / kUpdBlock);
+        const dim3 grid(cblocks * uint32_t(p.batch)), block(kUpdBlock);
+        if (silu) update_run_kernel<W, true><<<grid, block, 0, s>>>(p, cblocks);
+        else update_run_kernel<W, false><<<grid, block, 0, s>>>(p, cblocks);
+        return hipGetLastError();
+    }
     if (vec_layout(p)) {
         const int32_t lanes = p.dim / kVecCh;
         const uint32_t cblocks = uint32_t((lanes + kUpdBlock - 1) / kUpdBlock);

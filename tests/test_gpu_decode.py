@@ -12,7 +12,7 @@ DEV = "cuda"
 BF = torch.bfloat16
 
 
-def both(d, activation="silu", in_place=False, values_exact=False):
+def both(d, activation="silu", in_place=False, values_exact=False, out_like_x=False):
     x_cpu = d["x"]
     st_ref = d["conv_state"].clone()
     out_ref = torch.full(x_cpu.shape, -3.0, dtype=BF)
@@ -31,7 +31,7 @@ def both(d, activation="silu", in_place=False, values_exact=False):
             if line == -1:
                 out_ref[bi] = x_cpu[bi]
     else:
-        out = torch.full(x.shape, -3.0, dtype=BF, device=DEV)
+        out = torch.full_like(x, -3.0) if out_like_x else torch.full(x.shape, -3.0, dtype=BF, device=DEV)
         S.conv1d_update_decode(x, st, w, b, activation=activation, cache_indices=ci, out=out)
     torch.cuda.synchronize()
     if values_exact:
@@ -39,6 +39,22 @@ def both(d, activation="silu", in_place=False, values_exact=False):
     else:
         assert_close(out, out_ref, "decode out")
     assert_bits(st, st_ref, "decode state")
+
+
+@pytest.mark.parametrize("seqlen", [1, 6])
+@pytest.mark.parametrize("width", [2, 3, 4, 5])
+def test_decode_four_channel_runs(width, seqlen):
+    """Channel-contiguous x and out, (lines, dim, width-1) states and dim %
+    4 == 0: four channels' histories are one run per lane.  Two workgroups
+    of channels (the second partial), pads, one and six tokens; exact values
+    bit for bit, and SiLU."""
+    for values, act in (("exact", None), ("normal", "silu")):
+        d = W.decode_batch(batch=9, dim=1156, width=width, seqlen=seqlen, seed=560 + width,
+                           num_lines=12, n_pad=2, values=values)
+        assert d["x"].stride(1) == 1 and d["conv_state"].is_contiguous()
+        say(f"[decode] four-channel runs W{width} seqlen {seqlen} {values}")
+        both(d, activation=act, values_exact=values == "exact", out_like_x=True)
+        both(d, activation=act, values_exact=values == "exact", in_place=True)
 
 
 @pytest.mark.parametrize("width", [2, 3, 4, 5])
