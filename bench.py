@@ -289,6 +289,23 @@ def extras(torch, S, W, dev):
     log(f"[bench] decode dim4096 T1: {warm*1e3:.2f} us/launch in a graph, {cold*1e3:.2f} us "
         f"cold, host latency {statistics.median(lat)*1e6:.1f} us")
 
+    # decode at a serving batch: 64 entries x dim 8192, one token each
+    d = W.decode_batch(batch=64, dim=8192, width=4, seed=W.seed_for(2, 2), num_lines=128,
+                       device=dev)
+    xo = d["x"].clone()
+    fn = lambda: S.conv1d_update_decode(d["x"], d["conv_state"], d["weight"], d["bias"],
+                                        activation="silu", cache_indices=d["cache_indices"],
+                                        out=xo)
+    fn()
+    cold = event_time_ms(fn, 50, flush)
+    warm = graph_time_ms(fn)
+    nb = 64 * (4 * 8192 + 4 * 3 * 8192) + 2 * 8192 * 4 + 2 * 8192 + 4 * 64
+    ex["decode_64x8192_T1"] = {"graph_us_per_launch": round(warm * 1e3, 2),
+                               "cold_cache_us": round(cold * 1e3, 2), "bytes": nb,
+                               "GB/s_graph": round(nb / warm / 1e6, 1)}
+    log(f"[bench] decode 64x8192 T1: {warm*1e3:.2f} us/launch in a graph "
+        f"({nb / warm / 1e6:.0f} GB/s), {cold*1e3:.2f} us cold")
+
     # speculative verify: 64 entries x dim 8192, 4 tokens each, state rolled
     cfg = W.SPEC_DECODE
     d = W.spec_decode_batch(batch=cfg["batch"], dim=cfg["dim"], width=cfg["width"],
