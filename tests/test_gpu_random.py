@@ -76,12 +76,15 @@ def test_random_varlen_forward(case):
 
 @pytest.mark.parametrize("case", range(24))
 def test_random_update(case):
-    """Plain decode update: random batch, channel count, token count, width,
-    pads and bias, bit for bit with exact values."""
+    """Plain decode update: random batch, channel count (whole four-channel
+    groups in half the cases), token count, width, pads, bias and out
+    storage, bit for bit with exact values."""
     r = torch.Generator().manual_seed(7000 + case)
     ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=r))
     width = ri(2, 5)
     batch, dim, seqlen = ri(1, 12), ri(1, 700), ri(1, 6)
+    if case % 2 == 0:
+        dim = 4 * ri(1, 400)              # whole four-channel groups
     n_pad = ri(0, 2) if batch > 2 else 0
     d = W.decode_batch(batch=batch, dim=dim, width=width, seqlen=seqlen, seed=7100 + case,
                        num_lines=batch + ri(0, 3), n_pad=n_pad, values="exact",
@@ -92,8 +95,11 @@ def test_random_update(case):
     oracle.update_decode(x, st_ref, d["weight"], d["bias"], out_ref, cache_indices=ci,
                          activation=None)
     st_gpu = d["conv_state"].to(DEV)
-    out = torch.full(x.shape, -5.0, dtype=BF, device=DEV)
-    S.conv1d_update(x.to(DEV), st_gpu, d["weight"].to(DEV),
+    x_dev = x.to(DEV)
+    # out contiguous, or laid out like x (channel-contiguous)
+    out = (torch.full_like(x_dev, -5.0) if ri(0, 1) == 1
+           else torch.full(x.shape, -5.0, dtype=BF, device=DEV))
+    S.conv1d_update(x_dev, st_gpu, d["weight"].to(DEV),
                     None if d["bias"] is None else d["bias"].to(DEV), activation=None,
                     cache_indices=ci.to(DEV), out=out)
     torch.cuda.synchronize()
