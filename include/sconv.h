@@ -220,6 +220,14 @@ int conv1d_update_decode(const void *x, int64_t x_stride_seq, int64_t x_stride_d
  * is pad_slot_id or outside [0, num_cache_lines), when num_accepted_tokens[b]
  * is below 1 or above state_len - width + 2, or when cache_seqlens[b] is
  * negative.
+ * Layouts and speed (results do not depend on the layout): with dim % 4 ==
+ *   0, x and out of unit dim stride and every base and stride keeping four
+ *   channels 8-byte aligned, a lane handles four channels with 8-byte
+ *   accesses when either (a) the call has no option and conv_state is
+ *   [lines][dim][width-1] token-contiguous (the usual decode cache), or (b)
+ *   conv_state (and intermediate, when given) has unit dim stride.  Other
+ *   layouts take one lane per channel with 2-byte accesses, which bounds
+ *   large batches by the address unit (about 1.5-2x slower there).
  * Errors: as for conv1d_update_decode; cache_seqlens together with any of
  *   the three speculative options -> SCONV_ERR_ARG; state_len < width-1 ->
  *   SCONV_ERR_SHAPE; intermediate overlapping x, out, conv_state, weight or
