@@ -727,6 +727,27 @@ __global__ __launch_bounds__(kRowsBlock) void fwd_tok_rows_kernel(FwdTokParams p
 // query_start_loc and the per-sequence lines and flags are staged in LDS.
 constexpr int kVarWaves = 4;                      // waves per block sharing the staged tables
 
+// K adjacent bf16 values from p through vector loads of only the dwords
+// that hold them (as sld_run, in vector registers).
+template <int K>
+__device__ __forceinline__ U16Run<K> vld_run(const uint16_t *p) {
+    constexpr int N = K / 2 + 1;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(a & ~uintptr_t(3));
+    const uint32_t m = uint32_t(a >> 1) & 1u;
+    uint32_t raw[N];
+#pragma unroll
+    for (int i = 0; i < N - 1; ++i) raw[i] = q[i];
+    raw[N - 1] = (K & 1) ? q[N - 1] : q[N - 2 + m];
+    U16Run<K> r;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint64_t hi = i + 1 < N ? uint64_t(raw[i + 1]) << 32 : 0;
+        r.d[i] = uint32_t((hi | raw[i]) >> (16 * m));
+    }
+    return r;
+}
+
 template <int W, bool SILU>
 __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(FwdTokParams p,
                                                                                 uint32_t chunk_blocks) {
@@ -796,15 +817,23 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         const size_t row0 = size_t(c) * T;
         const uint16_t *hbase = init ? p.sb.cs + line * p.sb.cs_sl + int64_t(c) * p.sb.cs_sd : p.x + row0;
         const Taps<W> tp = load_taps<W>(p, c);
+        // the sequence's first and last width-1 inputs as two runs of the row
+        // (a first run that would pass the row's end starts d earlier)
+        const int64_t xs = st + H <= int64_t(T) ? st : int64_t(T) - H;
+        const int d = int(st - xs);
+        const U16Run<H> xrun = vld_run<H>(p.x + row0 + size_t(xs));
+        const U16Run<H> nrun = vld_run<H>(p.x + row0 + size_t(L >= H ? en - H : xs));
         uint32_t h[H], xh[H], nb[H];
 #pragma unroll
         for (int q = 0; q < H; ++q) {
             const uint16_t hv = hbase[init ? q * p.sb.cs_st : 0];
-            const uint16_t xv = p.x[row0 + size_t(st) + (q < L ? q : 0)];
-            const uint16_t nv = p.x[row0 + size_t(L >= H ? en - H + q : st)];
+            uint32_t xv = xrun.elem(q);
+#pragma unroll
+            for (int e = 1; e < H; ++e)
+                if (d == e && q + e < H) xv = xrun.elem(q + e < H ? q + e : 0);
             h[q] = init ? hv : 0u;
             xh[q] = q < L ? xv : 0u;
-            nb[q] = nv;
+            nb[q] = nrun.elem(q);
         }
         // outputs j < min(L, H): u = history ++ sequence, output j uses u[j .. j+H]
 #pragma unroll
