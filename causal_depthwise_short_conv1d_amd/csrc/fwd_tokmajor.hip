@@ -42,6 +42,10 @@ constexpr int kLongWaves = 4;                     // waves per long-row block (f
                                                   // workgroups dispatch faster at 10^5 waves)
 constexpr int kLongRounds = 4;                    // 64-chunk rounds per long-row wave (measured:
                                                   // 1 and 2 repeat the wave setup too often)
+constexpr int kLongRoundsMid = 3;                 // rounds for kLongMidLo <= T < kLongMidHi
+constexpr uint32_t kLongMidLo = 3072;             // (measured on gfx950: 3 rounds are 1.3-3.5%
+constexpr uint32_t kLongMidHi = 10000;            // faster at T 3100-9999, 5% slower at T 2048,
+                                                  // where 4 rounds are exactly one row per wave)
 
 // Weights of one channel for the dot2 path: taps as packed bf16 pairs
 // (w[2p], w[2p+1]), the odd last tap and the bias as fp32.
@@ -1136,9 +1140,15 @@ hipError_t launch_ws(const FwdTokParams &p, hipStream_t s) {
     } else if (p.sb.batch > 1) {
         fwd_tokmajor_kernel<W, SILU, true><<<grid, block, 0, s>>>(p);
     } else if (p.T >= kWaveElems) {
-        constexpr uint32_t kLB = kLongWaves * kLongRounds * kWaveSize;
-        const uint32_t lb = (p.n_chunks + kLB - 1) / kLB;
-        fwd_tok_long_kernel<W, SILU, kLongRounds><<<dim3(lb), dim3(kLongWaves * kWaveSize), 0, s>>>(p);
+        if (p.T >= kLongMidLo && p.T < kLongMidHi) {
+            constexpr uint32_t kLB = kLongWaves * kLongRoundsMid * kWaveSize;
+            const uint32_t lb = (p.n_chunks + kLB - 1) / kLB;
+            fwd_tok_long_kernel<W, SILU, kLongRoundsMid><<<dim3(lb), dim3(kLongWaves * kWaveSize), 0, s>>>(p);
+        } else {
+            constexpr uint32_t kLB = kLongWaves * kLongRounds * kWaveSize;
+            const uint32_t lb = (p.n_chunks + kLB - 1) / kLB;
+            fwd_tok_long_kernel<W, SILU, kLongRounds><<<dim3(lb), dim3(kLongWaves * kWaveSize), 0, s>>>(p);
+        }
     } else if (p.T >= uint32_t(kShortMinT)) {
         // Rounds per wave, measured on gfx950: one round (the most waves in
         // flight) up to 512K chunks, two from there, four from 2M, where a
