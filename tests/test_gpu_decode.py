@@ -57,6 +57,19 @@ def test_decode_four_channel_runs(width, seqlen):
         both(d, activation=act, values_exact=values == "exact", in_place=True)
 
 
+@pytest.mark.parametrize("values", ["normal", "exact"])
+def test_decode_serving_batch_full_size(values):
+    """64 entries x dim 8192, one token each, 128 lines, out laid out like x:
+    the decode step the benchmark times at a serving batch."""
+    d = W.decode_batch(batch=64, dim=8192, width=4, seed=W.seed_for(2, 2), num_lines=128,
+                       values=values)
+    say(f"[decode] 64 x 8192 T1 {values}")
+    if values == "exact":
+        both(d, activation=None, values_exact=True, out_like_x=True)
+    else:
+        both(d, out_like_x=True)
+
+
 @pytest.mark.parametrize("width", [2, 3, 4, 5])
 def test_decode_single_token_dim4096(width):
     """The T=1 row of the prefill sweep, through the decode entry point."""

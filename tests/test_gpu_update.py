@@ -91,6 +91,10 @@ def test_spec_roll_full_size(state_layout):
                             state_layout=state_layout)
     say(f"[update] spec roll full size {state_layout}")
     both(d)
+    if state_layout == "dim_contig":
+        # out laid out like x, as the benchmark launches it: the four-channel kernel
+        say("[update] spec roll full size, out like x")
+        both(d, out_like_x=True)
 
 
 @pytest.mark.parametrize("width", [2, 3, 4, 5])
