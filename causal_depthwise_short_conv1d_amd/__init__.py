@@ -151,11 +151,12 @@ def _call(fn: str, *args) -> None:
 
 
 def new_output(x: torch.Tensor) -> torch.Tensor:
-    """An uninitialised output in x's storage class: a compact (dim, T) array
-    for token-contiguous x, else (T, pitch) storage viewed as (dim, T) with a
-    row pitch rounded up to 8 elements (16-byte aligned rows)."""
+    """An uninitialised output in the storage class of x's smaller stride: a
+    compact (dim, T) array when tokens are x's closer axis, else (T, pitch)
+    storage viewed as (dim, T) with a row pitch rounded up to 8 elements
+    (16-byte aligned rows).  Both are layouts the vector kernels take."""
     dim, total = x.shape
-    if total > 1 and x.stride(1) == 1 and (dim == 1 or x.stride(0) == total):
+    if dim == 1 or (total > 1 and x.stride(1) < x.stride(0)):
         return torch.empty((dim, total), dtype=x.dtype, device=x.device)
     pitch = (dim + 7) // 8 * 8
     return torch.empty((total, pitch), dtype=x.dtype, device=x.device)[:, :dim].t()
@@ -164,9 +165,9 @@ def new_output(x: torch.Tensor) -> torch.Tensor:
 def conv1d_fwd_varlen(x, weight, bias, conv_states, query_start_loc,
                       cache_indices=None, has_initial_state=None,
                       activation="silu", pad_slot_id: int = -1, out=None):
-    """Varlen prefill.  x: logical (dim, total_T) bf16, token-contiguous
-    (compact (dim, T)) or channel-contiguous ((T, dim) storage viewed as
-    (dim, T)); weight (dim, width); bias (dim,) or None; conv_states
+    """Varlen prefill.  x: logical (dim, total_T) bf16 with any strides
+    (compact (dim, T) and 16-byte aligned (T, dim) rows take the vector
+    kernels); weight (dim, width); bias (dim,) or None; conv_states
     (lines, dim, width-1) or None, updated in place; query_start_loc int32
     (batch+1,); cache_indices int32 (batch,) or None; has_initial_state bool
     (batch,) or None.  Returns out (a new tensor with x's strides unless

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsconv.so")
-SOURCES = ["sconv_api.hip", "fwd_tokmajor.hip", "fwd_chanlast.hip",
+SOURCES = ["sconv_api.hip", "fwd_tokmajor.hip", "fwd_chanlast.hip", "general.hip",
            "update_decode.hip", "paged_fused.hip", "seq_metadata.hip"]
 ARCH = os.environ.get("SCONV_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

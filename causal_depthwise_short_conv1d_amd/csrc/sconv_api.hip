@@ -1,6 +1,8 @@
 // libsconv C ABI: host-side validation, layout dispatch and launch.
-// Nothing here touches device memory or synchronises; every successful call
-// enqueues exactly one kernel on the caller's stream.
+// Nothing here touches device memory or synchronises.  A successful call
+// enqueues one kernel on the caller's stream: a vector kernel when the
+// layout allows one, else the general-stride kernel (a token-contiguous
+// forward of 2^32 elements or more enqueues one launch per channel group).
 #include <stddef.h>
 #include <initializer_list>
 #include <stdint.h>
@@ -15,7 +17,7 @@ namespace {
 constexpr int kVersionMajor = 1;
 constexpr int kMaxWidthHistory = SCONV_MAX_WIDTH - 1;
 static_assert(kMaxPagedStreams == SCONV_MAX_PAGED_STREAMS, "stream table size");
-constexpr int kVersionMinor = 3;
+constexpr int kVersionMinor = 4;
 
 // Byte range [lo, hi) covered by a strided bf16 tensor; empty when a size is 0.
 struct Span {
@@ -43,6 +45,30 @@ bool overlap(const Span &a, const Span &b) {
 }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// No two elements of a strided tensor share an address: taken in order of
+// stride, every dimension of size > 1 steps past the whole span of the
+// smaller ones.  Outputs and written caches must pass (their elements are
+// written by different lanes); inputs may be any view, broadcasts included.
+bool non_overlapping(std::initializer_list<int64_t> sizes, std::initializer_list<int64_t> strides) {
+    int64_t n[4], st[4];
+    int k = 0;
+    auto sp = strides.begin();
+    for (int64_t s : sizes) {
+        const int64_t d = *sp++;
+        if (s <= 1) continue;
+        int i = k++;
+        for (; i > 0 && st[i - 1] > d; --i) { n[i] = n[i - 1]; st[i] = st[i - 1]; }
+        n[i] = s;
+        st[i] = d;
+    }
+    int64_t span = 1;          // one past the largest offset of the dimensions so far
+    for (int i = 0; i < k; ++i) {
+        if (st[i] < span) return false;
+        span += st[i] * (n[i] - 1);
+    }
+    return true;
+}
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SCONV_OK : SCONV_ERR_LAUNCH; }
 
@@ -83,7 +109,7 @@ const char *sconv_status_string(int status) {
         case SCONV_ERR_STRIDE: return "unsupported stride / layout";
         case SCONV_ERR_WIDTH: return "width outside 2..5";
         case SCONV_ERR_ALIAS: return "output overlaps an input";
-        case SCONV_ERR_ALIGN: return "pointer or stride misaligned for 16-byte vectors";
+        case SCONV_ERR_ALIGN: return "pointer not aligned to its element size";
         case SCONV_ERR_ARG: return "invalid enumerated argument";
         case SCONV_ERR_LAUNCH: return "kernel launch failed";
         default: return "unknown status";
@@ -109,18 +135,22 @@ int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
     if (!x || !weight || !query_start_loc || !out) return SCONV_ERR_NULL;
     if (has_initial_state && !conv_states) return SCONV_ERR_NULL;
     if (x_stride_dim < 0 || x_stride_tok < 0 || o_stride_dim < 0 || o_stride_tok < 0 ||
-        cs_stride_line < 0 || cs_stride_dim < 0 || cs_stride_tok < 0)
+        cs_stride_line < 0 || cs_stride_dim < 0 || cs_stride_tok < 0 || w_stride_dim < 0)
         return SCONV_ERR_STRIDE;
-    if (w_stride_dim < width) return SCONV_ERR_STRIDE;
     if (conv_states) {
         if (num_cache_lines < 1) return SCONV_ERR_SHAPE;
         if (!cache_indices && num_cache_lines < batch) return SCONV_ERR_SHAPE;
     }
-    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(weight, 2) || !aligned(bias, 2) ||
+    if (!aligned(x, 2) || !aligned(out, 2) || !aligned(weight, 2) || !aligned(bias, 2) ||
         !aligned(conv_states, 2) || !aligned(cache_indices, 4) || !aligned(query_start_loc, 4))
         return SCONV_ERR_ALIGN;
 
     const int64_t T = total_tokens;
+    // outputs and states are written element by element: no two may coincide
+    if (!non_overlapping({dim, T}, {o_stride_dim, o_stride_tok})) return SCONV_ERR_STRIDE;
+    if (conv_states && !non_overlapping({num_cache_lines, dim, width - 1},
+                                        {cs_stride_line, cs_stride_dim, cs_stride_tok}))
+        return SCONV_ERR_STRIDE;
     const Span sx = span_of(x, {dim, T}, {x_stride_dim, x_stride_tok});
     const Span so = span_of(out, {dim, T}, {o_stride_dim, o_stride_tok});
     const Span sw = span_of(weight, {dim, width}, {w_stride_dim, 1});
@@ -145,12 +175,21 @@ int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
     sb.total_T = T;
     const bool silu = activation == SCONV_ACT_SILU;
 
+    // The vector kernels read x and out in 16-byte pieces and whole weight
+    // rows through buffer descriptors; every other layout takes the
+    // general-stride kernel.
+    const bool vec_ok = aligned(x, 16) && aligned(out, 16) && w_stride_dim >= width;
+    // one descriptor spans a state line's channels
+    const int64_t line_span =
+        conv_states ? ((int64_t(dim) - 1) * cs_stride_dim + int64_t(width - 2) * cs_stride_tok + 1) * 2
+                    : 0;
+
     // A single token is both layouts at once; the per-row kernel of the
     // token-contiguous path (one lane per channel) serves it with the
     // shortest chain of reads.
     const bool one_token_rows = T == 1 && batch <= 1 && tokmajor_ok(x_stride_dim, x_stride_tok, dim, T) &&
                                 tokmajor_ok(o_stride_dim, o_stride_tok, dim, T);
-    if (!one_token_rows && chanlast_ok(x_stride_dim, x_stride_tok, dim, T) &&
+    if (vec_ok && !one_token_rows && chanlast_ok(x_stride_dim, x_stride_tok, dim, T) &&
         chanlast_ok(o_stride_dim, o_stride_tok, dim, T)) {
         FwdClParams p;
         p.x = static_cast<const uint16_t *>(x);
@@ -169,42 +208,70 @@ int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
         const int64_t row_span = int64_t(p.bt + 2 * kMaxWidthHistory) *
                                      (x_stride_tok > o_stride_tok ? x_stride_tok : o_stride_tok) * 2 +
                                  int64_t(dim) * 2;
-        const int64_t line_span =
-            conv_states ? ((int64_t(dim) - 1) * cs_stride_dim + int64_t(width - 2) * cs_stride_tok + 1) * 2
-                        : 0;
-        if (row_span >= kMaxDescriptorSpan || line_span >= kMaxDescriptorSpan) return SCONV_ERR_SHAPE;
         p.n_tiles = int32_t((T + p.bt - 1) / p.bt);
-        if (uint64_t(p.n_tiles) * uint64_t(p.n_slabs) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;
-        return launch_status(launch_fwd_chanlast(p, width, silu, stream));
+        if (row_span < kMaxDescriptorSpan && line_span < kMaxDescriptorSpan &&
+            uint64_t(p.n_tiles) * uint64_t(p.n_slabs) < (uint64_t(1) << 31))
+            return launch_status(launch_fwd_chanlast(p, width, silu, stream));
+    } else if (vec_ok && line_span < kMaxDescriptorSpan &&
+               tokmajor_ok(x_stride_dim, x_stride_tok, dim, T) &&
+               tokmajor_ok(o_stride_dim, o_stride_tok, dim, T)) {
+        // The token-contiguous kernels index a (dim, T) array with 32-bit
+        // element offsets.  Channels are independent, so a larger array is
+        // run as consecutive channel groups of fewer than 2^32 elements,
+        // each a compact (group, T) array of its own (one launch per group;
+        // groups start on 16-byte boundaries).
+        int64_t group = dim;
+        if (uint64_t(dim) * uint64_t(T) >= (uint64_t(1) << 32)) {
+            group = int64_t((uint64_t(1) << 32) - 1) / T;
+            if (T % kVec) group -= group % kVec;
+        }
+        if (group > 0) {
+            for (int64_t c0 = 0; c0 < dim; c0 += group) {
+                const int64_t g = dim - c0 < group ? dim - c0 : group;
+                const uint64_t n = uint64_t(g) * uint64_t(T);
+                FwdTokParams p;
+                p.x = static_cast<const uint16_t *>(x) + c0 * T;
+                p.out = static_cast<uint16_t *>(out) + c0 * T;
+                p.w = static_cast<const uint16_t *>(weight) + c0 * w_stride_dim;
+                p.w_sd = w_stride_dim;
+                p.bias = bias ? static_cast<const uint16_t *>(bias) + c0 : nullptr;
+                p.sb = sb;
+                if (conv_states) p.sb.cs = sb.cs + c0 * cs_stride_dim;
+                p.T = uint32_t(T);
+                p.divT = FastDivU32::make(uint32_t(T));
+                p.n_elems = uint32_t(n);
+                p.n_chunks = uint32_t((n + kVec - 1) / kVec);
+                p.dim = int32_t(g);
+                p.bias_rd = p.bias ? p.bias : p.w;
+                p.bias_mask = p.bias ? 0xffffu : 0u;
+                p.ci_rd = sb.cache_idx ? sb.cache_idx : sb.qsl;
+                p.hi_rd = sb.has_init ? sb.has_init : reinterpret_cast<const uint8_t *>(sb.qsl);
+                const int rc = launch_status(launch_fwd_tokmajor(p, width, silu, stream));
+                if (rc != SCONV_OK) return rc;
+            }
+            return SCONV_OK;
+        }
     }
-    if (tokmajor_ok(x_stride_dim, x_stride_tok, dim, T) &&
-        tokmajor_ok(o_stride_dim, o_stride_tok, dim, T)) {
-        const uint64_t n = uint64_t(dim) * uint64_t(T);
-        if (n >= (uint64_t(1) << 32)) return SCONV_ERR_SHAPE;
-        // one descriptor spans a state line's channels
-        const int64_t line_span =
-            conv_states ? ((int64_t(dim) - 1) * cs_stride_dim + int64_t(width - 2) * cs_stride_tok + 1) * 2
-                        : 0;
-        if (line_span >= kMaxDescriptorSpan) return SCONV_ERR_SHAPE;
-        FwdTokParams p;
-        p.x = static_cast<const uint16_t *>(x);
-        p.out = static_cast<uint16_t *>(out);
-        p.w = static_cast<const uint16_t *>(weight);
-        p.w_sd = w_stride_dim;
-        p.bias = static_cast<const uint16_t *>(bias);
-        p.sb = sb;
-        p.T = uint32_t(T);
-        p.divT = FastDivU32::make(uint32_t(T));
-        p.n_elems = uint32_t(n);
-        p.n_chunks = uint32_t((n + kVec - 1) / kVec);
-        p.dim = dim;
-        p.bias_rd = bias ? p.bias : p.w;
-        p.bias_mask = bias ? 0xffffu : 0u;
-        p.ci_rd = sb.cache_idx ? sb.cache_idx : sb.qsl;
-        p.hi_rd = sb.has_init ? sb.has_init : reinterpret_cast<const uint8_t *>(sb.qsl);
-        return launch_status(launch_fwd_tokmajor(p, width, silu, stream));
-    }
-    return SCONV_ERR_STRIDE;
+
+    FwdGenParams g;
+    g.x = static_cast<const uint16_t *>(x);
+    g.out = static_cast<uint16_t *>(out);
+    g.x_sd = x_stride_dim;
+    g.x_st = x_stride_tok;
+    g.o_sd = o_stride_dim;
+    g.o_st = o_stride_tok;
+    g.w = static_cast<const uint16_t *>(weight);
+    g.w_sd = w_stride_dim;
+    g.bias = static_cast<const uint16_t *>(bias);
+    g.sb = sb;
+    g.dim = dim;
+    g.T = T;
+    // lanes along the axis of x with the smaller stride
+    g.lanes_on_tokens = dim == 1 || (T > 1 && x_stride_tok < x_stride_dim);
+    const int64_t lane_axis = g.lanes_on_tokens ? T : dim;
+    g.tiles_per_line = (lane_axis + kGenTile - 1) / kGenTile;
+    g.n_tiles = (g.lanes_on_tokens ? int64_t(dim) : T) * g.tiles_per_line;
+    return launch_status(launch_fwd_general(g, width, silu, stream));
 }
 
 int conv1d_update(const void *x, int64_t x_stride_seq, int64_t x_stride_dim,
@@ -233,9 +300,16 @@ int conv1d_update(const void *x, int64_t x_stride_seq, int64_t x_stride_dim,
     if (x_stride_seq < 0 || x_stride_dim < 0 || x_stride_tok < 0 || o_stride_seq < 0 ||
         o_stride_dim < 0 || o_stride_tok < 0 || cs_stride_line < 0 || cs_stride_dim < 0 ||
         cs_stride_tok < 0 || it_stride_seq < 0 || it_stride_step < 0 || it_stride_dim < 0 ||
-        it_stride_win < 0 || osi_stride_seq < 0 || osi_stride_step < 0)
+        it_stride_win < 0 || osi_stride_seq < 0 || osi_stride_step < 0 || w_stride_dim < 0)
         return SCONV_ERR_STRIDE;
-    if (w_stride_dim < width) return SCONV_ERR_STRIDE;
+    // outputs, states and saved windows are written element by element
+    if (!non_overlapping({batch, dim, seqlen}, {o_stride_seq, o_stride_dim, o_stride_tok}) ||
+        !non_overlapping({num_cache_lines, dim, state_len},
+                         {cs_stride_line, cs_stride_dim, cs_stride_tok}) ||
+        (intermediate && !non_overlapping({batch, seqlen, dim, width - 1},
+                                          {it_stride_seq, it_stride_step, it_stride_dim,
+                                           it_stride_win})))
+        return SCONV_ERR_STRIDE;
     if (num_cache_lines < 1 || (!cache_indices && num_cache_lines < batch)) return SCONV_ERR_SHAPE;
     if (!aligned(x, 2) || !aligned(out, 2) || !aligned(weight, 2) || !aligned(bias, 2) ||
         !aligned(conv_state, 2) || !aligned(intermediate, 2) || !aligned(cache_indices, 4) ||
@@ -376,38 +450,47 @@ int sconv_paged_fused_multi(int32_t num_streams, const void *const *x,
         return SCONV_ERR_NULL;
     if (bt_stride_req < 0 || c_stride_blk < 0 || c_stride_head < 0 || c_stride_slot < 0)
         return SCONV_ERR_STRIDE;
-    if (c_stride_blk % kVec || c_stride_head % kVec || c_stride_slot % kVec ||
-        !aligned(cache, 16) || !aligned(positions, 8) || !aligned(slot_mapping, 8) ||
+    if (!aligned(cache, 2) || !aligned(positions, 8) || !aligned(slot_mapping, 8) ||
         !aligned(query_start_loc, 4) || !aligned(block_table, 4))
         return SCONV_ERR_ALIGN;
-    if (c_stride_blk * 2 >= kMaxDescriptorSpan) return SCONV_ERR_SHAPE;
-    // slots and block-table positions are resolved in 32-bit arithmetic
-    if (num_blocks * int64_t(block_size) >= (int64_t(1) << 31) ||
-        int64_t(max_blocks) * block_size >= (int64_t(1) << 31))
-        return SCONV_ERR_SHAPE;
+    // inserts write cache elements: no two slots / heads may share one
+    if (!non_overlapping({num_blocks, num_heads, block_size, head_dim},
+                         {c_stride_blk, c_stride_head, c_stride_slot, 1}))
+        return SCONV_ERR_STRIDE;
     const Span sc = span_of(cache, {num_blocks, num_heads, block_size, head_dim},
                             {c_stride_blk, c_stride_head, c_stride_slot, 1});
 
+    // The vector kernel moves 4 channels of one head per lane in 8-byte
+    // pieces through buffer descriptors, with 32-bit slot arithmetic; other
+    // layouts take the general-stride kernel.
+    bool vec_ok = aligned(cache, 16) && c_stride_blk % kVec == 0 && c_stride_head % kVec == 0 &&
+                  c_stride_slot % kVec == 0 && c_stride_blk * 2 < kMaxDescriptorSpan &&
+                  num_blocks * int64_t(block_size) < (int64_t(1) << 31) &&
+                  int64_t(max_blocks) * block_size < (int64_t(1) << 31);
+
     PagedParams p;
     Span sx[kMaxPagedStreams], so[kMaxPagedStreams], sw[kMaxPagedStreams], sb[kMaxPagedStreams];
-    int64_t total_slabs = 0;
+    int64_t total_slabs = 0, total_cols = 0;
     for (int i = 0; i < num_streams; ++i) {
         const void *bi = bias ? bias[i] : nullptr;
         if (!x[i] || !weight[i] || !out[i]) return SCONV_ERR_NULL;
         const int64_t C = int64_t(num_heads) * ws[i];
         if (C > INT32_MAX) return SCONV_ERR_SHAPE;
-        if (x_stride_tok[i] < C || o_stride_tok[i] < C || w_stride_dim[i] < width)
+        if (x_stride_tok[i] < 0 || o_stride_tok[i] < 0 || w_stride_dim[i] < 0)
             return SCONV_ERR_STRIDE;
-        if (ws[i] % kVec || off_s[i] % kVec || x_stride_tok[i] % kVec ||
-            o_stride_tok[i] % kVec || !aligned(x[i], 16) || !aligned(out[i], 16) ||
-            !aligned(weight[i], 2) || !aligned(bi, 2))
+        // rows of out are written element by element: they may not overlap
+        if (!non_overlapping({num_tokens, C}, {o_stride_tok[i], 1})) return SCONV_ERR_STRIDE;
+        if (!aligned(x[i], 2) || !aligned(out[i], 2) || !aligned(weight[i], 2) || !aligned(bi, 2))
             return SCONV_ERR_ALIGN;
         // one descriptor spans a tile's rows of x (with the width-1 before it) or of out
         const int64_t row_span = int64_t(kPagedBT + SCONV_MAX_WIDTH) *
                                      (x_stride_tok[i] > o_stride_tok[i] ? x_stride_tok[i]
                                                                         : o_stride_tok[i]) * 2 +
                                  C * 2;
-        if (row_span >= kMaxDescriptorSpan) return SCONV_ERR_SHAPE;
+        vec_ok = vec_ok && ws[i] % kVec == 0 && off_s[i] % kVec == 0 &&
+                 x_stride_tok[i] % kVec == 0 && o_stride_tok[i] % kVec == 0 &&
+                 x_stride_tok[i] >= C && aligned(x[i], 16) && aligned(out[i], 16) &&
+                 row_span < kMaxDescriptorSpan;
         sx[i] = span_of(x[i], {num_tokens, C}, {x_stride_tok[i], 1});
         so[i] = span_of(out[i], {num_tokens, C}, {o_stride_tok[i], 1});
         sw[i] = span_of(weight[i], {C, width}, {w_stride_dim[i], 1});
@@ -425,6 +508,7 @@ int sconv_paged_fused_multi(int32_t num_streams, const void *const *x,
         st.C = int32_t(C);
         st.slab0 = int32_t(total_slabs);
         total_slabs += (C + kPagedSlab - 1) / kPagedSlab;
+        total_cols += (C + kGenTile - 1) / kGenTile;
     }
     for (int i = num_streams; i < kMaxPagedStreams; ++i) p.s[i] = p.s[0];
     // outputs overlap nothing; the cache overlaps no input
@@ -436,35 +520,64 @@ int sconv_paged_fused_multi(int32_t num_streams, const void *const *x,
                 (j != i && overlap(so[i], so[j])))
                 return SCONV_ERR_ALIAS;
     }
+    const bool silu = activation == SCONV_ACT_SILU;
 
-    p.num_streams = num_streams;
-    p.cache = static_cast<uint16_t *>(cache);
-    p.c_sb = c_stride_blk;
-    p.c_sh = c_stride_head;
-    p.c_sn = c_stride_slot;
-    p.num_blocks = num_blocks;
-    p.block_size = block_size;
-    p.pos = positions;
-    p.slot = slot_mapping;
-    p.qsl = query_start_loc;
-    p.num_reqs = num_reqs;
-    p.bt = block_table;
-    p.bt_sr = bt_stride_req;
-    p.max_blocks = block_table ? max_blocks : 0;
-    p.div_n = FastDivU32::make(uint32_t(block_size));
-    p.slot_lim = num_blocks * int64_t(block_size);
-    p.src_lim = int64_t(p.max_blocks) * block_size;
-    p.bt_rd = (block_table && num_reqs > 0 && max_blocks > 0) ? block_table : query_start_loc;
-    p.T = num_tokens;
-    // A step that would not fill the chip once with 16-token tiles takes
-    // 8-token tiles: twice the waves, each with half the chain of round trips.
-    const int64_t tiles16 = (num_tokens + kPagedBT - 1) / kPagedBT;
-    p.tile_bt = tiles16 * total_slabs < kPagedFillWaves ? kPagedBTSmall : kPagedBT;
-    p.n_tiles = int32_t((num_tokens + p.tile_bt - 1) / p.tile_bt);
-    if (uint64_t(p.n_tiles) * uint64_t(total_slabs) >= (uint64_t(1) << 31)) return SCONV_ERR_SHAPE;
-    p.total_slabs = int32_t(total_slabs);
-    return launch_status(launch_paged_fused(p, width, activation == SCONV_ACT_SILU,
-                                            use_residual != 0, stream));
+    if (vec_ok) {
+        p.num_streams = num_streams;
+        p.cache = static_cast<uint16_t *>(cache);
+        p.c_sb = c_stride_blk;
+        p.c_sh = c_stride_head;
+        p.c_sn = c_stride_slot;
+        p.num_blocks = num_blocks;
+        p.block_size = block_size;
+        p.pos = positions;
+        p.slot = slot_mapping;
+        p.qsl = query_start_loc;
+        p.num_reqs = num_reqs;
+        p.bt = block_table;
+        p.bt_sr = bt_stride_req;
+        p.max_blocks = block_table ? max_blocks : 0;
+        p.div_n = FastDivU32::make(uint32_t(block_size));
+        p.slot_lim = num_blocks * int64_t(block_size);
+        p.src_lim = int64_t(p.max_blocks) * block_size;
+        p.bt_rd = (block_table && num_reqs > 0 && max_blocks > 0) ? block_table : query_start_loc;
+        p.T = num_tokens;
+        // A step that would not fill the chip once with 16-token tiles takes
+        // 8-token tiles: twice the waves, each with half the chain of round trips.
+        const int64_t tiles16 = (num_tokens + kPagedBT - 1) / kPagedBT;
+        p.tile_bt = tiles16 * total_slabs < kPagedFillWaves ? kPagedBTSmall : kPagedBT;
+        p.n_tiles = int32_t((num_tokens + p.tile_bt - 1) / p.tile_bt);
+        p.total_slabs = int32_t(total_slabs);
+        if (uint64_t(p.n_tiles) * uint64_t(total_slabs) < (uint64_t(1) << 31))
+            return launch_status(launch_paged_fused(p, width, silu, use_residual != 0, stream));
+    }
+
+    PagedGenParams g;
+    for (int i = 0; i < kMaxPagedStreams; ++i) g.s[i] = p.s[i];
+    int64_t col0 = 0;
+    for (int i = 0; i < num_streams; ++i) {
+        g.s[i].slab0 = int32_t(col0);
+        col0 += (int64_t(g.s[i].C) + kGenTile - 1) / kGenTile;
+    }
+    for (int i = num_streams; i < kMaxPagedStreams; ++i) g.s[i] = g.s[0];
+    g.num_streams = num_streams;
+    g.cols = total_cols;
+    g.cache = static_cast<uint16_t *>(cache);
+    g.c_sb = c_stride_blk;
+    g.c_sh = c_stride_head;
+    g.c_sn = c_stride_slot;
+    g.num_blocks = num_blocks;
+    g.block_size = block_size;
+    g.pos = positions;
+    g.slot = slot_mapping;
+    g.qsl = query_start_loc;
+    g.num_reqs = num_reqs;
+    g.bt = block_table;
+    g.bt_sr = bt_stride_req;
+    g.max_blocks = block_table ? max_blocks : 0;
+    g.T = num_tokens;
+    g.n_tiles = num_tokens * total_cols;
+    return launch_status(launch_paged_general(g, width, silu, use_residual != 0, stream));
 }
 
 int sconv_paged_fused(const void *x, int64_t x_stride_tok, const void *weight,

@@ -84,6 +84,26 @@ struct FwdClParams {           // channel-contiguous (T, dim) storage
     int32_t n_tiles;           // ceil(T / bt)
 };
 
+// Any storage of x / out: element (c, t) at c * sd + t * st, 64-bit offsets,
+// bases aligned to 2 bytes only.  Work is cut into tiles of kGenTile lanes
+// along whichever axis of x has the smaller stride, so a wave's reads are
+// as close together as the layout allows.
+struct FwdGenParams {
+    const uint16_t *x;
+    uint16_t *out;
+    int64_t x_sd, x_st, o_sd, o_st;
+    const uint16_t *w;
+    int64_t w_sd;
+    const uint16_t *bias;      // or null
+    SeqBatch sb;
+    int32_t dim;
+    int64_t T;
+    bool lanes_on_tokens;      // a tile is kGenTile tokens of one channel, else
+                               // kGenTile channels of one token
+    int64_t tiles_per_line;    // tiles along the lane axis
+    int64_t n_tiles;
+};
+
 struct UpdParams {
     const uint16_t *x;
     int64_t x_sb, x_sd, x_st;
@@ -147,6 +167,29 @@ struct PagedParams {
     const int32_t *bt_rd;      // the block table, or query_start_loc when it is empty
 };
 
+// The paged step for any layout: strides and D offsets of any size, bases
+// aligned to their element size, 64-bit slot arithmetic.  A tile is one
+// token row of kGenTile channels of one stream; the streams' channel tiles
+// are numbered consecutively (PagedStream::slab0 is a stream's first).
+struct PagedGenParams {
+    PagedStream s[kMaxPagedStreams];
+    int32_t num_streams;
+    int64_t cols;              // channel tiles of all streams
+    uint16_t *cache;
+    int64_t c_sb, c_sh, c_sn;
+    int64_t num_blocks;
+    int32_t block_size;
+    const int64_t *pos;
+    const int64_t *slot;
+    const int32_t *qsl;
+    int32_t num_reqs;
+    const int32_t *bt;         // or null when no request has a table entry
+    int64_t bt_sr;
+    int32_t max_blocks;
+    int64_t T;
+    int64_t n_tiles;           // T * cols
+};
+
 // Launchers: each enqueues one kernel and returns hipGetLastError().
 hipError_t launch_fwd_tokmajor(const FwdTokParams &p, int width, bool silu, hipStream_t s);
 hipError_t launch_fwd_chanlast(const FwdClParams &p, int width, bool silu, hipStream_t s);
@@ -156,6 +199,9 @@ hipError_t launch_seq_metadata(const int32_t *qsl, int32_t num_reqs, int32_t num
                                hipStream_t s);
 hipError_t launch_paged_fused(const PagedParams &p, int width, bool silu, bool residual,
                               hipStream_t s);
+hipError_t launch_fwd_general(const FwdGenParams &p, int width, bool silu, hipStream_t s);
+hipError_t launch_paged_general(const PagedGenParams &p, int width, bool silu, bool residual,
+                                hipStream_t s);
 
 // Tile geometry used by both the host (grid sizes) and the kernels.
 constexpr int kWaveSize = 64;
@@ -175,5 +221,7 @@ constexpr int kPagedSlab = 256;                  // channels per paged wave (4 p
 // reached through one descriptor must span less than this many bytes.
 constexpr int64_t kMaxDescriptorSpan = int64_t(1) << 31;
 constexpr int kQslLdsMax = 2048;                 // qsl entries staged in LDS
+constexpr int kGenTile = 256;                    // lanes (one workgroup) per general-stride tile
+constexpr int64_t kGenMaxBlocks = int64_t(1) << 20;  // general-stride grid cap (tile loop beyond)
 
 }  // namespace sconv

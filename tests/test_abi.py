@@ -13,7 +13,7 @@ import causal_depthwise_short_conv1d_amd as S
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sconv.h")
 
-OK, ENULL, ESHAPE, ESTRIDE, EWIDTH, EALIAS, EALIGN, EARG = 0, -1, -2, -3, -4, -5, -6, -7
+OK, ENULL, ESHAPE, ESTRIDE, EWIDTH, EALIAS, EALIGN, EARG, ELAUNCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 # fake, well-aligned, non-overlapping "device" addresses: validation only
 # compares them, it never dereferences them.
@@ -67,7 +67,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert S.version() == (1, 3)
+    assert S.version() == (1, 4)
     for code in range(-8, 1):
         assert S.status_string(code) != "unknown status"
     assert S.status_string(-99) == "unknown status"
@@ -119,12 +119,21 @@ def test_fwd_nulls(lib):
 
 
 def test_fwd_strides_and_layouts(lib):
-    assert fwd(lib, wsd=3) == ESTRIDE          # weight rows narrower than width
-    assert fwd(lib, xst=2, xsd=2) == ESTRIDE   # neither storage class
-    assert fwd(lib, xst=60) == ESTRIDE         # channel-contiguous rows shorter than dim
-    assert fwd(lib, xst=68) == ESTRIDE         # row pitch not a multiple of 8
-    assert fwd(lib, osd=10, ost=1) == ESTRIDE  # out in the other storage class
+    # Any non-negative strides are accepted; layouts outside the vector
+    # kernels' storage classes take the general-stride kernel.  Here no GPU
+    # is visible, so an accepted call reaches the launch and fails there.
+    assert fwd(lib, wsd=3) == ELAUNCH          # overlapping weight rows: read-only, fine
+    assert fwd(lib, wsd=0) == ELAUNCH          # one set of taps broadcast to every channel
+    assert fwd(lib, xst=2, xsd=2) == ELAUNCH   # x elements shared between (c, t): read-only
+    assert fwd(lib, xst=60) == ELAUNCH         # overlapping input rows
+    assert fwd(lib, xst=68) == ELAUNCH         # row pitch not a multiple of 8
+    assert fwd(lib, osd=10, ost=1) == ELAUNCH  # out token-contiguous, x channel-contiguous
     assert fwd(lib, xsd=-1) == ESTRIDE
+    assert fwd(lib, wsd=-4) == ESTRIDE
+    assert fwd(lib, osd=1, ost=5) == ESTRIDE   # out rows overlap: two outputs, one address
+    assert fwd(lib, osd=0) == ESTRIDE          # every channel's output at one address
+    assert fwd(lib, csl=0) == ESTRIDE          # four state lines at one address
+    assert fwd(lib, csd=1, cst=1) == ESTRIDE   # state columns overlap the next channel's
 
 
 def test_fwd_state_shape(lib):
@@ -133,9 +142,15 @@ def test_fwd_state_shape(lib):
 
 
 def test_fwd_alignment(lib):
-    assert fwd(lib, x=ctypes.c_void_p(BASE + GB + 8)) == EALIGN
-    assert fwd(lib, out=ctypes.c_void_p(BASE + 8 * GB + 2)) == EALIGN
+    # bf16 tensors need 2-byte, index arrays 4-byte alignment; nothing more
+    assert fwd(lib, x=ctypes.c_void_p(BASE + GB + 8)) == ELAUNCH
+    assert fwd(lib, out=ctypes.c_void_p(BASE + 8 * GB + 2)) == ELAUNCH
+    assert fwd(lib, x=ctypes.c_void_p(BASE + GB + 1)) == EALIGN
+    assert fwd(lib, out=ctypes.c_void_p(BASE + 8 * GB + 3)) == EALIGN
     assert fwd(lib, w=ctypes.c_void_p(BASE + 2 * GB + 1)) == EALIGN
+    assert fwd(lib, cs=ctypes.c_void_p(BASE + 4 * GB + 1)) == EALIGN
+    assert fwd(lib, qsl=ctypes.c_void_p(BASE + 7 * GB + 2)) == EALIGN
+    assert fwd(lib, ci=ctypes.c_void_p(BASE + 5 * GB + 2)) == EALIGN
 
 
 def test_fwd_aliasing(lib):
@@ -167,9 +182,12 @@ def test_decode_validation(lib):
     assert upd(lib, batch=0, x=None) == OK
     assert upd(lib, cs=None) == ENULL
     assert upd(lib, ci=None, lines=1) == ESHAPE
-    assert upd(lib, wsd=2) == ESTRIDE
+    assert upd(lib, wsd=2) == ELAUNCH                                    # any weight stride
+    assert upd(lib, wsd=-1) == ESTRIDE
+    assert upd(lib, osd=0) == ESTRIDE                                    # outputs coincide
+    assert upd(lib, csl=2) == ESTRIDE                                    # state lines overlap
     assert upd(lib, out=ctypes.c_void_p(BASE + GB + 2)) == EALIAS        # partial overlap
-    assert upd(lib, out=addr(1), osd=2) == EALIAS                        # same base, other strides
+    assert upd(lib, out=addr(1), osd=2, osb=128) == EALIAS               # same base, other strides
     assert upd(lib, cs=ctypes.c_void_p(BASE + GB + 4)) == EALIAS
     assert upd(lib, x=ctypes.c_void_p(BASE + GB + 1)) == EALIGN
 
@@ -237,13 +255,21 @@ def test_paged_validation(lib):
     assert paged(lib, H=0) == ESHAPE
     assert paged(lib, bt=None) == ENULL
     assert paged(lib, slot=None) == ENULL
-    assert paged(lib, xst=4000) == ESTRIDE        # row shorter than C
-    assert paged(lib, ws=100, xst=3200, ost=3200) == EALIGN   # ws not a multiple of 8
-    assert paged(lib, off=4) == EALIGN
-    assert paged(lib, csn=500) == EALIGN
-    assert paged(lib, x=ctypes.c_void_p(BASE + GB + 8)) == EALIGN
-    assert paged(lib, nb=1 << 27) == ESHAPE       # 2^31 slots: beyond 32-bit slot arithmetic
-    assert paged(lib, mb=1 << 27, btsr=1 << 27) == ESHAPE   # positions past 2^31 in the table
+    assert paged(lib, ost=4000) == ESTRIDE        # output rows overlap
+    assert paged(lib, csn=500) == ESTRIDE         # slots overlap inside a head
+    assert paged(lib, csb=-1) == ESTRIDE
+    assert paged(lib, x=ctypes.c_void_p(BASE + GB + 1)) == EALIGN
+    assert paged(lib, pos=ctypes.c_void_p(BASE + 4 * GB + 4)) == EALIGN
+    assert paged(lib, bt=ctypes.c_void_p(BASE + 7 * GB + 2)) == EALIGN
+    # accepted (the general-stride kernel where the vector one does not fit):
+    # here no GPU is visible, so they fail at the launch
+    assert paged(lib, xst=4000) == ELAUNCH        # overlapping input rows: read-only
+    assert paged(lib, ws=100, xst=3200, ost=3200) == ELAUNCH   # ws not a multiple of 8
+    assert paged(lib, off=4) == ELAUNCH
+    assert paged(lib, csn=520, csh=16 * 520, csb=32 * 16 * 520) == ELAUNCH
+    assert paged(lib, x=ctypes.c_void_p(BASE + GB + 8)) == ELAUNCH
+    assert paged(lib, nb=1 << 27, c=addr(64)) == ELAUNCH       # 2^31 slots: 64-bit slots
+    assert paged(lib, mb=1 << 27, btsr=1 << 27) == ELAUNCH
     assert paged(lib, out=addr(1)) == EALIAS
     assert paged(lib, out=ctypes.c_void_p(BASE + 3 * GB + 1024)) == EALIAS   # out inside cache
 
@@ -301,4 +327,4 @@ def test_paged_multi_validation(lib):
     assert pmulti(lib, outs=[addr(20), addr(10)]) == EALIAS      # out over another x
     assert pmulti(lib, outs=[addr(20), addr(20)]) == EALIAS      # two outs coincide
     assert pmulti(lib, outs=[addr(20), addr(3)]) == EALIAS       # out over the cache
-    assert pmulti(lib, offs=(0, 132), wss=(128, 120)) == EALIGN  # off_s not a multiple of 8
+    assert pmulti(lib, offs=(0, 132), wss=(128, 120)) == ELAUNCH  # general kernel (no GPU here)

@@ -35,19 +35,23 @@ def run_fwd(d, activation="silu", out_fill=None, pad_slot_id=-1):
     return out, cs
 
 
-def p3_model_fp64(x, weight, bias, initial_state, activation):
-    """The benchmark page's reference forward, evaluated in float64."""
+def windowed_reference_fp64(x, weight, bias, history, activation):
+    """The forward that the benchmark page's reference implementation
+    defines (atrex-bench #003 "causal_conv1d", section "Reference
+    Implementation"), evaluated in float64 through torch's window view
+    instead of a convolution: with u = (the last width-1 state columns) ++ x,
+    output t of channel c is bias[c] + sum_j weight[c, j] * u[c, t + j],
+    followed by SiLU y * sigmoid(y)."""
     width = weight.shape[1]
-    seq = x.unsqueeze(0).double()
-    state = initial_state.double()
-    hist = state[:, :, state.shape[2] - (width - 1):]
-    seq_with_state = torch.cat([hist, seq], dim=-1)
-    out = F.conv1d(seq_with_state, weight.double().unsqueeze(1),
-                   None if bias is None else bias.double(), groups=weight.shape[0])
-    out = out[:, :, -x.shape[-1]:]
+    h = history[0].double()
+    u = torch.cat([h[:, h.shape[1] - (width - 1):], x.double()], dim=1)
+    win = u.unfold(1, width, 1)                     # win[c, t, j] = u[c, t + j]
+    y = (win * weight.double().unsqueeze(1)).sum(dim=-1)
+    if bias is not None:
+        y = y + bias.double().unsqueeze(1)
     if activation in ("silu", "swish"):
-        out = F.silu(out)
-    return out.squeeze(0)
+        y = y * torch.sigmoid(y)
+    return y
 
 
 @pytest.mark.parametrize("width", [2, 3, 4, 5])
@@ -60,7 +64,7 @@ def test_matches_benchmark_reference_in_fp64(width, T, activation, init):
         d["has_initial_state"] = torch.zeros(1, dtype=torch.bool)
     out, _ = run_fwd(d, activation)
     state = d["conv_states"] if init else torch.zeros_like(d["conv_states"])
-    ref = p3_model_fp64(d["x"], d["weight"], d["bias"], state, activation)
+    ref = windowed_reference_fp64(d["x"], d["weight"], d["bias"], state, activation)
     o = out.double()
     # the oracle's bf16 value must be the correctly rounded fp64 result
     assert torch.all((o - ref).abs() <= bf16_ulp_half(ref) * (1 + 1e-9))
@@ -363,7 +367,7 @@ def test_decode_single_token_matches_benchmark_reference():
     out = torch.empty_like(d["x"])
     st = d["conv_state"].clone()
     oracle.update_decode(d["x"], st, d["weight"], d["bias"], out, activation="silu")
-    ref = p3_model_fp64(d["x"][0], d["weight"], d["bias"], d["conv_state"], "silu")
+    ref = windowed_reference_fp64(d["x"][0], d["weight"], d["bias"], d["conv_state"], "silu")
     assert torch.all((out[0].double() - ref).abs() <= bf16_ulp_half(ref) * (1 + 1e-9))
     # state: shifted left by one with the new input at the end
     assert torch.equal(st[0, :, :2], d["conv_state"][0, :, 1:])
