@@ -27,14 +27,24 @@
  *   - bf16 tensors are passed as void* (IEEE bfloat16 bit patterns).  Index
  *     arrays are int32 (query_start_loc, cache_indices, block_table), int64
  *     (positions, slot_mapping) or bytes (has_initial_state, 0 = false).
- *   - Strides are in ELEMENTS and must be non-negative.
+ *   - Strides are in ELEMENTS and must be non-negative; any such view is
+ *     accepted (sliced, pitched, offset, transposed, broadcast inputs).  A
+ *     tensor the call WRITES (outputs, states, caches, saved windows) must
+ *     not have two elements at one address (else SCONV_ERR_STRIDE).  Pointers
+ *     need only their element's alignment: 2 bytes for bf16, 4 for int32,
+ *     8 for int64.  Layouts decide only the speed: each call documents the
+ *     ones its vector kernels take; every other layout runs a general-stride
+ *     kernel (one lane per element, 64-bit offsets) with the same results.
  *   - The library allocates nothing, never reads device memory on the host
  *     and never synchronises: each call validates its host arguments, then
- *     enqueues exactly one kernel on `stream` (NULL = the default stream) and
- *     returns.  Calls are therefore safe to capture in a HIP graph.
+ *     enqueues one kernel on `stream` (NULL = the default stream) and
+ *     returns (a token-contiguous forward of 2^32 or more elements enqueues
+ *     one kernel per channel group).  Calls are therefore safe to capture in
+ *     a HIP graph.
  *   - Return value: SCONV_OK, or a negative sconv_status.  On any error
- *     nothing is enqueued.  An empty problem (zero tokens, zero sequences)
- *     returns SCONV_OK without enqueueing anything.
+ *     other than SCONV_ERR_LAUNCH nothing is enqueued.  An empty problem
+ *     (zero tokens, zero sequences) returns SCONV_OK without enqueueing
+ *     anything.
  *   - Device data is not validated on the host (it is never read there).
  *     Kernels guard every data-dependent index: a cache line outside
  *     [0, num_cache_lines) skips its sequence, a block id outside
@@ -58,10 +68,10 @@ typedef enum sconv_status {
     SCONV_OK = 0,
     SCONV_ERR_NULL = -1,    /* a required pointer is NULL                       */
     SCONV_ERR_SHAPE = -2,   /* a size is negative, inconsistent or too large    */
-    SCONV_ERR_STRIDE = -3,  /* a layout the kernels do not take                 */
+    SCONV_ERR_STRIDE = -3,  /* a negative stride, or written elements overlap   */
     SCONV_ERR_WIDTH = -4,   /* width outside [SCONV_MIN_WIDTH, SCONV_MAX_WIDTH] */
     SCONV_ERR_ALIAS = -5,   /* an output overlaps an input it must not overlap  */
-    SCONV_ERR_ALIGN = -6,   /* a pointer / stride breaks a vector alignment     */
+    SCONV_ERR_ALIGN = -6,   /* a pointer not aligned to its element size        */
     SCONV_ERR_ARG = -7,     /* an enumerated argument (activation, ...) is bad  */
     SCONV_ERR_LAUNCH = -8   /* the HIP runtime refused the launch               */
 } sconv_status;
@@ -86,18 +96,23 @@ int sconv_version(void);
  * reference forward.
  *
  * x            logical [dim][total_tokens] bf16; element (c, t) at
- *              x[c*x_stride_dim + t*x_stride_tok].  Two storages are taken:
+ *              x[c*x_stride_dim + t*x_stride_tok], any strides.  The vector
+ *              kernels take two storages, when x and out are both in one of
+ *              them, 16-byte aligned, and w_stride_dim >= width:
  *                token-contiguous: x_stride_tok == 1 and
  *                  x_stride_dim == total_tokens (a compact (dim, T) array,
- *                  the benchmark page's layout; dim*total_tokens < 2^32);
+ *                  the benchmark page's layout);
  *                channel-contiguous: x_stride_dim == 1, x_stride_tok >= dim
  *                  and a multiple of 8 (the (T, dim) layout the tokenspeed
  *                  launcher requires).  With total_tokens == 1 the token
  *                  stride is ignored.
- *              x and out must be 16-byte aligned.
+ *              Any other layout (a slice x[:, a:b], a (T, dim) batch of
+ *              pitch dim with dim % 8 != 0, an offset view, out stored
+ *              unlike x, ...) takes the general-stride kernel.
  * weight       logical [dim][width] bf16, element (c, j) at
  *              weight[c*w_stride_dim + j] (unit width stride, as the page
- *              asserts).  w_stride_dim >= width.
+ *              asserts); w_stride_dim may be anything >= 0 (0 broadcasts one
+ *              set of taps to every channel).
  * bias         [dim] bf16, or NULL for no bias.
  * conv_states  logical [num_cache_lines][dim][width-1] bf16, element
  *              (l, c, k) at conv_states[l*cs_stride_line + c*cs_stride_dim
@@ -114,15 +129,17 @@ int sconv_version(void);
  * query_start_loc  [batch+1] int32 token offsets: 0, then the running sum of
  *              the lengths; the last entry must equal total_tokens.
  * activation   SCONV_ACT_NONE or SCONV_ACT_SILU ("silu" / "swish").
- * out          logical [dim][total_tokens] bf16 in the same storage class as
- *              x (strides o_stride_dim / o_stride_tok, same rules).  It must
- *              not overlap x or conv_states.  Rows of skipped sequences are
- *              left untouched.
+ * out          logical [dim][total_tokens] bf16 (strides o_stride_dim /
+ *              o_stride_tok).  Its address range must not overlap those of
+ *              x or conv_states.  Rows of skipped sequences are left
+ *              untouched.
  * Errors: NULL x/weight/query_start_loc/out (when there is work), or
  *   has_initial_state without conv_states -> SCONV_ERR_NULL; bad sizes,
  *   conv_states narrower than the lines cache_indices may not check ->
- *   SCONV_ERR_SHAPE; unsupported strides -> SCONV_ERR_STRIDE; alignment ->
- *   SCONV_ERR_ALIGN; overlap -> SCONV_ERR_ALIAS.
+ *   SCONV_ERR_SHAPE; a negative stride, or out / conv_states with two
+ *   elements at one address -> SCONV_ERR_STRIDE; a bf16 pointer not 2-byte
+ *   or an index array not 4-byte aligned -> SCONV_ERR_ALIGN; overlap ->
+ *   SCONV_ERR_ALIAS.
  */
 int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
                       const void *weight, int64_t w_stride_dim,
@@ -288,21 +305,23 @@ int sconv_seq_metadata(const int32_t *query_start_loc, int32_t num_reqs,
  * _seq_metadata_kernel is done inside the kernel from query_start_loc.
  *
  * x            [num_tokens][C] bf16, C = num_heads * ws, channel stride 1,
- *              row stride x_stride_tok (multiple of 8, >= C); head-major
- *              channels: channel c is head c / ws, cache D-index
- *              off_s + c % ws.
- * weight       [C][width] bf16 (unit width stride), bias [C] or NULL (the
- *              page has none).
+ *              row stride x_stride_tok (any); head-major channels: channel
+ *              c is head c / ws, cache D-index off_s + c % ws.
+ * weight       [C][width] bf16 (unit width stride, any row stride), bias
+ *              [C] or NULL (the page has none).
  * cache        [num_blocks][num_heads][block_size][head_dim] bf16 with unit
- *              D stride; strides c_stride_blk / c_stride_head /
- *              c_stride_slot (multiples of 8).  It holds the conv input of
- *              every absolute position: position p of request r lives in
- *              block block_table[r*bt_stride_req + p / block_size], slot
- *              p % block_size, D range [off_s, off_s + ws).
- *              Requires ws % 8 == 0, off_s % 8 == 0, off_s + ws <= head_dim,
- *              and num_blocks * block_size and max_blocks * block_size
- *              below 2^31 (slots and positions are resolved in 32-bit
- *              arithmetic), else SCONV_ERR_SHAPE.
+ *              D stride (the page asserts it; there is no D stride
+ *              argument); strides c_stride_blk / c_stride_head /
+ *              c_stride_slot, no two elements at one address.  It holds the
+ *              conv input of every absolute position: position p of request
+ *              r lives in block block_table[r*bt_stride_req + p /
+ *              block_size], slot p % block_size, D range [off_s, off_s + ws),
+ *              off_s + ws <= head_dim (else SCONV_ERR_SHAPE).
+ *              The vector kernel runs when ws, off_s, the row strides and
+ *              the cache strides are multiples of 8, x, out and the cache
+ *              are 16-byte aligned, and num_blocks * block_size and
+ *              max_blocks * block_size are below 2^31 (32-bit slot
+ *              arithmetic); other layouts take the general-stride kernel.
  * positions    [num_tokens] int64 absolute position of each row.
  * slot_mapping [num_tokens] int64 flat slot block*block_size + offset of
  *              each row; < 0 marks a pad row.
@@ -318,8 +337,9 @@ int sconv_seq_metadata(const int32_t *query_start_loc, int32_t num_reqs,
  * before the call (rows inside the forward are never read back from it),
  * which requires the blocks written by one request not to be read as
  * pre-forward taps by another.
- * out          [num_tokens][C] bf16 with row stride o_stride_tok; must not
- *              overlap x or the cache.
+ * out          [num_tokens][C] bf16 with row stride o_stride_tok (rows may
+ *              not overlap: o_stride_tok >= C when num_tokens > 1); its
+ *              address range must not overlap x or the cache.
  */
 int sconv_paged_fused(const void *x, int64_t x_stride_tok,
                       const void *weight, int64_t w_stride_dim,
