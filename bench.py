@@ -31,10 +31,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective HBM GB/s (% of peak) + tokens/s, bf16 causal conv1d dim 8192 width 4"
 HEADLINE = dict(dim=8192, T=14807, width=4)
-KERNEL_SOURCES = ["causal_depthwise_short_conv1d_amd/csrc/fwd_tokmajor.hip",
-                  "causal_depthwise_short_conv1d_amd/csrc/sconv_device.h",
-                  "causal_depthwise_short_conv1d_amd/csrc/sconv_params.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_tok_long_dim8192_T14807_traffic.json")
+CSRC = os.path.join(ROOT, "causal_depthwise_short_conv1d_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "workloads_traffic.json")
+HEADLINE_WORKLOAD = "long_T14807_dim_tok"
+PROFILE_REPS = 10          # timed launches per workload in a profile run (after one warm-up)
 
 
 def log(*a):
@@ -104,11 +104,171 @@ def graph_time_ms(fn, reps=100, replays=20):
 
 
 def kernel_hash():
+    """Hash of every kernel source: counter figures are reported only while
+    the kernels are the ones they were taken on."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """Per-workload HBM counter figures (profiles/workloads_traffic.json),
+    or {} when they were taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    tr = json.load(open(TRAFFIC_FILE))
+    return tr.get("workloads", {}) if tr.get("kernel_hash") == kernel_hash() else {}
+
+
+def varlen_bytes(d, width):
+    """Algorithmic bytes of a varlen batch: the processed sequences' tokens,
+    histories read where a sequence continues from its state, states written
+    for every processed non-empty sequence, and all index arrays."""
+    lens = d["lengths"].tolist()
+    lines = d["cache_indices"].tolist()
+    init = d["has_initial_state"].tolist()
+    kept = [l for l, c in zip(lens, lines) if c != -1]
+    n_init = sum(1 for l, c, h in zip(lens, lines, init) if c != -1 and h and l > 0)
+    n_state = sum(1 for l, c in zip(lens, lines) if c != -1 and l > 0)
+    dim = d["weight"].shape[0]
+    n_pad = len(lens) - len(kept)
+    return (fwd_bytes(dim, kept, width, n_init=n_init, n_state=n_state, cache_indices=True)
+            + 5 * n_pad), sum(kept)
+
+
+def workload_builders():
+    """Every benchmarked workload as (name, builder); builder(torch, S, W, dev)
+    returns (launch, algorithmic bytes, tokens).  The order is the order of a
+    profile run."""
+    def single(dim, T, layout):
+        def b(torch, S, W, dev):
+            d = W.single_sequence(dim=dim, T=T, width=4, seed=W.seed_for(3, T % 97),
+                                  device=dev, layout=layout)
+            out = torch.empty_like(d["x"])
+            fn = lambda: S.conv1d_fwd_varlen(d["x"], d["weight"], d["bias"], d["conv_states"],
+                                             d["query_start_loc"],
+                                             has_initial_state=d["has_initial_state"], out=out)
+            return fn, fwd_bytes(dim, [T], 4), T
+        return b
+
+    def varlen(width, layout):
+        def b(torch, S, W, dev):
+            d = W.varlen_batch(dim=8192, width=width, seed=W.seed_for(4, width), device=dev,
+                               layout=layout)
+            out = torch.empty_like(d["x"])
+            nb, toks = varlen_bytes(d, width)
+            fn = lambda: S.conv1d_fwd_varlen(d["x"], d["weight"], d["bias"], d["conv_states"],
+                                             d["query_start_loc"],
+                                             cache_indices=d["cache_indices"],
+                                             has_initial_state=d["has_initial_state"], out=out)
+            return fn, nb, toks
+        return b
+
+    def paged(n_streams):
+        def b(torch, S, W, dev):
+            cfg = {k: v for k, v in W.PAGED_MIXED.items() if k != "off_s"}
+            d = W.paged_multi_batch(seed=W.seed_for(5), device=dev, **cfg)
+            Tp, C = d["x"].shape
+            valid = int((d["slot_mapping"] >= 0).sum())
+            R = d["query_start_loc"].numel() - 1
+            outs = [torch.empty_like(x) for x in d["xs"]]
+            if n_streams == 1:
+                fn = lambda: S.sconv_paged_fused(d["x"], d["weight"], d["cache"], d["positions"],
+                                                 d["slot_mapping"], d["query_start_loc"],
+                                                 d["block_table"], W.PAGED_MIXED["off_s"],
+                                                 d["ws"], activation="silu", use_residual=True,
+                                                 out=outs[0])
+            else:
+                fn = lambda: S.sconv_paged_fused_multi(d["xs"], d["weights"], d["cache"],
+                                                       d["positions"], d["slot_mapping"],
+                                                       d["query_start_loc"], d["block_table"],
+                                                       d["offs"], d["ws"], activation="silu",
+                                                       use_residual=True, outs=outs)
+            return fn, paged_bytes(C, Tp, valid, R, cfg["width"], n_streams=n_streams), valid
+        return b
+
+    def decode(batch, dim):
+        def b(torch, S, W, dev):
+            d = W.decode_batch(batch=batch, dim=dim, width=4, seed=W.seed_for(2, 1 + (batch > 1)),
+                               num_lines=max(batch, 128 if batch > 1 else 1), device=dev)
+            xo = d["x"].clone()
+            fn = lambda: S.conv1d_update_decode(d["x"], d["conv_state"], d["weight"], d["bias"],
+                                                activation="silu",
+                                                cache_indices=d["cache_indices"], out=xo)
+            return fn, decode_bytes(batch, dim, 4), batch
+        return b
+
+    def verify(torch, S, W, dev):
+        cfg = W.SPEC_DECODE
+        d = W.spec_decode_batch(batch=cfg["batch"], dim=cfg["dim"], width=cfg["width"],
+                                seqlen=cfg["seqlen"], num_lines=cfg["num_lines"],
+                                n_pad=cfg["n_pad"], seed=W.seed_for(6, 0), mode="roll",
+                                device=dev)
+        so = torch.empty_like(d["x"])
+        fn = lambda: S.conv1d_update(d["x"], d["conv_state"], d["weight"], d["bias"],
+                                     activation="silu", cache_indices=d["cache_indices"],
+                                     num_accepted_tokens=d["num_accepted_tokens"], out=so)
+        live = cfg["batch"] - cfg["n_pad"]
+        return fn, spec_bytes(cfg["dim"], live, cfg["seqlen"], cfg["width"], 2 * cfg["batch"]), \
+            live * cfg["seqlen"]
+
+    out = [(HEADLINE_WORKLOAD, single(8192, 14807, "dim_tok")),
+           ("long_T14807_tok_dim", single(8192, 14807, "tok_dim"))]
+    for T in (4195, 11027):
+        for layout in ("dim_tok", "tok_dim"):
+            out.append((f"long_T{T}_{layout}", single(8192, T, layout)))
+    for width in (2, 3, 4, 5):
+        out.append((f"varlen_W{width}_tok_dim", varlen(width, "tok_dim")))
+    out.append(("varlen_W4_dim_tok", varlen(4, "dim_tok")))
+    out += [("paged_1stream", paged(1)), ("paged_4streams", paged(4)),
+            ("decode_1x4096", decode(1, 4096)), ("decode_64x8192", decode(64, 8192)),
+            ("verify_64x8192x4", verify)]
+    return out
+
+
+def decode_bytes(batch, dim, width):
+    """Algorithmic bytes of a decode step: per entry x read, out written, the
+    width-1 history read and rewritten, its line index; taps and bias once."""
+    return batch * (4 * dim + 4 * (width - 1) * dim + 4) + 2 * dim * width + 2 * dim
+
+
+def profile_set(reps, bytes_out=None):
+    """Every workload, one after another: a warm-up launch, then `reps`
+    launches each after a 1 GiB read (cold caches, as the benchmark times
+    them); three 256 MiB device copies first calibrate the HBM counters.
+    Run under rocprofv3 (kernel trace, or one counter pass) and turned into
+    the committed summaries by `bench.py summarize-set`."""
+    import torch
+    import causal_depthwise_short_conv1d_amd as S
+    import workloads as W
+    S.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    src = torch.empty(1 << 27, dtype=torch.bfloat16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    sizes = {}
+    for name, build in workload_builders():
+        fn, nb, _ = build(torch, S, W, dev)
+        sizes[name] = nb
+        fn()
+        for _ in range(reps):
+            torch.sum(scratch, dim=0, out=sink)
+            fn()
+        torch.cuda.synchronize()
+        log(f"[profile] {name}: {reps + 1} launches, {nb} algorithmic bytes each")
+        del fn
+        torch.cuda.empty_cache()
+    if bytes_out:
+        json.dump(sizes, open(bytes_out, "w"), indent=1)
 
 
 def event_time_ms(fn, reps, flush=None, stream=None):
@@ -136,7 +296,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--profile-set", action="store_true",
+                    help="run every workload PROFILE_REPS times for rocprofv3, print no JSON")
+    ap.add_argument("--bytes-out", default=None,
+                    help="with --profile-set: write each workload's algorithmic bytes here")
     args = ap.parse_args()
+    if args.profile_set:
+        profile_set(PROFILE_REPS, args.bytes_out)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -197,11 +364,9 @@ def main():
     torch.cuda.synchronize()
     del src, dst
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("kernel_hash") == kernel_hash():
-            traffic = tr.get("bytes_per_launch")
+    counters = load_traffic()
+    head_tr = counters.get(HEADLINE_WORKLOAD)
+    traffic = head_tr["traffic_bytes"] if head_tr else None
 
     result = {
         "metric": METRIC,
@@ -243,6 +408,21 @@ def extras(torch, S, W, dev):
     which evicts the caches and leaves no dirty lines to drain during the
     timed launch (median of the repetitions)."""
     ex = {}
+    counters = load_traffic()
+
+    def with_counters(entry, name, us):
+        """Add the workload's HBM counter figures (profiles/workloads_traffic.json,
+        taken on these kernel sources): counter bytes, their ratio to the
+        algorithmic bytes, and counter bytes over this run's time and over
+        the profile's kernel-only median."""
+        c = counters.get(name)
+        if c:
+            entry["counter_bytes"] = c["traffic_bytes"]
+            entry["counter_over_algorithmic"] = c["ratio"]
+            entry["achieved_GB/s"] = round(c["traffic_bytes"] / us / 1e3, 1)
+            entry["kernel_only_us"] = c["median_us"]
+            entry["achieved_GB/s_kernel_only"] = c["achieved_GBps"]
+        return entry
     scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
     sink = torch.empty((), dtype=torch.float32, device=dev)
     flush = lambda: torch.sum(scratch, dim=0, out=sink)
@@ -261,8 +441,9 @@ def extras(torch, S, W, dev):
                 fn()
                 ms = event_time_ms(fn, 15, flush)
                 nb = fwd_bytes(dim, [T], 4)
-                sweep[f"dim{dim}_T{T}_{layout}"] = {"us": round(ms * 1e3, 2),
-                                                    "GB/s": round(nb / ms / 1e6, 1)}
+                sweep[f"dim{dim}_T{T}_{layout}"] = with_counters(
+                    {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1)},
+                    f"long_T{T}_{layout}", ms * 1e3)
                 log(f"[bench] prefill dim{dim} T{T} {layout}: {ms*1e3:.2f} us {nb/ms/1e6:.0f} GB/s")
     ex["prefill_sweep"] = sweep
 
@@ -281,11 +462,11 @@ def extras(torch, S, W, dev):
         fn()
         torch.cuda.synchronize()
         lat.append(time.perf_counter() - t0)
-    dec_bytes = 4 * 4096 + 4 * 3 * 4096 + 2 * 4096 * 4 + 2 * 4096 + 4
-    ex["decode_dim4096_T1"] = {"graph_us_per_launch": round(warm * 1e3, 2),
-                               "cold_cache_us": round(cold * 1e3, 2),
-                               "host_latency_us_median": round(statistics.median(lat) * 1e6, 2),
-                               "bytes": dec_bytes}
+    dec_bytes = decode_bytes(1, 4096, 4)
+    ex["decode_dim4096_T1"] = with_counters(
+        {"graph_us_per_launch": round(warm * 1e3, 2), "cold_cache_us": round(cold * 1e3, 2),
+         "host_latency_us_median": round(statistics.median(lat) * 1e6, 2), "bytes": dec_bytes},
+        "decode_1x4096", cold * 1e3)
     log(f"[bench] decode dim4096 T1: {warm*1e3:.2f} us/launch in a graph, {cold*1e3:.2f} us "
         f"cold, host latency {statistics.median(lat)*1e6:.1f} us")
 
@@ -299,10 +480,10 @@ def extras(torch, S, W, dev):
     fn()
     cold = event_time_ms(fn, 50, flush)
     warm = graph_time_ms(fn)
-    nb = 64 * (4 * 8192 + 4 * 3 * 8192) + 2 * 8192 * 4 + 2 * 8192 + 4 * 64
-    ex["decode_64x8192_T1"] = {"graph_us_per_launch": round(warm * 1e3, 2),
-                               "cold_cache_us": round(cold * 1e3, 2), "bytes": nb,
-                               "GB/s_graph": round(nb / warm / 1e6, 1)}
+    nb = decode_bytes(64, 8192, 4)
+    ex["decode_64x8192_T1"] = with_counters(
+        {"graph_us_per_launch": round(warm * 1e3, 2), "cold_cache_us": round(cold * 1e3, 2),
+         "bytes": nb, "GB/s_graph": round(nb / warm / 1e6, 1)}, "decode_64x8192", cold * 1e3)
     log(f"[bench] decode 64x8192 T1: {warm*1e3:.2f} us/launch in a graph "
         f"({nb / warm / 1e6:.0f} GB/s), {cold*1e3:.2f} us cold")
 
@@ -321,9 +502,9 @@ def extras(torch, S, W, dev):
     warm = graph_time_ms(fn)
     live = cfg["batch"] - cfg["n_pad"]
     nb = spec_bytes(cfg["dim"], live, cfg["seqlen"], cfg["width"], 2 * cfg["batch"])
-    ex["spec_verify_64x8192_seqlen4"] = {"cold_cache_us": round(cold * 1e3, 2),
-                                         "graph_us_per_launch": round(warm * 1e3, 2),
-                                         "GB/s_cold": round(nb / cold / 1e6, 1), "bytes": nb}
+    ex["spec_verify_64x8192_seqlen4"] = with_counters(
+        {"cold_cache_us": round(cold * 1e3, 2), "graph_us_per_launch": round(warm * 1e3, 2),
+         "GB/s_cold": round(nb / cold / 1e6, 1), "bytes": nb}, "verify_64x8192x4", cold * 1e3)
     log(f"[bench] spec verify 64x8192x4: {cold*1e3:.2f} us cold ({nb/cold/1e6:.0f} GB/s), "
         f"{warm*1e3:.2f} us/launch in a graph")
     del d, so
@@ -336,14 +517,7 @@ def extras(torch, S, W, dev):
         d = W.varlen_batch(dim=8192, width=width, seed=W.seed_for(4, width), device=dev,
                            layout=layout)
         out = torch.empty_like(d["x"])
-        lens = d["lengths"].tolist()
-        lines = d["cache_indices"].tolist()
-        init = d["has_initial_state"].tolist()
-        kept = [l for l, c in zip(lens, lines) if c != -1]
-        n_init = sum(1 for l, c, h in zip(lens, lines, init) if c != -1 and h and l > 0)
-        n_state = sum(1 for l, c in zip(lens, lines) if c != -1 and l > 0)
-        nb = fwd_bytes(8192, kept, width, n_init=n_init, n_state=n_state,
-                       cache_indices=True) + 4 * (len(lens) - len(kept)) + (len(lens) - len(kept))
+        nb, toks = varlen_bytes(d, width)
         cs = d["conv_states"]
         fn = lambda: S.conv1d_fwd_varlen(d["x"], d["weight"], d["bias"], cs,
                                          d["query_start_loc"], cache_indices=d["cache_indices"],
@@ -351,8 +525,9 @@ def extras(torch, S, W, dev):
         fn()
         ms = event_time_ms(fn, 10, flush)
         key = f"W{width}" if layout == "tok_dim" else f"W{width}_{layout}"
-        vl[key] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
-                   "tokens": sum(kept), "tokens_per_s": round(sum(kept) / ms * 1e3, 1)}
+        vl[key] = with_counters({"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
+                                 "tokens": toks, "tokens_per_s": round(toks / ms * 1e3, 1)},
+                                f"varlen_W{width}_{layout}", ms * 1e3)
         log(f"[bench] varlen {key}: {ms*1e3:.1f} us {nb/ms/1e6:.0f} GB/s")
         del d, out, cs
     ex["varlen_64seq_dim8192"] = vl
@@ -371,8 +546,9 @@ def extras(torch, S, W, dev):
     fn()
     ms = event_time_ms(fn, 20, flush)
     nb = paged_bytes(C, Tp, valid, R, cfg["width"])
-    ex["paged_mixed_T4128_C4096"] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
-                                     "bytes": nb}
+    ex["paged_mixed_T4128_C4096"] = with_counters(
+        {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1), "bytes": nb},
+        "paged_1stream", ms * 1e3)
     log(f"[bench] paged: {ms*1e3:.1f} us {nb/ms/1e6:.0f} GB/s")
     fn = lambda: S.sconv_paged_fused_multi(d["xs"], d["weights"], d["cache"], d["positions"],
                                            d["slot_mapping"], d["query_start_loc"],
@@ -381,8 +557,9 @@ def extras(torch, S, W, dev):
     fn()
     ms = event_time_ms(fn, 20, flush)
     nb = paged_bytes(C, Tp, valid, R, cfg["width"], n_streams=len(d["xs"]))
-    ex["paged_mixed_4streams_T4128_C4096"] = {"us": round(ms * 1e3, 2),
-                                              "GB/s": round(nb / ms / 1e6, 1), "bytes": nb}
+    ex["paged_mixed_4streams_T4128_C4096"] = with_counters(
+        {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1), "bytes": nb},
+        "paged_4streams", ms * 1e3)
     log(f"[bench] paged 4 streams: {ms*1e3:.1f} us {nb/ms/1e6:.0f} GB/s")
     del d, outs
 
@@ -441,8 +618,8 @@ def summarize(argv):
     TRACE_DIR holds --kernel-trace --stats output, FETCH_DIR / WRITE_DIR the
     --pmc FETCH_SIZE / --pmc WRITE_SIZE passes of the same command.  The
     counters are scaled by what they read for the run's calibration copies
-    (the last three 256 MiB device copies).  Writes OUT_PREFIX.txt and, for
-    the headline kernel, the traffic JSON that the benchmark reports."""
+    (the last three 256 MiB device copies).  Writes OUT_PREFIX.txt (the
+    traffic figures the benchmark reports come from `summarize-set`)."""
     import csv
     import glob
     trace_dir, fetch_dir, write_dir, out_prefix, cmdline = argv[:5]
@@ -500,11 +677,6 @@ def summarize(argv):
               f"HBM traffic {traffic:.0f} B vs algorithmic {nbytes} B "
               f"({100 * (traffic / nbytes - 1):+.2f}%)"]
     open(out_prefix + ".txt", "w").write("\n".join(lines) + "\n")
-    json.dump({"kernel_hash": kernel_hash(), "bytes_per_launch": round(traffic),
-               "fetch_bytes": round(fetch * fr), "write_bytes": round(write * fw),
-               "fetch_calibration": round(fr, 4), "write_calibration": round(fw, 4),
-               "algorithmic_bytes": nbytes, "command": cmdline},
-              open(TRAFFIC_FILE, "w"), indent=1)
     print("\n".join(lines))
 
 
@@ -541,10 +713,121 @@ def summarize_trace(argv):
     print("\n".join(lines))
 
 
+def _profile_dispatches(d, counter=None):
+    """The libsconv dispatches of a profile run in launch order, assigned to
+    the workloads (each launched PROFILE_REPS + 1 times, in the order of
+    workload_builders), and the run's calibration copies.  With `counter`,
+    d holds one --pmc pass and each dispatch carries that counter's value in
+    bytes (the CSV gives KiB); else d holds a kernel trace and each dispatch
+    its duration in us."""
+    import csv
+    import glob
+    name = "*counter_collection.csv" if counter else "*kernel_trace.csv"
+    f = glob.glob(os.path.join(d, "**", name), recursive=True)
+    if not f:
+        raise SystemExit(f"no {name} under {d}")
+    rows = list(csv.DictReader(open(f[0])))
+    if counter:
+        rows = [r for r in rows if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        val = lambda r: float(r["Counter_Value"]) * 1024
+        grid = lambda r: int(r["Grid_Size"])
+    else:
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        val = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        grid = lambda r: int(r["Grid_Size_X"]) if "Grid_Size_X" in r else int(r["Grid_Size"])
+    calib = [val(r) for r in rows if "copyBuffer" in r["Kernel_Name"] and grid(r) == 131072][:3]
+    ours = [(r["Kernel_Name"], val(r)) for r in rows if "sconv::" in r["Kernel_Name"]]
+    names = [n for n, _ in workload_builders()]
+    per = PROFILE_REPS + 1
+    if len(ours) != per * len(names):
+        raise SystemExit(f"{d}: {len(ours)} libsconv dispatches, expected {per * len(names)}")
+    out = {}
+    for i, n in enumerate(names):
+        grp = ours[i * per:(i + 1) * per]
+        kern = {k for k, _ in grp}
+        if len(kern) != 1:
+            raise SystemExit(f"{d}: workload {n} ran several kernels: {kern}")
+        out[n] = (kern.pop(), [v for _, v in grp[1:]])      # the warm-up launch dropped
+    return out, calib
+
+
+def summarize_set(argv):
+    """Per-workload kernel time and HBM traffic from three rocprofv3 runs of
+    `bench.py --profile-set` (a kernel trace, a FETCH_SIZE pass and a
+    WRITE_SIZE pass), and optionally one pass of SQ counters:
+
+        python bench.py summarize-set BYTES_JSON TRACE_DIR FETCH_DIR WRITE_DIR SQ_DIR|- CMDLINE
+
+    The counters are scaled by what they read for the run's three 256 MiB
+    device copies (each reads and writes 268435456 bytes); BYTES_JSON is the
+    algorithmic byte count of every workload that the profile run wrote.
+    Writes profiles/workloads_counters.txt and profiles/workloads_traffic.json."""
+    import re
+    bytes_json, trace_dir, fetch_dir, write_dir, sq_dir, cmdline = argv[:6]
+    calib = float(1 << 28)
+    trace, _ = _profile_dispatches(trace_dir)
+    fetch, fcal = _profile_dispatches(fetch_dir, "FETCH_SIZE")
+    write, wcal = _profile_dispatches(write_dir, "WRITE_SIZE")
+    ff = calib / statistics.mean(fcal)
+    fw = calib / statistics.mean(wcal)
+    sq = {}
+    if sq_dir != "-":
+        import csv
+        import glob
+        f = glob.glob(os.path.join(sq_dir, "**", "*counter_collection.csv"), recursive=True)
+        rows = list(csv.DictReader(open(f[0])))
+        for cname in sorted({r["Counter_Name"] for r in rows}):
+            got, _ = _profile_dispatches(sq_dir, cname)
+            for n, (_, vals) in got.items():
+                sq.setdefault(n, {})[cname] = statistics.mean(vals) / 1024   # raw counts
+    alg = json.load(open(bytes_json))
+    lines = [f"# rocprofv3 per-workload summary: kernel-only time and HBM traffic of every "
+             f"benchmarked workload ({PROFILE_REPS} cold-cache launches each)",
+             f"# command: {cmdline}",
+             f"# kernel source hash: {kernel_hash()}",
+             f"# counters scaled by the run's 256 MiB device copies: FETCH_SIZE x {ff:.4f}, "
+             f"WRITE_SIZE x {fw:.4f}",
+             "",
+             "workload | kernel | median us | algorithmic MB | counter MB (fetch + write) | "
+             "counter / algorithmic | effective GB/s | achieved GB/s (counters) | % of 8 TB/s"]
+    result = {}
+    for n, (kern, durs) in trace.items():
+        med = statistics.median(durs)
+        fb = statistics.mean(fetch[n][1]) * ff
+        wb = statistics.mean(write[n][1]) * fw
+        nb = alg[n]
+        k = re.sub(r"\(.*", "", kern.replace("(anonymous namespace)::", "").replace("void ", ""))
+        result[n] = {"kernel": k, "median_us": round(med, 2), "algorithmic_bytes": nb,
+                     "fetch_bytes": round(fb), "write_bytes": round(wb),
+                     "traffic_bytes": round(fb + wb), "ratio": round((fb + wb) / nb, 4),
+                     "effective_GBps": round(nb / med / 1e3, 1),
+                     "achieved_GBps": round((fb + wb) / med / 1e3, 1)}
+        if n in sq:
+            result[n]["sq"] = {c: round(v, 1) for c, v in sq[n].items()}
+        lines.append(f"{n} | {k} | {med:.2f} | {nb / 1e6:.2f} | {fb / 1e6:.2f} + {wb / 1e6:.2f} | "
+                     f"{(fb + wb) / nb:.3f} | {nb / med / 1e3:.0f} | {(fb + wb) / med / 1e3:.0f} | "
+                     f"{100 * nb / med / 1e3 / HBM_PEAK_GBS:.1f}")
+    if sq:
+        cols = sorted({c for v in sq.values() for c in v})
+        lines += ["", "## SQ counters, mean per launch (raw counts)", "workload | " + " | ".join(cols)]
+        for n in trace:
+            lines.append(f"{n} | " + " | ".join(f"{sq.get(n, {}).get(c, float('nan')):.0f}"
+                                               for c in cols))
+    txt = os.path.join(ROOT, "profiles", "workloads_counters.txt")
+    open(txt, "w").write("\n".join(lines) + "\n")
+    json.dump({"kernel_hash": kernel_hash(), "command": cmdline,
+               "fetch_calibration": round(ff, 4), "write_calibration": round(fw, 4),
+               "workloads": result}, open(TRAFFIC_FILE, "w"), indent=1)
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "summarize":
         summarize(sys.argv[2:])
     elif len(sys.argv) > 1 and sys.argv[1] == "summarize-trace":
         summarize_trace(sys.argv[2:])
+    elif len(sys.argv) > 1 and sys.argv[1] == "summarize-set":
+        summarize_set(sys.argv[2:])
     else:
         main()
