@@ -456,19 +456,39 @@ def extras(torch, S, W, dev):
     fn()
     cold = event_time_ms(fn, 50, flush)
     warm = graph_time_ms(fn)
-    lat = []
-    for _ in range(1000):
-        t0 = time.perf_counter()
-        fn()
-        torch.cuda.synchronize()
-        lat.append(time.perf_counter() - t0)
+    # Enqueue-to-completion latency seen by a host caller, three ways: the
+    # Python binding with torch's synchronize; the binding with the HIP
+    # runtime's stream synchronize; and the library itself, called through
+    # a pre-bound launcher (arguments marshalled once) with the HIP stream
+    # synchronize -- the C call and the wait, without the binding.
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")               # the runtime torch has loaded
+    hip.hipStreamSynchronize.argtypes = [ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    bound = S.bind_update_decode(d["x"], d["conv_state"], d["weight"], d["bias"],
+                                 activation="silu", cache_indices=d["cache_indices"], out=xo)
+
+    def latency(call, sync):
+        ts = []
+        for _ in range(1000):
+            t0 = time.perf_counter()
+            call()
+            sync()
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts) * 1e6
+    lat = latency(fn, torch.cuda.synchronize)
+    lat_hip = latency(fn, lambda: hip.hipStreamSynchronize(stream))
+    lat_lib = latency(bound, lambda: hip.hipStreamSynchronize(stream))
     dec_bytes = decode_bytes(1, 4096, 4)
     ex["decode_dim4096_T1"] = with_counters(
         {"graph_us_per_launch": round(warm * 1e3, 2), "cold_cache_us": round(cold * 1e3, 2),
-         "host_latency_us_median": round(statistics.median(lat) * 1e6, 2), "bytes": dec_bytes},
+         "host_latency_us_median": round(lat, 2),
+         "host_latency_us_median_hip_sync": round(lat_hip, 2),
+         "library_latency_us_median": round(lat_lib, 2), "bytes": dec_bytes},
         "decode_1x4096", cold * 1e3)
     log(f"[bench] decode dim4096 T1: {warm*1e3:.2f} us/launch in a graph, {cold*1e3:.2f} us "
-        f"cold, host latency {statistics.median(lat)*1e6:.1f} us")
+        f"cold; host latency {lat:.1f} us (binding + torch sync), {lat_hip:.1f} us (binding + "
+        f"HIP sync), {lat_lib:.1f} us (pre-bound C call + HIP sync)")
 
     # decode at a serving batch: 64 entries x dim 8192, one token each
     d = W.decode_batch(batch=64, dim=8192, width=4, seed=W.seed_for(2, 2), num_lines=128,

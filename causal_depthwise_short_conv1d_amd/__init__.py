@@ -14,6 +14,7 @@ Entry points (same names as the C ABI):
   sconv_paged_fused    -- paged sliding-window cache insert + conv
   sconv_paged_fused_multi -- several conv streams sharing one paged cache
   sconv_seq_metadata   -- per-token (request, first row) buffers
+bind_update_decode marshals a decode step once for repeated launches.
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ import os
 import torch
 
 __all__ = ["conv1d_fwd_varlen", "conv1d_update_decode", "conv1d_update", "sconv_paged_fused",
-           "sconv_paged_fused_multi", "sconv_seq_metadata", "new_output",
+           "sconv_paged_fused_multi", "sconv_seq_metadata", "new_output", "bind_update_decode",
            "SconvError", "library_path", "load_library", "exported_symbols",
            "version", "status_string"]
 
@@ -140,7 +141,15 @@ def _act(activation) -> int:
     raise ValueError(f"unsupported activation {activation!r}")
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device) -> ctypes.c_void_p:
+    """The current stream of `device` as a raw handle (torch's accessor when
+    it has one: no Stream object per call)."""
+    if _raw_stream is not None:
+        return ctypes.c_void_p(_raw_stream(device.index if device.index is not None
+                                           else torch.cuda.current_device()))
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
@@ -148,6 +157,17 @@ def _call(fn: str, *args) -> None:
     rc = getattr(load_library(), fn)(*args)
     if rc != 0:
         raise SconvError(fn, rc)
+
+
+def _launch(fn: str, dev, args) -> None:
+    """Call `fn` with the current stream of `dev` appended, with `dev` made
+    the current device for the call (the library launches on the current
+    device) unless it already is."""
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        _call(fn, *args, _stream(dev))
+    else:
+        with torch.cuda.device(dev):
+            _call(fn, *args, _stream(dev))
 
 
 def new_output(x: torch.Tensor) -> torch.Tensor:
@@ -201,8 +221,7 @@ def conv1d_fwd_varlen(x, weight, bias, conv_states, query_start_loc,
         batch, total, dim, width, _act(activation), pad_slot_id,
         _dev(out, bf, "out", dev), out.stride(0), out.stride(1),
     )
-    with torch.cuda.device(dev):
-        _call("conv1d_fwd_varlen", *args, _stream(dev))
+    _launch("conv1d_fwd_varlen", dev, args)
     return out
 
 
@@ -239,11 +258,53 @@ def conv1d_update_decode(x, conv_state, weight, bias=None, activation=None,
         batch, dim, seqlen, width, _act(activation), pad_slot_id,
         _dev(ov, bf, "out", dev), *ov.stride(),
     )
-    with torch.cuda.device(dev):
-        _call("conv1d_update_decode", *args, _stream(dev))
+    _launch("conv1d_update_decode", dev, args)
     if out is not None:
         return out
     return ov.squeeze(-1) if squeeze else ov
+
+
+def bind_update_decode(x, conv_state, weight, bias=None, activation=None, cache_indices=None,
+                       pad_slot_id: int = -1, out=None, stream=None):
+    """A pre-bound conv1d_update_decode for a caller that launches the same
+    decode step over and over on fixed buffers (a serving loop): the tensors
+    are checked and marshalled once, here, and the returned function only
+    enqueues the launch on `stream` (default: the current stream of x's
+    device now) and raises on a non-zero status.  out=None computes in
+    place (x is overwritten, as the page's update does).  The tensors must
+    stay alive and in place while the function is used."""
+    dev = x.device
+    squeeze = x.dim() == 2
+    xv = x.unsqueeze(-1) if squeeze else x
+    ov = xv if out is None else (out.unsqueeze(-1) if out.dim() == 2 else out)
+    batch, dim, seqlen = xv.shape
+    width = weight.shape[1]
+    if weight.dim() != 2 or weight.shape[0] != dim or weight.stride(1) != 1:
+        raise ValueError("weight must be (dim, width) with unit width stride")
+    if conv_state.dim() != 3 or conv_state.shape[1] != dim or conv_state.shape[2] != width - 1:
+        raise ValueError("conv_state must be (lines, dim, width-1)")
+    if bias is not None and (bias.shape != (dim,) or bias.stride(0) != 1):
+        raise ValueError("bias must be a contiguous (dim,) tensor")
+    if ov.shape != xv.shape:
+        raise ValueError("out must have x's shape")
+    bf = torch.bfloat16
+    st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(dev)
+    args = (
+        _dev(xv, bf, "x", dev), *xv.stride(),
+        _dev(weight, bf, "weight", dev), weight.stride(0),
+        _dev(bias, bf, "bias", dev),
+        _dev(conv_state, bf, "conv_state", dev), *conv_state.stride(), conv_state.shape[0],
+        _index(cache_indices, torch.int32, "cache_indices", dev, batch),
+        batch, dim, seqlen, width, _act(activation), pad_slot_id,
+        _dev(ov, bf, "out", dev), *ov.stride(), st,
+    )
+    f = load_library().conv1d_update_decode
+
+    def launch():
+        rc = f(*args)
+        if rc != 0:
+            raise SconvError("conv1d_update_decode", rc)
+    return launch
 
 
 def conv1d_update(x, conv_state, weight, bias=None, activation=None, cache_indices=None,
@@ -298,8 +359,7 @@ def conv1d_update(x, conv_state, weight, bias=None, activation=None, cache_indic
         batch, dim, seqlen, width, _act(activation), pad_slot_id,
         _dev(ov, bf, "out", dev), *ov.stride(),
     )
-    with torch.cuda.device(dev):
-        _call("conv1d_update", *args, _stream(dev))
+    _launch("conv1d_update", dev, args)
     if out is not None:
         return out
     return ov.squeeze(-1) if squeeze else ov
@@ -347,8 +407,7 @@ def sconv_paged_fused(x, weight, cache, positions, slot_mapping, query_start_loc
         T, width, _act(activation), int(bool(use_residual)),
         _dev(out, bf, "out", dev), out.stride(0),
     )
-    with torch.cuda.device(dev):
-        _call("sconv_paged_fused", *args, _stream(dev))
+    _launch("sconv_paged_fused", dev, args)
     return out
 
 
@@ -368,8 +427,7 @@ def sconv_seq_metadata(query_start_loc, num_reqs: int, num_actual_tokens: int,
         _dev(seq_idx_out, torch.int32, "seq_idx_out", dev), seq_idx_out.numel(),
         _dev(query_start_out, torch.int32, "query_start_out", dev), query_start_out.numel(),
     )
-    with torch.cuda.device(dev):
-        _call("sconv_seq_metadata", *args, _stream(dev))
+    _launch("sconv_seq_metadata", dev, args)
 
 
 def sconv_paged_fused_multi(xs, weights, cache, positions, slot_mapping, query_start_loc,
@@ -428,6 +486,5 @@ def sconv_paged_fused_multi(xs, weights, cache, positions, slot_mapping, query_s
         block_table.shape[1] if block_table.dim() == 2 else 0,
         T, width, _act(activation), int(bool(use_residual)),
     )
-    with torch.cuda.device(dev):
-        _call("sconv_paged_fused_multi", *args, _stream(dev))
+    _launch("sconv_paged_fused_multi", dev, args)
     return outs

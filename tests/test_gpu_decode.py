@@ -119,3 +119,24 @@ def test_decode_equals_forward_on_gpu():
     torch.cuda.synchronize()
     assert_bits(o1[0], o2, "decode vs fwd out")
     assert_bits(st1, st2, "decode vs fwd state")
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_bound_decode_equals_the_call(in_place):
+    """bind_update_decode marshals once and then launches exactly what
+    conv1d_update_decode launches: outputs and states bit-identical over
+    repeated steps, in place and out of place."""
+    d = W.decode_batch(batch=5, dim=520, width=4, seed=577, num_lines=8, n_pad=1)
+    x = d["x"].to(DEV)
+    w, b, ci = d["weight"].to(DEV), d["bias"].to(DEV), d["cache_indices"].to(DEV)
+    st_a, st_b = d["conv_state"].to(DEV), d["conv_state"].to(DEV)
+    xa, xb = x.clone(), x.clone()
+    oa = xa if in_place else torch.full_like(x, -3.0)
+    ob = xb if in_place else torch.full_like(x, -3.0)
+    launch = S.bind_update_decode(xb, st_b, w, b, activation="silu", cache_indices=ci, out=ob)
+    for step in range(3):
+        S.conv1d_update_decode(xa, st_a, w, b, activation="silu", cache_indices=ci, out=oa)
+        launch()
+        torch.cuda.synchronize()
+        assert_bits(ob, oa, f"bound decode step {step} out")
+        assert_bits(st_b, st_a, f"bound decode step {step} state")
