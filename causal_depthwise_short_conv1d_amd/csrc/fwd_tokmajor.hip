@@ -277,6 +277,14 @@ __device__ void slow_chunk(const FwdTokParams &p, const int32_t *qsl, uint32_t i
     }
 }
 
+// Tap k of a PairTaps as fp32.
+template <int W>
+__device__ __forceinline__ float tap_of(const PairTaps<W> &t, int k) {
+    if ((W & 1) && k == W - 1) return t.wl;
+    const uint32_t pr = t.wp[k >> 1];
+    return (k & 1) ? bf_hi(pr) : bf_lo(pr);
+}
+
 // Channel c's taps and bias through the scalar cache (with no bias the
 // stand-in read is masked to 0).
 template <int W>
@@ -296,10 +304,13 @@ __device__ __forceinline__ PairTaps<W> sload_pair_taps(const FwdTokParams &p, ui
 // rows' taps are wave-uniform values read with scalar loads issued right
 // after the wave's x loads, so they complete under them; the head chunks are
 // computed in registers and one lane writes the new state after the wave's
-// reads.  Only three rare cases fall back to the element path: the ragged
-// last chunk, and a head whose first width-1 tokens cross into the next wave
-// (its owner computes them element by element and the next wave's first
-// chunk skips them).
+// reads.  A head belongs to the wave that holds its last history-reading
+// token, so a head that straddles two waves is computed by the second one,
+// from its 4-element halo and the history; the first leaves those elements
+// alone.  No wave waits on a second round trip for these rare heads (an
+// element path with several dependent loads made a few waves the tail of
+// the grid).  Only the ragged last chunk of the array and a sequence that
+// does not cover every token take the element path.
 template <int W, bool SILU, int ROUNDS>
 __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(FwdTokParams p) {
     constexpr uint32_t kCPW = ROUNDS * kWaveSize;           // chunks per wave
@@ -345,14 +356,21 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
     const uint32_t e_last = (e_first + kWE <= p.n_elems ? e_first + kWE : p.n_elems) - 1;
     const uint32_t cA = p.divT.div(e_first);
     const uint32_t row_a = cA * T, row_end = row_a + T;
+    // The wave owns the head of a row (its first width-1 tokens, the ones
+    // that read the history) when it holds the head's last token: row cA's
+    // head when the wave starts at most width-2 tokens into the row (those
+    // first tokens are then in the wave's 4-element halo), or row cA+1's
+    // head when it ends inside the wave.  A head of row cA+1 that runs past
+    // the wave's end belongs to the next wave: this wave leaves its first
+    // tokens alone.
     uint32_t hp = kNone, R = 0;
-    if (e_first == row_a) { hp = e_first; R = cA; }
-    else if (row_end <= e_last) { hp = row_end; R = cA + 1; }
-    const bool cross = hp != kNone && uint64_t(hp) + (H - 1) > e_last;
-    const bool lead_owned = H >= 2 && e_first > row_a && e_first - row_a <= uint32_t(H - 1);
+    if (e_first - row_a <= uint32_t(H - 1)) { hp = row_a; R = cA; }
+    else if (uint64_t(row_end) + (H - 1) <= e_last) { hp = row_end; R = cA + 1; }
+    const bool next_head = row_end <= e_last && uint64_t(row_end) + (H - 1) > e_last;
+    const uint32_t lead = hp < e_first ? e_first - hp : 0u;  // head tokens before the wave
     const PairTaps<W> tA = sload_pair_taps<W>(p, cA);
     const PairTaps<W> tB = sload_pair_taps<W>(p, cA + 1 < uint32_t(p.dim) ? cA + 1 : cA);
-    const bool own_head = simple && hp != kNone && !cross && !skip;
+    const bool own_head = simple && hp != kNone && !skip;
     const PairTaps<W> &t_head = (R == cA) ? tA : tB;
     // Waves that hold a row head also read its history (the cached state,
     // read by this wave only) and the row's last width-1 inputs (the new
@@ -400,8 +418,9 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
         const uint32_t chunk = wbase + r * kWaveSize + lane;
         const uint32_t i0 = chunk * kVec;
         const bool at_head = hp != kNone && i0 + kVec > hp && i0 <= hp + (H - 1);
-        const bool is_slow = !simple || chunk >= n_full || (lead_owned && r == 0 && lane == 0) ||
-                             (at_head && cross);
+        const bool is_slow = !simple || chunk >= n_full;
+        // the chunk that holds the start of the next wave's head
+        const bool cut = next_head && i0 <= row_end && row_end < i0 + kVec;
         Window win;
         win.d[0] = hz[r];
         win.d[1] = hw[r];
@@ -419,8 +438,57 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
             asm volatile("");                               // keeps this a branch, not a select
             if (at_head) o = head_merge<W, SILU>(o, win, i0, hp, t_head, hb);
         }
-        __builtin_amdgcn_raw_buffer_store_b128(o, outr, mine && !is_slow ? uint32_t(r * kWaveSize + lane) * 16u : kOob,
+        __builtin_amdgcn_raw_buffer_store_b128(o, outr,
+                                               mine && !is_slow && !cut ? uint32_t(r * kWaveSize + lane) * 16u
+                                                                        : kOob,
                                                0, kNt);
+        if (next_head) {                                    // wave-uniform
+            asm volatile("");
+            if (cut && mine && !is_slow) {
+                // the elements before the next wave's head, one by one
+                const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                for (int j = 0; j < kVec - 1; ++j)
+                    if (i0 + uint32_t(j) < row_end)
+                        p.out[size_t(i0) + j] = uint16_t((ov[j >> 1] >> ((j & 1) * 16)) & 0xffffu);
+            }
+        }
+    }
+    // Head tokens before the wave (in its halo): their outputs from the
+    // history and the halo, by one lane.
+    if (own_head && lead > 0 && lane == 0) {
+        const uint64_t hv = pack_hist<H>(hb);
+        // e[m] of the halo: x[e_first - 4 + m], m < 4
+        const uint32_t hz0 = hz[0], hw0 = hw[0];
+        auto halo = [&](int m) {                            // m compile-time, 0..3
+            const uint32_t d = m < 2 ? hz0 : hw0;
+            return (d >> (16 * (m & 1))) & 0xffffu;
+        };
+#pragma unroll
+        for (int j = 0; j < H - 1; ++j) {
+            if (uint32_t(j) < lead) {
+                // output of head token j: u[j + k], u = history ++ row, where
+                // row token n (< lead) is halo element 4 - lead + n
+                float acc = t_head.b;
+#pragma unroll
+                for (int k = 0; k < W; ++k) {
+                    const int m = j + k;                    // compile-time
+                    uint32_t bits;
+                    if (m < H) {
+                        bits = hist_bits<H>(hv, m - H);
+                    } else {
+                        const int n = m - H;                // row token, n <= j < lead
+                        bits = 0;
+#pragma unroll
+                        for (int ld = 1; ld < H; ++ld)      // lead is 1..H-1 (runtime)
+                            if (uint32_t(ld) == lead && 4 - ld + n >= 0 && 4 - ld + n < 4)
+                                bits = halo(4 - ld + n < 0 ? 0 : (4 - ld + n > 3 ? 3 : 4 - ld + n));
+                    }
+                    acc = __builtin_fmaf(tap_of<W>(t_head, k), bf_one(uint16_t(bits)), acc);
+                }
+                p.out[size_t(hp) + j] = to_bf16(act<SILU>(acc));
+            }
+        }
     }
     // One lane replaces the history this wave read with the row's last
     // width-1 inputs.
@@ -432,14 +500,6 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
 #pragma unroll 1
     for (int r = 0; r < ROUNDS; ++r)
         if (slow & (1u << r)) slow_chunk<W, SILU>(p, p.sb.qsl, (wbase + r * kWaveSize + lane) * kVec);
-}
-
-// Tap k of a PairTaps as fp32.
-template <int W>
-__device__ __forceinline__ float tap_of(const PairTaps<W> &t, int k) {
-    if ((W & 1) && k == W - 1) return t.wl;
-    const uint32_t pr = t.wp[k >> 1];
-    return (k & 1) ? bf_hi(pr) : bf_lo(pr);
 }
 
 // Taps of channel row `lr` of a wave-local weight descriptor (row pitch
