@@ -359,18 +359,17 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
     // The wave owns the head of a row (its first width-1 tokens, the ones
     // that read the history) when it holds the head's last token: row cA's
     // head when the wave starts at most width-2 tokens into the row (those
-    // first tokens are then in the wave's 4-element halo), or row cA+1's
-    // head when it ends inside the wave.  A head of row cA+1 that runs past
-    // the wave's end belongs to the next wave: this wave leaves its first
-    // tokens alone.
+    // first tokens then lie just before the wave), or row cA+1's head when
+    // it ends inside the wave.  A head of row cA+1 that runs past the wave's
+    // end belongs to the next wave: this wave leaves its first tokens alone.
     uint32_t hp = kNone, R = 0;
     if (e_first - row_a <= uint32_t(H - 1)) { hp = row_a; R = cA; }
     else if (uint64_t(row_end) + (H - 1) <= e_last) { hp = row_end; R = cA + 1; }
     const bool next_head = row_end <= e_last && uint64_t(row_end) + (H - 1) > e_last;
-    const uint32_t lead = hp < e_first ? e_first - hp : 0u;  // head tokens before the wave
     const PairTaps<W> tA = sload_pair_taps<W>(p, cA);
     const PairTaps<W> tB = sload_pair_taps<W>(p, cA + 1 < uint32_t(p.dim) ? cA + 1 : cA);
-    const bool own_head = simple && hp != kNone && !skip;
+    const bool live = !skip;                                // padded sequence: nothing to do
+    const bool own_head = simple && hp != kNone && live;
     const PairTaps<W> &t_head = (R == cA) ? tA : tB;
     // Waves that hold a row head also read its history (the cached state,
     // read by this wave only) and the row's last width-1 inputs (the new
@@ -394,7 +393,36 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
     for (int k = 0; k < H; ++k) pin_sgpr(hb[k]);
 #pragma unroll
     for (int i = 0; i < H / 2 + 1; ++i) pin_sgpr(nh.d[i]);
-    const bool live = !skip;                                // padded sequence: nothing to do
+
+    // The elements around a row boundary are computed one per lane after
+    // the rounds, and the chunks that hold them are not stored by the
+    // rounds.  Span A: the chunks that hold the wave's own head (from the
+    // head itself when it starts just before the wave), at most 16
+    // elements, for lanes 0..15.  Span B: the start of the chunk that holds
+    // the next wave's head, up to that head (1..7 elements), for lanes
+    // 16..23.  Each of these lanes reads its element's width inputs with
+    // 2-byte loads issued here, under the x loads.
+    const uint32_t fa0 = own_head ? (hp < e_first ? hp : hp & ~uint32_t(kVec - 1)) : 0u;
+    const uint32_t fa1 = own_head ? ((hp + (H - 1)) & ~uint32_t(kVec - 1)) + kVec : 0u;
+    const uint32_t fb0 = row_end & ~uint32_t(kVec - 1);
+    const uint32_t nb = (next_head && simple && live) ? row_end - fb0 : 0u;
+    const bool in_a = lane < 16;
+    const uint32_t fe = in_a ? fa0 + uint32_t(lane) : fb0 + uint32_t(lane - 16);
+    const bool fvalid = in_a ? fe < fa1 : uint32_t(lane - 16) < nb;
+    // span offsets are relative to 8 elements before the wave
+    const uint32_t xb = e_first >= kVec ? e_first - kVec : 0u;
+    const Rsrc xfr = make_rsrc(p.x + xb, int64_t(p.n_elems - xb) * 2);
+    const Rsrc ofr = make_rsrc(p.out + xb, int64_t(p.n_elems - xb) * 2);
+    uint32_t fx[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const int64_t pos = int64_t(fe) - H + k;
+        fx[k] = buf_ld16(xfr, fvalid && pos >= int64_t(xb) ? uint32_t(pos - xb) * 2u : kOob);
+    }
+    // chunks (relative to the wave) the rounds leave to the lanes above
+    const uint32_t sa0 = fa0 < e_first ? 0u : fa0 / kVec - wbase;
+    const uint32_t na = fa1 > fa0 ? (fa1 - 1) / kVec - wbase + 1 - sa0 : 0u;
+    const uint32_t sbr = nb ? fb0 / kVec - wbase : kNone;
 
     // Halo of every round first (each permute waits only for its own load).
     const int src_lane = (lane + kWaveSize - 1) & (kWaveSize - 1);
@@ -409,18 +437,16 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
         prev_w = rw;
     }
 
-    // Chunks computed and stored round by round; the (at most two) chunks of
-    // the row head take the history in place of the previous row's inputs.
-    // Element-path chunks are only marked here.
+    // Chunks computed and stored round by round.  Element-path chunks are
+    // only marked here.
     uint32_t slow = 0;
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
-        const uint32_t chunk = wbase + r * kWaveSize + lane;
+        const uint32_t rel = uint32_t(r * kWaveSize + lane);
+        const uint32_t chunk = wbase + rel;
         const uint32_t i0 = chunk * kVec;
-        const bool at_head = hp != kNone && i0 + kVec > hp && i0 <= hp + (H - 1);
         const bool is_slow = !simple || chunk >= n_full;
-        // the chunk that holds the start of the next wave's head
-        const bool cut = next_head && i0 <= row_end && row_end < i0 + kVec;
+        const bool spanned = rel - sa0 < na || rel == sbr;
         Window win;
         win.d[0] = hz[r];
         win.d[1] = hw[r];
@@ -431,64 +457,35 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
         // Every lane computes its chunk and stores it through a descriptor
         // (a lane with nothing to store writes past its end): no branch
         // stands between the wave's loads and the taps' first use.
-        u32x4 o = fast_chunk<W, SILU>(win, select(i0 >= row_end, tB, tA));
+        const u32x4 o = fast_chunk<W, SILU>(win, select(i0 >= row_end, tB, tA));
         const bool mine = live && chunk < p.n_chunks;
         if (mine && is_slow) slow |= 1u << r;
-        if (own_head) {                                     // wave-uniform: a row head is here
-            asm volatile("");                               // keeps this a branch, not a select
-            if (at_head) o = head_merge<W, SILU>(o, win, i0, hp, t_head, hb);
-        }
         __builtin_amdgcn_raw_buffer_store_b128(o, outr,
-                                               mine && !is_slow && !cut ? uint32_t(r * kWaveSize + lane) * 16u
-                                                                        : kOob,
+                                               mine && !is_slow && !spanned ? rel * 16u : kOob,
                                                0, kNt);
-        if (next_head) {                                    // wave-uniform
-            asm volatile("");
-            if (cut && mine && !is_slow) {
-                // the elements before the next wave's head, one by one
-                const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-                for (int j = 0; j < kVec - 1; ++j)
-                    if (i0 + uint32_t(j) < row_end)
-                        p.out[size_t(i0) + j] = uint16_t((ov[j >> 1] >> ((j & 1) * 16)) & 0xffffu);
-            }
-        }
     }
-    // Head tokens before the wave (in its halo): their outputs from the
-    // history and the halo, by one lane.
-    if (own_head && lead > 0 && lane == 0) {
+    // The spanned elements, one per lane: the head's taps from the head on
+    // (its first width-1 tokens read the history in place of the previous
+    // row), the previous row's taps before it.  The same pairwise
+    // accumulation as the rounds.
+    if (own_head || nb != 0) {                              // wave-uniform
+        asm volatile("");
+        const bool head_side = in_a && fe >= hp;
+        const PairTaps<W> tf = select(head_side, t_head, tA);
         const uint64_t hv = pack_hist<H>(hb);
-        // e[m] of the halo: x[e_first - 4 + m], m < 4
-        const uint32_t hz0 = hz[0], hw0 = hw[0];
-        auto halo = [&](int m) {                            // m compile-time, 0..3
-            const uint32_t d = m < 2 ? hz0 : hw0;
-            return (d >> (16 * (m & 1))) & 0xffffu;
-        };
+        uint32_t u[W];
 #pragma unroll
-        for (int j = 0; j < H - 1; ++j) {
-            if (uint32_t(j) < lead) {
-                // output of head token j: u[j + k], u = history ++ row, where
-                // row token n (< lead) is halo element 4 - lead + n
-                float acc = t_head.b;
-#pragma unroll
-                for (int k = 0; k < W; ++k) {
-                    const int m = j + k;                    // compile-time
-                    uint32_t bits;
-                    if (m < H) {
-                        bits = hist_bits<H>(hv, m - H);
-                    } else {
-                        const int n = m - H;                // row token, n <= j < lead
-                        bits = 0;
-#pragma unroll
-                        for (int ld = 1; ld < H; ++ld)      // lead is 1..H-1 (runtime)
-                            if (uint32_t(ld) == lead && 4 - ld + n >= 0 && 4 - ld + n < 4)
-                                bits = halo(4 - ld + n < 0 ? 0 : (4 - ld + n > 3 ? 3 : 4 - ld + n));
-                    }
-                    acc = __builtin_fmaf(tap_of<W>(t_head, k), bf_one(uint16_t(bits)), acc);
-                }
-                p.out[size_t(hp) + j] = to_bf16(act<SILU>(acc));
-            }
+        for (int k = 0; k < W; ++k) {
+            const uint32_t hi = fe - hp + uint32_t(k);      // history index when < H
+            const uint32_t hbits = uint32_t(hv >> (16 * (hi < uint32_t(H) ? hi : 0u))) & 0xffffu;
+            u[k] = head_side && hi < uint32_t(H) ? hbits : fx[k];
         }
+        float acc = tf.b;
+#pragma unroll
+        for (int q = 0; q < W / 2; ++q) acc = dot2(u[2 * q] | (u[2 * q + 1] << 16), tf.wp[q], acc);
+        if constexpr (W & 1) acc = __builtin_fmaf(tf.wl, bf_one(uint16_t(u[W - 1])), acc);
+        __builtin_amdgcn_raw_buffer_store_b16(to_bf16(act<SILU>(acc)), ofr,
+                                              fvalid ? (fe - xb) * 2u : kOob, 0, 0);
     }
     // One lane replaces the history this wave read with the row's last
     // width-1 inputs.

@@ -142,6 +142,34 @@ def test_long_rows_every_head_position(T, width, init):
     check_full(g, activation="silu", label=f"long rows T{T} W{width} silu")
 
 
+def lead_and_cut_waves(T, dim, width):
+    """Long-row waves that start at most width-2 tokens into a row (they own
+    that row's head, whose first tokens lie just before them) and end inside
+    the next row's head, whose first tokens the next wave owns."""
+    elems, H, n = long_wave_elems(T), width - 1, dim * T
+    hits = []
+    for w in range((n + elems - 1) // elems):
+        e0 = w * elems
+        e_last = min(e0 + elems, n) - 1
+        c = e0 // T
+        row_end = (c + 1) * T
+        if e0 - c * T <= H - 1 and row_end <= e_last and row_end + H - 1 > e_last:
+            hits.append(w)
+    return hits
+
+
+@pytest.mark.parametrize("width", [4, 5])
+def test_long_rows_wave_with_head_before_and_cut_after(width):
+    """T 2049, dim 2048: waves 2046-2047 start 2-3 tokens into a row and end
+    1-2 tokens into the next one -- both boundary spans of one wave."""
+    T, dim = 2049, 2048
+    assert lead_and_cut_waves(T, dim, width)
+    d = W.single_sequence(dim=dim, T=T, width=width, seed=T + width, values="exact")
+    g = to_dev(d)
+    check_full(g, activation=None, exact=True, label=f"lead+cut T{T} dim{dim} W{width}")
+    check_full(g, activation="silu", label=f"lead+cut T{T} dim{dim} W{width} silu")
+
+
 @pytest.mark.parametrize("T", [16, 17, 18, 19, 20, 23, 24, 25, 31, 33, 100, 127, 128, 129,
                                514, 1000, 1023, 1024, 2047])
 @pytest.mark.parametrize("width", [2, 3, 4, 5])
