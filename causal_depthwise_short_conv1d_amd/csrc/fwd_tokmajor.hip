@@ -46,6 +46,16 @@ constexpr int kLongRoundsMid = 3;                 // rounds for kLongMidLo <= T 
 constexpr uint32_t kLongMidLo = 3072;             // (measured on gfx950: 3 rounds are 1.3-3.5%
 constexpr uint32_t kLongMidHi = 10000;            // faster at T 3100-9999, 5% slower at T 2048,
                                                   // where 4 rounds are exactly one row per wave)
+// Four-round waves each keep 4 KiB of loads in flight; at six resident
+// workgroups per CU (what the registers allow) the memory queues run deeper
+// than they need to.  From T 10000 on, an LDS reservation the kernel never
+// touches caps a CU at five (5 x 32 KiB of gfx950's 160 KiB): measured
+// 1.4-1.7% faster at T 11027, 14807 and 20000.  Three-round waves
+// (T 3072-9999) and four-round waves below T 3072 are best at six.
+#ifndef SCONV_LONG_FOUR_ROUND_LDS
+#define SCONV_LONG_FOUR_ROUND_LDS 32768
+#endif
+constexpr uint32_t kLongFourRoundLds = SCONV_LONG_FOUR_ROUND_LDS;
 
 // Weights of one channel for the dot2 path: taps as packed bf16 pairs
 // (w[2p], w[2p+1]), the odd last tap and the bias as fp32.
@@ -336,20 +346,7 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
     u32x4 v[ROUNDS];
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) v[r] = buf_ld128<kNt>(xr, uint32_t(r * kWaveSize + lane) * 16u);
-    // the 4 elements before the wave: lane 0's halo in round 0
-    const uint16_t *pp = p.x + (wbase > 0 ? size_t(wbase) * kVec - 4 : 0);
-    uint32_t prev_z = sld_u32(pp), prev_w = sld_u32(pp + 2);
-    if (wbase == 0) prev_z = prev_w = 0;
-
-    // Sequence 0: its token range, cache line and whether it has a history.
-    const int64_t q0 = int32_t(sld_u32(p.sb.qsl)), q1 = int32_t(sld_u32(p.sb.qsl + 1));
-    const int32_t ci = int32_t(sld_u32(p.ci_rd));
-    const uint32_t hiv = sld_u8(p.hi_rd);
-    const int64_t line = p.sb.cache_idx ? int64_t(ci) : 0;
-    const bool skip = (p.sb.cache_idx && line == p.sb.pad_slot_id) ||
-                      (p.sb.cs && (line < 0 || line >= p.sb.num_lines));
-    const bool init = p.sb.cs && p.sb.has_init && hiv != 0;
-    const bool simple = q0 <= 0 && q1 >= int64_t(T);       // the sequence covers every token
+    asm volatile("" ::: "memory");                          // the x loads go out first
 
     // Wave-uniform rows, head and history.
     const uint32_t e_first = wbase * kVec;
@@ -366,10 +363,55 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
     if (e_first - row_a <= uint32_t(H - 1)) { hp = row_a; R = cA; }
     else if (uint64_t(row_end) + (H - 1) <= e_last) { hp = row_end; R = cA + 1; }
     const bool next_head = row_end <= e_last && uint64_t(row_end) + (H - 1) > e_last;
+    // The elements around a row boundary are computed one per lane after
+    // the rounds, and the chunks that hold them are not stored by the
+    // rounds.  Span A: the chunks that hold the wave's head (from the head
+    // itself when it starts just before the wave), at most 16 elements, for
+    // lanes 0..15.  Span B: the start of the chunk that holds the next
+    // wave's head, up to that head (1..7 elements), for lanes 16..23.  Each
+    // of these lanes reads its element's width inputs with 2-byte loads
+    // issued here, right after the x loads: the spans follow from the row
+    // geometry alone, so no scalar load stands before them.
+    const uint32_t fa0 = hp != kNone ? (hp < e_first ? hp : hp & ~uint32_t(kVec - 1)) : 0u;
+    const uint32_t fa1 = hp != kNone ? ((hp + (H - 1)) & ~uint32_t(kVec - 1)) + kVec : 0u;
+    const uint32_t fb0 = row_end & ~uint32_t(kVec - 1);
+    const uint32_t nb_rows = next_head ? row_end - fb0 : 0u;
+    const bool in_a = lane < 16;
+    const uint32_t fe = in_a ? fa0 + uint32_t(lane) : fb0 + uint32_t(lane - 16);
+    const bool f_in = in_a ? fe < fa1 : uint32_t(lane - 16) < nb_rows;
+    // span offsets are relative to 8 elements before the wave
+    const uint32_t xb = e_first >= kVec ? e_first - kVec : 0u;
+    const Rsrc xfr = make_rsrc(p.x + xb, int64_t(p.n_elems - xb) * 2);
+    const Rsrc ofr = make_rsrc(p.out + xb, int64_t(p.n_elems - xb) * 2);
+    uint32_t fx[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const int64_t pos = int64_t(fe) - H + k;
+        fx[k] = buf_ld16(xfr, f_in && pos >= int64_t(xb) ? uint32_t(pos - xb) * 2u : kOob);
+    }
+    asm volatile("" ::: "memory");                          // and the span loads next
+    // the 4 elements before the wave: lane 0's halo in round 0
+    const uint16_t *pp = p.x + (wbase > 0 ? size_t(wbase) * kVec - 4 : 0);
+    uint32_t prev_z = sld_u32(pp), prev_w = sld_u32(pp + 2);
+    if (wbase == 0) prev_z = prev_w = 0;
+
+    // Sequence 0: its token range, cache line and whether it has a history.
+    const int64_t q0 = int32_t(sld_u32(p.sb.qsl)), q1 = int32_t(sld_u32(p.sb.qsl + 1));
+    const int32_t ci = int32_t(sld_u32(p.ci_rd));
+    const uint32_t hiv = sld_u8(p.hi_rd);
+    const int64_t line = p.sb.cache_idx ? int64_t(ci) : 0;
+    const bool skip = (p.sb.cache_idx && line == p.sb.pad_slot_id) ||
+                      (p.sb.cs && (line < 0 || line >= p.sb.num_lines));
+    const bool init = p.sb.cs && p.sb.has_init && hiv != 0;
+    const bool simple = q0 <= 0 && q1 >= int64_t(T);       // the sequence covers every token
+
+    const bool live = !skip;                                // padded sequence: nothing to do
+    // A span is computed when the whole row is one sequence that is not padded.
+    const bool own_head = simple && hp != kNone && live;
+    const uint32_t nb = simple && live ? nb_rows : 0u;
+    const bool fvalid = f_in && simple && live;
     const PairTaps<W> tA = sload_pair_taps<W>(p, cA);
     const PairTaps<W> tB = sload_pair_taps<W>(p, cA + 1 < uint32_t(p.dim) ? cA + 1 : cA);
-    const bool live = !skip;                                // padded sequence: nothing to do
-    const bool own_head = simple && hp != kNone && live;
     const PairTaps<W> &t_head = (R == cA) ? tA : tB;
     // Waves that hold a row head also read its history (the cached state,
     // read by this wave only) and the row's last width-1 inputs (the new
@@ -394,31 +436,6 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
 #pragma unroll
     for (int i = 0; i < H / 2 + 1; ++i) pin_sgpr(nh.d[i]);
 
-    // The elements around a row boundary are computed one per lane after
-    // the rounds, and the chunks that hold them are not stored by the
-    // rounds.  Span A: the chunks that hold the wave's own head (from the
-    // head itself when it starts just before the wave), at most 16
-    // elements, for lanes 0..15.  Span B: the start of the chunk that holds
-    // the next wave's head, up to that head (1..7 elements), for lanes
-    // 16..23.  Each of these lanes reads its element's width inputs with
-    // 2-byte loads issued here, under the x loads.
-    const uint32_t fa0 = own_head ? (hp < e_first ? hp : hp & ~uint32_t(kVec - 1)) : 0u;
-    const uint32_t fa1 = own_head ? ((hp + (H - 1)) & ~uint32_t(kVec - 1)) + kVec : 0u;
-    const uint32_t fb0 = row_end & ~uint32_t(kVec - 1);
-    const uint32_t nb = (next_head && simple && live) ? row_end - fb0 : 0u;
-    const bool in_a = lane < 16;
-    const uint32_t fe = in_a ? fa0 + uint32_t(lane) : fb0 + uint32_t(lane - 16);
-    const bool fvalid = in_a ? fe < fa1 : uint32_t(lane - 16) < nb;
-    // span offsets are relative to 8 elements before the wave
-    const uint32_t xb = e_first >= kVec ? e_first - kVec : 0u;
-    const Rsrc xfr = make_rsrc(p.x + xb, int64_t(p.n_elems - xb) * 2);
-    const Rsrc ofr = make_rsrc(p.out + xb, int64_t(p.n_elems - xb) * 2);
-    uint32_t fx[W];
-#pragma unroll
-    for (int k = 0; k < W; ++k) {
-        const int64_t pos = int64_t(fe) - H + k;
-        fx[k] = buf_ld16(xfr, fvalid && pos >= int64_t(xb) ? uint32_t(pos - xb) * 2u : kOob);
-    }
     // chunks (relative to the wave) the rounds leave to the lanes above
     const uint32_t sa0 = fa0 < e_first ? 0u : fa0 / kVec - wbase;
     const uint32_t na = fa1 > fa0 ? (fa1 - 1) / kVec - wbase + 1 - sa0 : 0u;
@@ -1197,14 +1214,16 @@ hipError_t launch_ws(const FwdTokParams &p, hipStream_t s) {
     } else if (p.sb.batch > 1) {
         fwd_tokmajor_kernel<W, SILU, true><<<grid, block, 0, s>>>(p);
     } else if (p.T >= kWaveElems) {
+        const dim3 b(kLongWaves * kWaveSize);
         if (p.T >= kLongMidLo && p.T < kLongMidHi) {
             constexpr uint32_t kLB = kLongWaves * kLongRoundsMid * kWaveSize;
-            const uint32_t lb = (p.n_chunks + kLB - 1) / kLB;
-            fwd_tok_long_kernel<W, SILU, kLongRoundsMid><<<dim3(lb), dim3(kLongWaves * kWaveSize), 0, s>>>(p);
+            const dim3 g((p.n_chunks + kLB - 1) / kLB);
+            fwd_tok_long_kernel<W, SILU, kLongRoundsMid><<<g, b, 0, s>>>(p);
         } else {
             constexpr uint32_t kLB = kLongWaves * kLongRounds * kWaveSize;
-            const uint32_t lb = (p.n_chunks + kLB - 1) / kLB;
-            fwd_tok_long_kernel<W, SILU, kLongRounds><<<dim3(lb), dim3(kLongWaves * kWaveSize), 0, s>>>(p);
+            const dim3 g((p.n_chunks + kLB - 1) / kLB);
+            const uint32_t lds = p.T >= kLongMidHi ? kLongFourRoundLds : 0u;
+            fwd_tok_long_kernel<W, SILU, kLongRounds><<<g, b, lds, s>>>(p);
         }
     } else if (p.T >= uint32_t(kShortMinT)) {
         // Rounds per wave, measured on gfx950: one round (the most waves in
