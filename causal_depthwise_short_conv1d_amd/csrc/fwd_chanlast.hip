@@ -453,6 +453,14 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_cl_one_kerne
     }
 }
 
+// The varlen kernel's waves keep their tile's rows in flight; at the six
+// or seven resident workgroups per CU that its registers allow, the memory
+// queues run deeper than they need to.  An LDS reservation the kernel never
+// touches caps a CU at five workgroups (5 x 32 KiB of gfx950's 160 KiB):
+// measured 1.6-3% faster on the 64-sequence dim-8192 batch at widths 2-5.
+// (The one-sequence kernel is best at full occupancy.)
+constexpr uint32_t kClCapLds = 32768;
+
 template <int W>
 hipError_t launch_w(const FwdClParams &p, bool silu, hipStream_t s) {
     const uint64_t waves = uint64_t(p.n_tiles) * uint64_t(p.n_slabs);
@@ -469,10 +477,10 @@ hipError_t launch_w(const FwdClParams &p, bool silu, hipStream_t s) {
         else fwd_cl_one_kernel<W, false><<<g, block, 0, s>>>(p, n_groups);
         return hipGetLastError();
     }
-    if (silu && full) fwd_chanlast_kernel<W, true, true><<<grid, block, 0, s>>>(p);
-    else if (silu) fwd_chanlast_kernel<W, true, false><<<grid, block, 0, s>>>(p);
-    else if (full) fwd_chanlast_kernel<W, false, true><<<grid, block, 0, s>>>(p);
-    else fwd_chanlast_kernel<W, false, false><<<grid, block, 0, s>>>(p);
+    if (silu && full) fwd_chanlast_kernel<W, true, true><<<grid, block, kClCapLds, s>>>(p);
+    else if (silu) fwd_chanlast_kernel<W, true, false><<<grid, block, kClCapLds, s>>>(p);
+    else if (full) fwd_chanlast_kernel<W, false, true><<<grid, block, kClCapLds, s>>>(p);
+    else fwd_chanlast_kernel<W, false, false><<<grid, block, kClCapLds, s>>>(p);
     return hipGetLastError();
 }
 
