@@ -383,12 +383,14 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
     const uint32_t xb = e_first >= kVec ? e_first - kVec : 0u;
     const Rsrc xfr = make_rsrc(p.x + xb, int64_t(p.n_elems - xb) * 2);
     const Rsrc ofr = make_rsrc(p.out + xb, int64_t(p.n_elems - xb) * 2);
-    uint32_t fx[W];
-#pragma unroll
-    for (int k = 0; k < W; ++k) {
-        const int64_t pos = int64_t(fe) - H + k;
-        fx[k] = buf_ld16(xfr, f_in && pos >= int64_t(xb) ? uint32_t(pos - xb) * 2u : kOob);
-    }
+    // one 12-byte load from the dword holding input 0 covers the width
+    // inputs (at most 6 elements from there); a span lane whose inputs
+    // start before x (the first row's head, all history) loads nothing
+    const int64_t p0 = int64_t(fe) - H;
+    const bool f_ld = f_in && p0 >= int64_t(xb);
+    const uint32_t f_odd = uint32_t(p0) & 1u;
+    const u32x3 fr = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(
+        xfr, f_ld ? uint32_t(p0 - xb - f_odd) * 2u : kOob, 0, 0));
     asm volatile("" ::: "memory");                          // and the span loads next
     // the 4 elements before the wave: lane 0's halo in round 0
     const uint16_t *pp = p.x + (wbase > 0 ? size_t(wbase) * kVec - 4 : 0);
@@ -490,12 +492,18 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
         const bool head_side = in_a && fe >= hp;
         const PairTaps<W> tf = select(head_side, t_head, tA);
         const uint64_t hv = pack_hist<H>(hb);
+        // the loaded inputs shifted down by the odd element, two per dword
+        const uint32_t g0 = __builtin_amdgcn_alignbit(fr.y, fr.x, 16 * f_odd);
+        const uint32_t g1 = __builtin_amdgcn_alignbit(fr.z, fr.y, 16 * f_odd);
+        const uint32_t g2 = f_odd ? fr.z >> 16 : fr.z;
+        const uint32_t gv[3] = {g0, g1, g2};
         uint32_t u[W];
 #pragma unroll
         for (int k = 0; k < W; ++k) {
             const uint32_t hi = fe - hp + uint32_t(k);      // history index when < H
             const uint32_t hbits = uint32_t(hv >> (16 * (hi < uint32_t(H) ? hi : 0u))) & 0xffffu;
-            u[k] = head_side && hi < uint32_t(H) ? hbits : fx[k];
+            const uint32_t xk = (gv[k >> 1] >> (16 * (k & 1))) & 0xffffu;
+            u[k] = head_side && hi < uint32_t(H) ? hbits : xk;
         }
         float acc = tf.b;
 #pragma unroll
