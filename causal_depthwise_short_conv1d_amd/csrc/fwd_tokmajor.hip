@@ -383,14 +383,16 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
     const uint32_t xb = e_first >= kVec ? e_first - kVec : 0u;
     const Rsrc xfr = make_rsrc(p.x + xb, int64_t(p.n_elems - xb) * 2);
     const Rsrc ofr = make_rsrc(p.out + xb, int64_t(p.n_elems - xb) * 2);
-    // one 12-byte load from the dword holding input 0 covers the width
-    // inputs (at most 6 elements from there); a span lane whose inputs
-    // start before x (the first row's head, all history) loads nothing
+    // One 12-byte load from the dword holding input 0 covers the width
+    // inputs (at most 6 elements from there).  Inputs before x occur only
+    // in the array's first wave (the first row's head, whose inputs before
+    // token 0 are history): such a lane loads from x's start instead.
     const int64_t p0 = int64_t(fe) - H;
-    const bool f_ld = f_in && p0 >= int64_t(xb);
-    const uint32_t f_odd = uint32_t(p0) & 1u;
+    const bool f_neg = p0 < int64_t(xb);
+    const uint32_t f_odd = f_neg ? 0u : uint32_t(p0) & 1u;
+    const uint32_t f_off = f_neg ? 0u : uint32_t(p0 - int64_t(xb)) * 2u - f_odd * 2u;
     const u32x3 fr = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(
-        xfr, f_ld ? uint32_t(p0 - xb - f_odd) * 2u : kOob, 0, 0));
+        xfr, f_in ? f_off : kOob, 0, 0));
     asm volatile("" ::: "memory");                          // and the span loads next
     // the 4 elements before the wave: lane 0's halo in round 0
     const uint16_t *pp = p.x + (wbase > 0 ? size_t(wbase) * kVec - 4 : 0);
@@ -497,13 +499,29 @@ __global__ __launch_bounds__(kLongWaves * kWaveSize) void fwd_tok_long_kernel(Fw
         const uint32_t g1 = __builtin_amdgcn_alignbit(fr.z, fr.y, 16 * f_odd);
         const uint32_t g2 = f_odd ? fr.z >> 16 : fr.z;
         const uint32_t gv[3] = {g0, g1, g2};
+        uint32_t xin[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) xin[k] = (gv[k >> 1] >> (16 * (k & 1))) & 0xffffu;
+        if (wbase == 0) {                                   // wave-uniform: the first wave
+            asm volatile("");
+            // a lane whose inputs start sh tokens before x read x from its
+            // start: input k >= sh is element k - sh of that run
+            const int32_t sh = f_neg ? int32_t(int64_t(xb) - p0) : 0;
+            const uint32_t fw[3] = {fr.x, fr.y, fr.z};
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int32_t i = k - sh;
+                const uint32_t ii = i < 0 ? 0u : uint32_t(i);
+                const uint32_t dw = (ii >> 1) == 0 ? fw[0] : ((ii >> 1) == 1 ? fw[1] : fw[2]);
+                if (sh > 0) xin[k] = (dw >> (16 * (ii & 1))) & 0xffffu;
+            }
+        }
         uint32_t u[W];
 #pragma unroll
         for (int k = 0; k < W; ++k) {
             const uint32_t hi = fe - hp + uint32_t(k);      // history index when < H
             const uint32_t hbits = uint32_t(hv >> (16 * (hi < uint32_t(H) ? hi : 0u))) & 0xffffu;
-            const uint32_t xk = (gv[k >> 1] >> (16 * (k & 1))) & 0xffffu;
-            u[k] = head_side && hi < uint32_t(H) ? hbits : xk;
+            u[k] = head_side && hi < uint32_t(H) ? hbits : xin[k];
         }
         float acc = tf.b;
 #pragma unroll
