@@ -401,6 +401,18 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_cl_one_kerne
         win[k] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                      xr.rsrc, mine ? voff : kOob, mine ? int((row - base) * xr.pitch) : 0, kNt));
     }
+    // Rows H.. of the wave read only its own rows: they are computed and
+    // stored as the rows arrive, before the workgroup waits on its slowest
+    // wave for the halos.
+    const Rows orr = make_rows(p.out, t0, p.o_st, T, p.dim);
+#pragma unroll
+    for (int u = H; u < kOneRows; ++u) {
+        u32x2 own[H];
+#pragma unroll
+        for (int k = 0; k < H; ++k) own[k] = xv[u - H + k];
+        const u32x2 o = conv_row<W, SILU>(tp, own, xv[u]);
+        if (nv > 0) st_rows(orr, t0 + u, voff, o);     // rows past T: dropped
+    }
 #pragma unroll
     for (int k = 0; k < H; ++k) edge[wave][k][lane] = xv[kOneRows - H + k];
     __syncthreads();
@@ -442,9 +454,9 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_cl_one_kerne
         }
     }
 
-    const Rows orr = make_rows(p.out, t0, p.o_st, T, p.dim);
+    // rows 0 .. H-1, whose windows reach into the halo
 #pragma unroll
-    for (int u = 0; u < kOneRows; ++u) {
+    for (int u = 0; u < H; ++u) {
         const u32x2 o = conv_row<W, SILU>(tp, win, xv[u]);
         if (nv > 0) st_rows(orr, t0 + u, voff, o);     // rows past T: dropped
 #pragma unroll
