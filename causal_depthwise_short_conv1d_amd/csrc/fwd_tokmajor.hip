@@ -817,17 +817,21 @@ __global__ __launch_bounds__(kRowsBlock) void fwd_tok_rows_kernel(FwdTokParams p
 }
 
 // A batch of sequences in rows of at least one wave (total tokens T >=
-// 2048), in one launch of two kinds of workgroups:
+// 2048), in two launches of one kernel on the same stream:
 //   * chunk workgroups stream x as the long kernel does (a wave spans at most
-//     two rows, so the row and its taps are wave-uniform) and compute every
-//     chunk from the plain window; an element is stored only when it is at
-//     least width-1 tokens into an unpadded sequence, because only then do
-//     all its taps lie inside its own sequence.  They never touch a state.
-//   * head workgroups give one lane to each (sequence, channel): it reads the
-//     cached history (when the sequence continues from it), computes the
-//     first width-1 outputs, and writes the new state -- the single reader
-//     and writer of that history.
-// The two write disjoint elements, so no ordering between them is needed.
+//     two rows, so the row and its taps are wave-uniform), compute every
+//     chunk from the plain window and store every element of an unpadded
+//     sequence, whole chunks wherever a chunk holds no padded or uncovered
+//     token.  A sequence's first width-1 outputs come out wrong here (their
+//     windows reach into the previous sequence).  They never touch a state.
+//   * head workgroups, launched after them, give one lane to each
+//     (sequence, channel): it reads the cached history (when the sequence
+//     continues from it), rewrites the first width-1 outputs, and writes the
+//     new state -- the single reader and writer of that history.
+// Stream order puts every head write after the chunk writes it replaces.
+// (Leaving the head elements to the head lanes alone split every line that
+// holds a sequence start between two writers and cost each boundary chunk
+// several narrow stores: measured 8% of the batch.)
 // query_start_loc and the per-sequence lines and flags are staged in LDS.
 constexpr int kVarWaves = 4;                      // waves per block sharing the staged tables
 
@@ -854,7 +858,8 @@ __device__ __forceinline__ U16Run<K> vld_run(const uint16_t *p) {
 
 template <int W, bool SILU>
 __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(FwdTokParams p,
-                                                                                uint32_t chunk_blocks) {
+                                                                                uint32_t chunk_blocks,
+                                                                                uint32_t block0) {
     constexpr int H = W - 1;
     __shared__ int32_t qsl[kQslLdsMax];                 // the host guarantees batch + 1 fits
     __shared__ uint8_t skip_of[kQslLdsMax];
@@ -868,9 +873,10 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     // taps and the 4 elements before the wave are scalar loads issued next.
     const int lane = threadIdx.x & (kWaveSize - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
-    const uint32_t wbase = (blockIdx.x * kVarWaves + wave) * uint32_t(kChunksPerWave);
+    const uint32_t bid = blockIdx.x + block0;               // chunk blocks, then head blocks
+    const uint32_t wbase = (bid * kVarWaves + wave) * uint32_t(kChunksPerWave);
     const uint32_t n_full = p.n_elems / kVec;
-    const bool chunk_wave = blockIdx.x < chunk_blocks && wbase < p.n_chunks;
+    const bool chunk_wave = bid < chunk_blocks && wbase < p.n_chunks;
     constexpr int kNt = 2;                                  // non-temporal cache policy bit
     const uint32_t n_mine = chunk_wave && wbase < n_full
                                 ? (n_full - wbase < uint32_t(kChunksPerWave) ? n_full - wbase : uint32_t(kChunksPerWave))
@@ -904,9 +910,9 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     }
     __syncthreads();
 
-    if (blockIdx.x >= chunk_blocks) {
+    if (bid >= chunk_blocks) {
         // ---- head lanes: (sequence, channel) = divmod(g, dim)
-        const uint64_t g = uint64_t(blockIdx.x - chunk_blocks) * (kVarWaves * kWaveSize) + threadIdx.x;
+        const uint64_t g = uint64_t(bid - chunk_blocks) * (kVarWaves * kWaveSize) + threadIdx.x;
         const int32_t sq = int32_t(g / uint64_t(p.dim));
         const uint32_t c = uint32_t(g - uint64_t(sq) * uint64_t(p.dim));
         if (sq >= B) return;
@@ -1003,7 +1009,7 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         const bool in_b = i0 >= row_end;
         const int64_t t0 = int64_t(i0) - int64_t(in_b ? row_end : row_a);
         // the sequence of the first element, and whether the chunk is plain:
-        // one row, one unpadded sequence, every element past its head
+        // one row, unpadded sequences only
         int32_t sq = in_b ? seq_search(qsl, B, t0) : s_wave;
         if (!in_b)
             while (sq + 1 < B && qsl[sq + 1] <= t0) ++sq;
@@ -1015,14 +1021,14 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         };
         // The common cases without a loop: a whole chunk inside one row that
         // starts inside sequence sq and holds at most one more sequence
-        // start.  An element is kept when it is at least H into an unpadded
-        // sequence.  (The next sequence's bounds and pad flag are read with
-        // sq's, in one round of LDS reads.)
+        // start.  An element is kept when its sequence is not padded.  (The
+        // next sequence's bounds and pad flag are read with sq's, in one
+        // round of LDS reads.)
         uint32_t keep = 0;                             // bit j: store element j
         bool done = false;
         if (n == uint32_t(kVec) && !row_cross && t0 >= st && t0 < en) {
             const int64_t ea = en - t0 < kVec ? en - t0 : kVec;     // elements of sq: [0, ea)
-            const int64_t ka = st + H - t0 > 0 ? st + H - t0 : 0;    // the first past its head
+            const int64_t ka = st - t0 > 0 ? st - t0 : 0;            // the first of sq
             const int32_t s2 = sq + 1 < B ? sq + 1 : sq;
             int64_t st2, en2;
             bounds(s2, st2, en2);
@@ -1031,7 +1037,7 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
             if (ea == kVec) {
                 done = true;
             } else if (s2 != sq && st2 == en && en2 >= t0 + kVec) {
-                const int64_t kb = st2 + H - t0;                     // > ea
+                const int64_t kb = st2 - t0;                         // == ea
                 if (kb < kVec && !pad2) keep |= bits(kb, kVec);
                 done = true;
             }
@@ -1039,7 +1045,7 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         if (!done) {
             keep = 0;
             // segment by segment (a run of elements of one sequence of one
-            // row): keep those at least H into an unpadded sequence
+            // row): keep those of an unpadded sequence
             int64_t row_base = in_b ? int64_t(row_end) : int64_t(row_a);
             uint32_t j = 0;
             while (j < n) {
@@ -1058,9 +1064,7 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
                     continue;
                 }
                 const uint32_t jend = uint32_t(en - t) < n - j ? j + uint32_t(en - t) : n;
-                const int64_t skip_n = st + H - t;    // head elements of the run, owned by a head lane
-                const uint32_t jkeep = skip_n <= 0 ? j : (uint64_t(skip_n) < jend - j ? j + uint32_t(skip_n) : jend);
-                if (!skip_of[sq]) keep |= ((1u << jend) - 1u) & ~((1u << jkeep) - 1u);
+                if (!skip_of[sq]) keep |= ((1u << jend) - 1u) & ~((1u << j) - 1u);
                 j = jend;
             }
         }
@@ -1235,8 +1239,14 @@ hipError_t launch_ws(const FwdTokParams &p, hipStream_t s) {
         const uint32_t chunk_blocks = (waves + kVarWaves - 1) / kVarWaves;
         const uint64_t heads = uint64_t(p.sb.batch) * uint64_t(p.dim);
         const uint32_t head_blocks = uint32_t((heads + kVarWaves * kWaveSize - 1) / (kVarWaves * kWaveSize));
-        fwd_tok_varlen_kernel<W, SILU><<<dim3(chunk_blocks + head_blocks), dim3(kVarWaves * kWaveSize), 0, s>>>(
-            p, chunk_blocks);
+        // chunk workgroups, then (stream-ordered) the head workgroups that
+        // rewrite each sequence's first outputs and write its state
+        fwd_tok_varlen_kernel<W, SILU><<<dim3(chunk_blocks), dim3(kVarWaves * kWaveSize), 0, s>>>(
+            p, chunk_blocks, 0u);
+        const hipError_t e1 = hipGetLastError();
+        if (e1 != hipSuccess) return e1;
+        fwd_tok_varlen_kernel<W, SILU><<<dim3(head_blocks), dim3(kVarWaves * kWaveSize), 0, s>>>(
+            p, chunk_blocks, chunk_blocks);
     } else if (p.sb.batch > 1) {
         fwd_tokmajor_kernel<W, SILU, true><<<grid, block, 0, s>>>(p);
     } else if (p.T >= kWaveElems) {

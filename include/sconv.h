@@ -38,9 +38,12 @@
  *   - The library allocates nothing, never reads device memory on the host
  *     and never synchronises: each call validates its host arguments, then
  *     enqueues one kernel on `stream` (NULL = the default stream) and
- *     returns (a token-contiguous forward of 2^32 or more elements enqueues
- *     one kernel per channel group).  Calls are therefore safe to capture in
- *     a HIP graph.
+ *     returns.  Two forms enqueue more, all on `stream`: a token-contiguous
+ *     forward of 2^32 or more elements (one kernel per channel group), and a
+ *     token-contiguous batch of several sequences with rows of at least 2048
+ *     tokens (a streaming kernel, then one that rewrites each sequence's
+ *     first width-1 outputs and writes its state).  Calls are therefore safe
+ *     to capture in a HIP graph.
  *   - Return value: SCONV_OK, or a negative sconv_status.  On any error
  *     other than SCONV_ERR_LAUNCH nothing is enqueued.  An empty problem
  *     (zero tokens, zero sequences) returns SCONV_OK without enqueueing
