@@ -834,6 +834,8 @@ __global__ __launch_bounds__(kRowsBlock) void fwd_tok_rows_kernel(FwdTokParams p
 // several narrow stores: measured 8% of the batch.)
 // query_start_loc and the per-sequence lines and flags are staged in LDS.
 constexpr int kVarWaves = 4;                      // waves per block sharing the staged tables
+constexpr uint32_t kHeadChans = 16;               // channels of a head workgroup
+constexpr uint32_t kHeadSeqs = kVarWaves * kWaveSize / kHeadChans;   // its sequences (16)
 
 // K adjacent bf16 values from p through vector loads of only the dwords
 // that hold them (as sld_run, in vector registers).
@@ -911,11 +913,18 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     __syncthreads();
 
     if (bid >= chunk_blocks) {
-        // ---- head lanes: (sequence, channel) = divmod(g, dim)
-        const uint64_t g = uint64_t(bid - chunk_blocks) * (kVarWaves * kWaveSize) + threadIdx.x;
-        const int32_t sq = int32_t(g / uint64_t(p.dim));
-        const uint32_t c = uint32_t(g - uint64_t(sq) * uint64_t(p.dim));
-        if (sq >= B) return;
+        // ---- head lanes: a workgroup takes kHeadSeqs sequences x kHeadChans
+        // channels (channel fastest), the workgroups of one channel group
+        // next to each other.  Sequence s's last inputs and s+1's first
+        // inputs lie in the same line of a row, so neighbouring sequences'
+        // lanes read each row's boundary lines once from HBM; a sequence's
+        // states are kHeadChans * (width-1) contiguous values.
+        const uint32_t hb = bid - chunk_blocks;
+        const uint32_t sgroups = (uint32_t(B) + kHeadSeqs - 1) / kHeadSeqs;
+        const uint32_t cg = hb / sgroups, sg = hb - cg * sgroups;
+        const int32_t sq = int32_t(sg * kHeadSeqs + threadIdx.x / kHeadChans);
+        const uint32_t c = cg * kHeadChans + threadIdx.x % kHeadChans;
+        if (sq >= B || c >= uint32_t(p.dim)) return;
         const int64_t st = qsl[sq] < 0 ? 0 : (qsl[sq] > int32_t(T) ? int64_t(T) : int64_t(qsl[sq]));
         const int64_t en = qsl[sq + 1] < st ? st : (qsl[sq + 1] > int32_t(T) ? int64_t(T) : int64_t(qsl[sq + 1]));
         const int64_t L = en - st;
@@ -1237,8 +1246,8 @@ hipError_t launch_ws(const FwdTokParams &p, hipStream_t s) {
     if (p.sb.batch > 1 && p.T >= kWaveElems && p.sb.batch + 1 <= kQslLdsMax) {
         const uint32_t waves = (p.n_chunks + kChunksPerWave - 1) / kChunksPerWave;
         const uint32_t chunk_blocks = (waves + kVarWaves - 1) / kVarWaves;
-        const uint64_t heads = uint64_t(p.sb.batch) * uint64_t(p.dim);
-        const uint32_t head_blocks = uint32_t((heads + kVarWaves * kWaveSize - 1) / (kVarWaves * kWaveSize));
+        const uint32_t head_blocks = ((uint32_t(p.sb.batch) + kHeadSeqs - 1) / kHeadSeqs) *
+                                     ((uint32_t(p.dim) + kHeadChans - 1) / kHeadChans);
         // chunk workgroups, then (stream-ordered) the head workgroups that
         // rewrite each sequence's first outputs and write its state
         fwd_tok_varlen_kernel<W, SILU><<<dim3(chunk_blocks), dim3(kVarWaves * kWaveSize), 0, s>>>(
