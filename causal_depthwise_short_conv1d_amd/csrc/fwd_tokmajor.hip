@@ -876,46 +876,11 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     const int lane = threadIdx.x & (kWaveSize - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
     const uint32_t bid = blockIdx.x + block0;               // chunk blocks, then head blocks
-    const uint32_t wbase = (bid * kVarWaves + wave) * uint32_t(kChunksPerWave);
-    const uint32_t n_full = p.n_elems / kVec;
-    const bool chunk_wave = bid < chunk_blocks && wbase < p.n_chunks;
-    constexpr int kNt = 2;                                  // non-temporal cache policy bit
-    const uint32_t n_mine = chunk_wave && wbase < n_full
-                                ? (n_full - wbase < uint32_t(kChunksPerWave) ? n_full - wbase : uint32_t(kChunksPerWave))
-                                : 0u;
-    const Rsrc xr = make_rsrc(p.x + size_t(chunk_wave ? wbase : 0) * kVec, int64_t(n_mine) * 16);
-    u32x4 v[kTokRounds];
-#pragma unroll
-    for (int r = 0; r < kTokRounds; ++r) v[r] = buf_ld128<kNt>(xr, uint32_t(r * kWaveSize + lane) * 16u);
-    if (chunk_wave && n_mine < uint32_t(kChunksPerWave) && n_full < p.n_chunks) {
-#pragma unroll
-        for (int r = 0; r < kTokRounds; ++r) {
-            const uint32_t ch = wbase + r * kWaveSize + lane;
-            if (ch == n_full) v[r] = ld8_partial(p.x + size_t(ch) * kVec, int(p.n_elems - ch * kVec));
-        }
-    }
-    const uint16_t *pp = p.x + (chunk_wave && wbase > 0 ? size_t(wbase) * kVec - 4 : 0);
-    uint32_t prev_z = sld_u32(pp), prev_w = sld_u32(pp + 2);
-    if (!chunk_wave || wbase == 0) prev_z = prev_w = 0;
-    const uint32_t e_first = wbase * kVec;
-    const uint32_t cA = chunk_wave ? p.divT.div(e_first) : 0u;
-    const PairTaps<W> tA = sload_pair_taps<W>(p, cA);
-    const PairTaps<W> tB = sload_pair_taps<W>(p, cA + 1 < uint32_t(p.dim) ? cA + 1 : cA);
-
-    for (int i = threadIdx.x; i <= B; i += kVarWaves * kWaveSize) {
-        qsl[i] = p.sb.qsl[i];
-        if (i < B) {
-            const int64_t line = p.sb.cache_idx ? int64_t(p.sb.cache_idx[i]) : int64_t(i);
-            skip_of[i] = (p.sb.cache_idx && line == p.sb.pad_slot_id) ||
-                         (p.sb.cs && (line < 0 || line >= p.sb.num_lines));
-        }
-    }
-    __syncthreads();
-
     if (bid >= chunk_blocks) {
-        // ---- head lanes: a workgroup takes kHeadSeqs sequences x kHeadChans
-        // channels (channel fastest), the workgroups of one channel group
-        // next to each other.  Sequence s's last inputs and s+1's first
+        // ---- head lanes, in their own launch after the chunk lanes' (no
+        // staging: a lane reads only its own sequence's entries).  A
+        // workgroup takes kHeadSeqs sequences x kHeadChans channels (channel
+        // fastest), the workgroups of one channel group next to each other.  Sequence s's last inputs and s+1's first
         // inputs lie in the same line of a row, so neighbouring sequences'
         // lanes read each row's boundary lines once from HBM; a sequence's
         // states are kHeadChans * (width-1) contiguous values.
@@ -925,17 +890,21 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         const int32_t sq = int32_t(sg * kHeadSeqs + threadIdx.x / kHeadChans);
         const uint32_t c = cg * kHeadChans + threadIdx.x % kHeadChans;
         if (sq >= B || c >= uint32_t(p.dim)) return;
-        const int64_t st = qsl[sq] < 0 ? 0 : (qsl[sq] > int32_t(T) ? int64_t(T) : int64_t(qsl[sq]));
-        const int64_t en = qsl[sq + 1] < st ? st : (qsl[sq + 1] > int32_t(T) ? int64_t(T) : int64_t(qsl[sq + 1]));
-        const int64_t L = en - st;
-        if (L <= 0 || skip_of[sq]) return;
+        // the lane's own sequence entries, its taps: one round trip
+        const int32_t q0 = p.sb.qsl[sq], q1 = p.sb.qsl[sq + 1];
         const int64_t line = p.sb.cache_idx ? int64_t(p.sb.cache_idx[sq]) : int64_t(sq);
         const bool init = p.sb.cs && p.sb.has_init && p.sb.has_init[sq] != 0;
+        const Taps<W> tp = load_taps<W>(p, c);
+        const int64_t st = q0 < 0 ? 0 : (q0 > int32_t(T) ? int64_t(T) : int64_t(q0));
+        const int64_t en = q1 < st ? st : (q1 > int32_t(T) ? int64_t(T) : int64_t(q1));
+        const int64_t L = en - st;
+        const bool skip = (p.sb.cache_idx && line == p.sb.pad_slot_id) ||
+                          (p.sb.cs && (line < 0 || line >= p.sb.num_lines));
+        if (L <= 0 || skip) return;
         // every load at once, from addresses valid whether or not the value is
         // wanted (the values are selected afterwards)
         const size_t row0 = size_t(c) * T;
         const uint16_t *hbase = init ? p.sb.cs + line * p.sb.cs_sl + int64_t(c) * p.sb.cs_sd : p.x + row0;
-        const Taps<W> tp = load_taps<W>(p, c);
         // the sequence's first and last width-1 inputs as two runs of the row
         // (a first run that would pass the row's end starts d earlier)
         const int64_t xs = st + H <= int64_t(T) ? st : int64_t(T) - H;
@@ -982,6 +951,42 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         }
         return;
     }
+
+    const uint32_t wbase = (bid * kVarWaves + wave) * uint32_t(kChunksPerWave);
+    const uint32_t n_full = p.n_elems / kVec;
+    const bool chunk_wave = bid < chunk_blocks && wbase < p.n_chunks;
+    constexpr int kNt = 2;                                  // non-temporal cache policy bit
+    const uint32_t n_mine = chunk_wave && wbase < n_full
+                                ? (n_full - wbase < uint32_t(kChunksPerWave) ? n_full - wbase : uint32_t(kChunksPerWave))
+                                : 0u;
+    const Rsrc xr = make_rsrc(p.x + size_t(chunk_wave ? wbase : 0) * kVec, int64_t(n_mine) * 16);
+    u32x4 v[kTokRounds];
+#pragma unroll
+    for (int r = 0; r < kTokRounds; ++r) v[r] = buf_ld128<kNt>(xr, uint32_t(r * kWaveSize + lane) * 16u);
+    if (chunk_wave && n_mine < uint32_t(kChunksPerWave) && n_full < p.n_chunks) {
+#pragma unroll
+        for (int r = 0; r < kTokRounds; ++r) {
+            const uint32_t ch = wbase + r * kWaveSize + lane;
+            if (ch == n_full) v[r] = ld8_partial(p.x + size_t(ch) * kVec, int(p.n_elems - ch * kVec));
+        }
+    }
+    const uint16_t *pp = p.x + (chunk_wave && wbase > 0 ? size_t(wbase) * kVec - 4 : 0);
+    uint32_t prev_z = sld_u32(pp), prev_w = sld_u32(pp + 2);
+    if (!chunk_wave || wbase == 0) prev_z = prev_w = 0;
+    const uint32_t e_first = wbase * kVec;
+    const uint32_t cA = chunk_wave ? p.divT.div(e_first) : 0u;
+    const PairTaps<W> tA = sload_pair_taps<W>(p, cA);
+    const PairTaps<W> tB = sload_pair_taps<W>(p, cA + 1 < uint32_t(p.dim) ? cA + 1 : cA);
+
+    for (int i = threadIdx.x; i <= B; i += kVarWaves * kWaveSize) {
+        qsl[i] = p.sb.qsl[i];
+        if (i < B) {
+            const int64_t line = p.sb.cache_idx ? int64_t(p.sb.cache_idx[i]) : int64_t(i);
+            skip_of[i] = (p.sb.cache_idx && line == p.sb.pad_slot_id) ||
+                         (p.sb.cs && (line < 0 || line >= p.sb.num_lines));
+        }
+    }
+    __syncthreads();
 
     // ---- chunk lanes
     if (!chunk_wave) return;
