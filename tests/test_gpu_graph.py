@@ -82,6 +82,12 @@ class Step:
                            n_pad=1, layout="tok_dim")
         self.c = {k: (t.to(DEV) if isinstance(t, torch.Tensor) else t) for k, t in c.items()}
         self.c_out = S.new_output(self.c["x"])
+        # token-contiguous batch with rows of at least 2048 tokens: the call
+        # enqueues two kernels (the stream, then the head lanes)
+        t = W.varlen_batch(lengths=[900, 0, 1400, 3], dim=72, width=4, seed=707, num_lines=6,
+                           n_pad=1, layout="dim_tok")
+        self.t = {k: (x.to(DEV) if isinstance(x, torch.Tensor) else x) for k, x in t.items()}
+        self.t_out = S.new_output(self.t["x"])
         qsl = self.p["query_start_loc"]
         self.n_req = qsl.numel() - 1
         self.n_tok = self.p["x"].shape[0]
@@ -92,10 +98,11 @@ class Step:
     def mutable(self):
         return [self.v["conv_states"], self.d["conv_state"], self.s["conv_state"],
                 self.s["intermediate"], self.p["cache"], self.m["cache"], self.r["conv_state"],
-                self.c["conv_states"]]
+                self.c["conv_states"], self.t["conv_states"]]
 
     def bf_outputs(self):
-        return [self.v_out, self.d_out, self.s_out, self.p_out, self.r_out, self.c_out] + self.m_outs
+        return [self.v_out, self.d_out, self.s_out, self.p_out, self.r_out, self.c_out,
+                self.t_out] + self.m_outs
 
     def outputs(self):
         return self.bf_outputs() + [self.si, self.qs] + self.mutable()
@@ -139,6 +146,11 @@ class Step:
                             c["query_start_loc"], cache_indices=c["cache_indices"],
                             has_initial_state=c["has_initial_state"], activation="silu",
                             out=self.c_out)
+        t = self.t
+        S.conv1d_fwd_varlen(t["x"], t["weight"], t["bias"], t["conv_states"],
+                            t["query_start_loc"], cache_indices=t["cache_indices"],
+                            has_initial_state=t["has_initial_state"], activation="silu",
+                            out=self.t_out)
 
 
 def test_graph_capture_replays_every_entry_point():
