@@ -1014,6 +1014,46 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         prev_w = rw;
     }
 
+    // A wave inside one row whose tokens all belong to unpadded sequences
+    // stores every chunk whole, with no per-lane sequence work (the first
+    // width-1 outputs of the sequences that start in it are rewritten by the
+    // head launch).  Deciding it is a short wave-uniform walk of the table.
+    const uint32_t e_end = e_first + kWaveElems <= p.n_elems ? e_first + kWaveElems : p.n_elems;
+    bool plain = e_end <= row_end;
+    if (plain) {
+        asm volatile("");
+        const int64_t ta0 = int64_t(e_first) - int64_t(row_a);     // the wave's tokens [ta0, ta1)
+        const int64_t ta1 = ta0 + int64_t(e_end - e_first);
+        plain = int64_t(__builtin_amdgcn_readfirstlane(qsl[0])) <= ta0 &&
+                int64_t(__builtin_amdgcn_readfirstlane(qsl[B])) >= ta1;
+        for (int32_t q = s_wave; plain && q < B; ++q) {
+            if (int64_t(__builtin_amdgcn_readfirstlane(qsl[q])) >= ta1) break;
+            if (__builtin_amdgcn_readfirstlane(int32_t(skip_of[q])) != 0) plain = false;
+        }
+    }
+    if (plain) {
+        asm volatile("");
+        const Rsrc outr = make_rsrc(p.out + size_t(wbase) * kVec, int64_t(n_mine) * 16);
+#pragma unroll
+        for (int r = 0; r < kTokRounds; ++r) {
+            const uint32_t rel = uint32_t(r * kWaveSize + lane);
+            const uint32_t chunk = wbase + rel;
+            Window win;
+            win.d[0] = hz[r];
+            win.d[1] = hw[r];
+            win.d[2] = v[r].x;
+            win.d[3] = v[r].y;
+            win.d[4] = v[r].z;
+            win.d[5] = v[r].w;
+            const u32x4 o = fast_chunk<W, SILU>(win, tA);
+            // full chunks through the descriptor (past its end: dropped)
+            __builtin_amdgcn_raw_buffer_store_b128(o, outr, rel * 16u, 0, kNt);
+            if (chunk == n_full && chunk < p.n_chunks)               // the ragged last chunk
+                st8_partial(p.out + size_t(chunk) * kVec, o, int(p.n_elems - chunk * kVec), true);
+        }
+        return;
+    }
+
 #pragma unroll
     for (int r = 0; r < kTokRounds; ++r) {
         const uint32_t chunk = wbase + r * kWaveSize + lane;
