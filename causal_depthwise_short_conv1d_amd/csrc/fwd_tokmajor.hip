@@ -858,6 +858,30 @@ __device__ __forceinline__ U16Run<K> vld_run(const uint16_t *p) {
     return r;
 }
 
+// K adjacent bf16 values from element `flat` of a descriptor's array, in
+// one load of the dwords that hold them (past the extent: 0).
+template <int K>
+__device__ __forceinline__ U16Run<K> bld_run(Rsrc r, uint32_t flat) {
+    constexpr int N = K / 2 + 1;
+    const uint32_t m = flat & 1u;
+    const uint32_t off = (flat - m) * 2u;
+    uint32_t raw[N];
+    if constexpr (N == 1) {
+        raw[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    } else if constexpr (N == 2) {
+        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+        raw[0] = v.x; raw[1] = v.y;
+    } else {
+        const u32x3 v = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0));
+        raw[0] = v.x; raw[1] = v.y; raw[2] = v.z;
+    }
+    U16Run<K> res;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        res.d[i] = __builtin_amdgcn_alignbit(i + 1 < N ? raw[i + 1 < N ? i + 1 : 0] : 0u, raw[i], 16 * m);
+    return res;
+}
+
 template <int W, bool SILU>
 __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(FwdTokParams p,
                                                                                 uint32_t chunk_blocks,
@@ -909,8 +933,22 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         // (a first run that would pass the row's end starts d earlier)
         const int64_t xs = st + H <= int64_t(T) ? st : int64_t(T) - H;
         const int d = int(st - xs);
-        const U16Run<H> xrun = vld_run<H>(p.x + row0 + size_t(xs));
-        const U16Run<H> nrun = vld_run<H>(p.x + row0 + size_t(L >= H ? en - H : xs));
+        // (one load per run through a descriptor at x when x spans less than
+        // 2^31 bytes, else the dwords one by one).  The descriptor ends with
+        // the dword that holds x's last element, which the one-by-one reads
+        // touch as well; a dword-aligned read that holds a valid element
+        // stays in its page, and dwords past that end read 0.
+        U16Run<H> xrun, nrun;
+        const int64_t ns = L >= H ? en - H : xs;
+        const int64_t x_bytes = (int64_t(p.n_elems) * 2 + 3) & ~int64_t(3);
+        if (x_bytes < (int64_t(1) << 31)) {                     // launch-uniform
+            const Rsrc xa = make_rsrc(p.x, x_bytes);
+            xrun = bld_run<H>(xa, uint32_t(row0 + size_t(xs)));
+            nrun = bld_run<H>(xa, uint32_t(row0 + size_t(ns)));
+        } else {
+            xrun = vld_run<H>(p.x + row0 + size_t(xs));
+            nrun = vld_run<H>(p.x + row0 + size_t(ns));
+        }
         uint32_t h[H], xh[H], nb[H];
 #pragma unroll
         for (int q = 0; q < H; ++q) {
