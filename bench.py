@@ -734,12 +734,13 @@ def summarize_trace(argv):
 
 
 def _profile_dispatches(d, counter=None):
-    """The libsconv dispatches of a profile run in launch order, assigned to
-    the workloads (each launched PROFILE_REPS + 1 times, in the order of
+    """The libsconv calls of a profile run in launch order, assigned to the
+    workloads (each called PROFILE_REPS + 1 times, in the order of
     workload_builders), and the run's calibration copies.  With `counter`,
-    d holds one --pmc pass and each dispatch carries that counter's value in
-    bytes (the CSV gives KiB); else d holds a kernel trace and each dispatch
-    its duration in us."""
+    d holds one --pmc pass and each call carries that counter's value in
+    bytes summed over its dispatches (the CSV gives KiB); else d holds a
+    kernel trace and each call the summed kernel-only time of its
+    dispatches in us."""
     import csv
     import glob
     name = "*counter_collection.csv" if counter else "*kernel_trace.csv"
@@ -757,11 +758,22 @@ def _profile_dispatches(d, counter=None):
         val = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         grid = lambda r: int(r["Grid_Size_X"]) if "Grid_Size_X" in r else int(r["Grid_Size"])
     calib = [val(r) for r in rows if "copyBuffer" in r["Kernel_Name"] and grid(r) == 131072][:3]
-    ours = [(r["Kernel_Name"], val(r)) for r in rows if "sconv::" in r["Kernel_Name"]]
+    # One call is a run of consecutive libsconv dispatches (a token-contiguous
+    # varlen batch is two: the stream kernel, then the head kernel); calls are
+    # separated by the flush reads and by the input set-up of each workload.
+    ours, prev = [], False
+    for r in rows:
+        mine = "sconv::" in r["Kernel_Name"]
+        if mine and prev:
+            k, v = ours[-1]
+            ours[-1] = (k + " + " + r["Kernel_Name"], v + val(r))
+        elif mine:
+            ours.append((r["Kernel_Name"], val(r)))
+        prev = mine
     names = [n for n, _ in workload_builders()]
     per = PROFILE_REPS + 1
     if len(ours) != per * len(names):
-        raise SystemExit(f"{d}: {len(ours)} libsconv dispatches, expected {per * len(names)}")
+        raise SystemExit(f"{d}: {len(ours)} libsconv calls, expected {per * len(names)}")
     out = {}
     for i, n in enumerate(names):
         grp = ours[i * per:(i + 1) * per]
@@ -817,7 +829,8 @@ def summarize_set(argv):
         fb = statistics.mean(fetch[n][1]) * ff
         wb = statistics.mean(write[n][1]) * fw
         nb = alg[n]
-        k = re.sub(r"\(.*", "", kern.replace("(anonymous namespace)::", "").replace("void ", ""))
+        k = " + ".join(re.sub(r"\(.*", "", part.replace("(anonymous namespace)::", "")
+                              .replace("void ", "")) for part in kern.split(" + "))
         result[n] = {"kernel": k, "median_us": round(med, 2), "algorithmic_bytes": nb,
                      "fetch_bytes": round(fb), "write_bytes": round(wb),
                      "traffic_bytes": round(fb + wb), "ratio": round((fb + wb) / nb, 4),
