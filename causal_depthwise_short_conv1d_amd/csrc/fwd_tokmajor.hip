@@ -997,10 +997,56 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     const uint32_t n_mine = chunk_wave && wbase < n_full
                                 ? (n_full - wbase < uint32_t(kChunksPerWave) ? n_full - wbase : uint32_t(kChunksPerWave))
                                 : 0u;
+    const uint32_t e_first = wbase * kVec;
+    const uint32_t cA = chunk_wave ? p.divT.div(e_first) : 0u;
+    // wave-uniform rows (at most two)
+    const uint32_t row_a = cA * T, row_end = row_a + T;
+    const uint32_t e_end = e_first + kWaveElems <= p.n_elems ? e_first + kWaveElems : p.n_elems;
+
+    // A chunk whose tokens all lie in padded sequences is never stored and
+    // feeds no stored output (an output at position width-1 or later of a
+    // sequence reads that sequence's inputs only; earlier ones are rewritten
+    // by the head launch), so its load is skipped.  Finding those chunks
+    // takes one read of the batch's table first: batches of at most 64
+    // sequences, one sequence per lane; larger batches load every chunk.
+    uint32_t dead = 0;                                      // bit r: round r's chunk
+    if (chunk_wave && B <= kWaveSize) {                     // launch-uniform
+        int32_t a = 0, b = 0;
+        bool pad = false;
+        if (lane < B) {
+            a = p.sb.qsl[lane];
+            b = p.sb.qsl[lane + 1];
+            const int64_t line = p.sb.cache_idx ? int64_t(p.sb.cache_idx[lane]) : int64_t(lane);
+            pad = (p.sb.cache_idx && line == p.sb.pad_slot_id) ||
+                  (p.sb.cs && (line < 0 || line >= p.sb.num_lines));
+        }
+        // the sequence's tokens clamped into [0, T], as the chunk lanes see them
+        const int32_t st = a < 0 ? 0 : (int64_t(a) > int64_t(T) ? int32_t(T) : a);
+        const int32_t en = b < st ? st : (int64_t(b) > int64_t(T) ? int32_t(T) : b);
+        const int64_t ta0 = int64_t(e_first) - int64_t(row_a);           // row A: [ta0, ta1)
+        const int64_t ta1 = int64_t(e_end < row_end ? e_end : row_end) - int64_t(row_a);
+        const int64_t tb1 = e_end > row_end ? int64_t(e_end - row_end) : 0;   // row B: [0, tb1)
+        uint64_t m = __ballot(pad && st < en && ((st < ta1 && en > ta0) || st < tb1));
+        while (m) {
+            const int q = __builtin_ctzll(m);
+            m &= m - 1;
+            const uint32_t s = uint32_t(__builtin_amdgcn_readlane(st, q));
+            const uint32_t e = uint32_t(__builtin_amdgcn_readlane(en, q));
+#pragma unroll
+            for (int r = 0; r < kTokRounds; ++r) {
+                const uint32_t i0 = (wbase + r * kWaveSize + lane) * kVec;
+                // the chunk's first token in its row (a chunk across the row end: none)
+                const uint32_t t = i0 + kVec <= row_end ? i0 - row_a : (i0 >= row_end ? i0 - row_end : kOob);
+                if (t != kOob && t >= s && t + kVec <= e) dead |= 1u << r;
+            }
+        }
+    }
+
     const Rsrc xr = make_rsrc(p.x + size_t(chunk_wave ? wbase : 0) * kVec, int64_t(n_mine) * 16);
     u32x4 v[kTokRounds];
 #pragma unroll
-    for (int r = 0; r < kTokRounds; ++r) v[r] = buf_ld128<kNt>(xr, uint32_t(r * kWaveSize + lane) * 16u);
+    for (int r = 0; r < kTokRounds; ++r)
+        v[r] = buf_ld128<kNt>(xr, (dead >> r) & 1u ? kOob : uint32_t(r * kWaveSize + lane) * 16u);
     if (chunk_wave && n_mine < uint32_t(kChunksPerWave) && n_full < p.n_chunks) {
 #pragma unroll
         for (int r = 0; r < kTokRounds; ++r) {
@@ -1011,8 +1057,6 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     const uint16_t *pp = p.x + (chunk_wave && wbase > 0 ? size_t(wbase) * kVec - 4 : 0);
     uint32_t prev_z = sld_u32(pp), prev_w = sld_u32(pp + 2);
     if (!chunk_wave || wbase == 0) prev_z = prev_w = 0;
-    const uint32_t e_first = wbase * kVec;
-    const uint32_t cA = chunk_wave ? p.divT.div(e_first) : 0u;
     const PairTaps<W> tA = sload_pair_taps<W>(p, cA);
     const PairTaps<W> tB = sload_pair_taps<W>(p, cA + 1 < uint32_t(p.dim) ? cA + 1 : cA);
 
@@ -1034,8 +1078,6 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         st = qsl[q] < 0 ? 0 : (qsl[q] > int32_t(T) ? int64_t(T) : int64_t(qsl[q]));
         en = qsl[q + 1] < st ? st : (qsl[q + 1] > int32_t(T) ? int64_t(T) : int64_t(qsl[q + 1]));
     };
-    // wave-uniform rows (at most two); their taps were read above
-    const uint32_t row_a = cA * T, row_end = row_a + T;
     // the sequence of the wave's first element; lanes of the first row walk
     // forward from it (a wave spans a few sequences), the second row searches
     const int32_t s_wave = __builtin_amdgcn_readfirstlane(seq_search(qsl, B, int64_t(e_first - row_a)));
@@ -1056,7 +1098,6 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     // stores every chunk whole, with no per-lane sequence work (the first
     // width-1 outputs of the sequences that start in it are rewritten by the
     // head launch).  Deciding it is a short wave-uniform walk of the table.
-    const uint32_t e_end = e_first + kWaveElems <= p.n_elems ? e_first + kWaveElems : p.n_elems;
     bool plain = e_end <= row_end;
     if (plain) {
         asm volatile("");
