@@ -23,8 +23,13 @@ SOURCES = ["sconv_api.hip", "fwd_tokmajor.hip", "fwd_chanlast.hip", "general.hip
 ARCH = os.environ.get("SCONV_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# -packed-fp32-ops: no packed fp32 instructions.  -dot13-insts: the bf16
+# dot2 is the three-operand form, whose accumulator input is a separate
+# register (the bias is shared by every output, not copied into each one);
+# measured 1-4% faster at dim 8192 T 4195.
 COMMON = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Xclang", "-target-feature", "-Xclang", "-dot13-insts",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 
@@ -44,9 +49,9 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     failed = []
     for src, pr in procs:
         out, _ = pr.communicate()
-        # hipcc's host pass does not know the fp32 packing feature; drop that note
+        # hipcc's host pass does not know the two device features; drop that note
         lines = [l for l in out.splitlines()
-                 if "packed-fp32-ops" not in l or "error" in l.lower()]
+                 if not ("packed-fp32-ops" in l or "dot13-insts" in l) or "error" in l.lower()]
         if lines and (verbose or pr.returncode):
             print("\n".join(lines), file=sys.stderr)
         if pr.returncode:

@@ -454,6 +454,41 @@ def test_varlen_long_rows_token_contiguous(width, seed, dim):
     check_full(gd, activation="silu", label=f"varlen long rows W{width} silu")
 
 
+@pytest.mark.parametrize("width", [2, 3, 4, 5])
+@pytest.mark.parametrize("lead", [2045, 2046, 2047, 2048])
+@pytest.mark.parametrize("init", ["all", "none", "mixed", "null", "no_state", "strided_state"])
+def test_varlen_long_starts_at_wave_edges(lead, width, init):
+    """Token-contiguous rows of 4101 tokens (2048-token waves, so several
+    waves cross a row end): a sequence of 64 tokens starting 3, 2, 1 or 0
+    tokens before a wave boundary (its first outputs spill into the next
+    wave), one of 63 (the shortest and longest lengths either side of the
+    split between the stream and head launches), the next row's first
+    sequence starting inside a wave, and a short one across a wave
+    boundary; a padded sequence next to the long ones.  Exact values, every
+    output and state compared bit for bit."""
+    lens = [lead, 64, 63, 1920 + (2047 - lead), 7]
+    assert sum(lens) == 4101
+    d = W.varlen_batch(lengths=lens, dim=7, width=width, seed=930 + lead + width, num_lines=9,
+                       n_pad=0, layout="dim_tok", values="exact")
+    d["cache_indices"][2] = W.PAD_SLOT_ID if lead % 2 else d["cache_indices"][2]
+    hi = torch.ones(len(lens), dtype=torch.bool)
+    if init == "none":
+        hi[:] = False
+    elif init == "mixed":
+        hi[1::2] = False
+    d["has_initial_state"] = None if init in ("null", "no_state") else hi
+    if init == "no_state":
+        d["conv_states"] = None
+    elif init == "strided_state":
+        # a [lines, width-1, dim] buffer viewed as [lines, dim, width-1]
+        cs = d["conv_states"]
+        d["conv_states"] = cs.transpose(1, 2).contiguous().transpose(1, 2)
+    say(f"[fwd] long starts at wave edges lead {lead} W{width} init {init}")
+    gd = to_dev(d)
+    check_full(gd, activation=None, exact=True, label=f"wave edges {lead} W{width} {init}")
+    check_full(gd, activation="silu", label=f"wave edges {lead} W{width} {init} silu")
+
+
 @pytest.mark.parametrize("layout", ["dim_tok", "tok_dim"])
 @pytest.mark.parametrize("nseq", [2047, 2048])
 def test_varlen_batch_size_at_lds_table_limit(nseq, layout):
