@@ -882,13 +882,18 @@ __device__ __forceinline__ U16Run<K> bld_run(Rsrc r, uint32_t flat) {
     return res;
 }
 
-template <int W, bool SILU>
+template <int W, bool SILU, bool SMALLB>
 __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(FwdTokParams p,
                                                                                 uint32_t chunk_blocks,
                                                                                 uint32_t block0) {
     constexpr int H = W - 1;
-    __shared__ int32_t qsl[kQslLdsMax];                 // the host guarantees batch + 1 fits
-    __shared__ uint8_t skip_of[kQslLdsMax];
+    // The table: staged in LDS for the workgroup, or (batches of at most 64
+    // sequences) copied by each wave from its lanes' registers into its own
+    // LDS rows, which needs no barrier.
+    __shared__ int32_t qsl[SMALLB ? 1 : kQslLdsMax];    // the host guarantees batch + 1 fits
+    __shared__ uint8_t skip_of[SMALLB ? 1 : kQslLdsMax];
+    __shared__ int32_t wqsl[SMALLB ? kVarWaves : 1][kWaveSize + 1];
+    __shared__ uint8_t wskip[SMALLB ? kVarWaves : 1][kWaveSize];
     const int32_t B = p.sb.batch;
     const uint32_t T = p.T;
 
@@ -1010,9 +1015,9 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     // takes one read of the batch's table first: batches of at most 64
     // sequences, one sequence per lane; larger batches load every chunk.
     uint32_t dead = 0;                                      // bit r: round r's chunk
-    if (chunk_wave && B <= kWaveSize) {                     // launch-uniform
-        int32_t a = 0, b = 0;
-        bool pad = false;
+    int32_t a = 0, b = 0;                                   // lane q: query_start_loc[q], [q+1]
+    bool pad = false;                                       // lane q: sequence q is padded
+    if (SMALLB && chunk_wave) {
         if (lane < B) {
             a = p.sb.qsl[lane];
             b = p.sb.qsl[lane + 1];
@@ -1060,27 +1065,39 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     const PairTaps<W> tA = sload_pair_taps<W>(p, cA);
     const PairTaps<W> tB = sload_pair_taps<W>(p, cA + 1 < uint32_t(p.dim) ? cA + 1 : cA);
 
-    for (int i = threadIdx.x; i <= B; i += kVarWaves * kWaveSize) {
-        qsl[i] = p.sb.qsl[i];
-        if (i < B) {
-            const int64_t line = p.sb.cache_idx ? int64_t(p.sb.cache_idx[i]) : int64_t(i);
-            skip_of[i] = (p.sb.cache_idx && line == p.sb.pad_slot_id) ||
-                         (p.sb.cs && (line < 0 || line >= p.sb.num_lines));
+    if constexpr (!SMALLB) {
+        for (int i = threadIdx.x; i <= B; i += kVarWaves * kWaveSize) {
+            qsl[i] = p.sb.qsl[i];
+            if (i < B) {
+                const int64_t line = p.sb.cache_idx ? int64_t(p.sb.cache_idx[i]) : int64_t(i);
+                skip_of[i] = (p.sb.cache_idx && line == p.sb.pad_slot_id) ||
+                             (p.sb.cs && (line < 0 || line >= p.sb.num_lines));
+            }
         }
+        __syncthreads();
     }
-    __syncthreads();
 
     // ---- chunk lanes
     if (!chunk_wave) return;
+    if constexpr (SMALLB) {
+        if (lane < B) {
+            wqsl[wave][lane] = a;
+            wskip[wave][lane] = pad ? 1 : 0;
+        }
+        if (lane == B - 1) wqsl[wave][B] = b;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's rows, before its reads
+    }
+    const int32_t *tq = SMALLB ? &wqsl[wave][0] : qsl;
+    const uint8_t *tskip = SMALLB ? &wskip[wave][0] : skip_of;
 
     // sequence bounds clamped into [0, T], as the head lanes see them
     auto bounds = [&](int32_t q, int64_t &st, int64_t &en) {
-        st = qsl[q] < 0 ? 0 : (qsl[q] > int32_t(T) ? int64_t(T) : int64_t(qsl[q]));
-        en = qsl[q + 1] < st ? st : (qsl[q + 1] > int32_t(T) ? int64_t(T) : int64_t(qsl[q + 1]));
+        st = tq[q] < 0 ? 0 : (tq[q] > int32_t(T) ? int64_t(T) : int64_t(tq[q]));
+        en = tq[q + 1] < st ? st : (tq[q + 1] > int32_t(T) ? int64_t(T) : int64_t(tq[q + 1]));
     };
     // the sequence of the wave's first element; lanes of the first row walk
     // forward from it (a wave spans a few sequences), the second row searches
-    const int32_t s_wave = __builtin_amdgcn_readfirstlane(seq_search(qsl, B, int64_t(e_first - row_a)));
+    const int32_t s_wave = __builtin_amdgcn_readfirstlane(seq_search(tq, B, int64_t(e_first - row_a)));
 
     const int src_lane = (lane + kWaveSize - 1) & (kWaveSize - 1);
     uint32_t hz[kTokRounds], hw[kTokRounds];
@@ -1103,11 +1120,11 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         asm volatile("");
         const int64_t ta0 = int64_t(e_first) - int64_t(row_a);     // the wave's tokens [ta0, ta1)
         const int64_t ta1 = ta0 + int64_t(e_end - e_first);
-        plain = int64_t(__builtin_amdgcn_readfirstlane(qsl[0])) <= ta0 &&
-                int64_t(__builtin_amdgcn_readfirstlane(qsl[B])) >= ta1;
+        plain = int64_t(__builtin_amdgcn_readfirstlane(tq[0])) <= ta0 &&
+                int64_t(__builtin_amdgcn_readfirstlane(tq[B])) >= ta1;
         for (int32_t q = s_wave; plain && q < B; ++q) {
-            if (int64_t(__builtin_amdgcn_readfirstlane(qsl[q])) >= ta1) break;
-            if (__builtin_amdgcn_readfirstlane(int32_t(skip_of[q])) != 0) plain = false;
+            if (int64_t(__builtin_amdgcn_readfirstlane(tq[q])) >= ta1) break;
+            if (__builtin_amdgcn_readfirstlane(int32_t(tskip[q])) != 0) plain = false;
         }
     }
     if (plain) {
@@ -1143,9 +1160,9 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         const int64_t t0 = int64_t(i0) - int64_t(in_b ? row_end : row_a);
         // the sequence of the first element, and whether the chunk is plain:
         // one row, unpadded sequences only
-        int32_t sq = in_b ? seq_search(qsl, B, t0) : s_wave;
+        int32_t sq = in_b ? seq_search(tq, B, t0) : s_wave;
         if (!in_b)
-            while (sq + 1 < B && qsl[sq + 1] <= t0) ++sq;
+            while (sq + 1 < B && tq[sq + 1] <= t0) ++sq;
         int64_t st, en;
         bounds(sq, st, en);
         const bool row_cross = !in_b && i0 + n > row_end;
@@ -1165,7 +1182,7 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
             const int32_t s2 = sq + 1 < B ? sq + 1 : sq;
             int64_t st2, en2;
             bounds(s2, st2, en2);
-            const bool pad1 = skip_of[sq] != 0, pad2 = skip_of[s2] != 0;
+            const bool pad1 = tskip[sq] != 0, pad2 = tskip[s2] != 0;
             if (ka < ea && !pad1) keep = bits(ka, ea);
             if (ea == kVec) {
                 done = true;
@@ -1186,10 +1203,10 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
                 if (t >= int64_t(T)) {                 // crossed into the next row
                     row_base += T;
                     t -= T;
-                    sq = seq_search(qsl, B, t);
+                    sq = seq_search(tq, B, t);
                     bounds(sq, st, en);
                 } else if (t >= en) {
-                    while (sq + 1 < B && qsl[sq + 1] <= t) ++sq;
+                    while (sq + 1 < B && tq[sq + 1] <= t) ++sq;
                     bounds(sq, st, en);
                 }
                 if (t < st || t >= en) {               // a token no sequence covers
@@ -1197,7 +1214,7 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
                     continue;
                 }
                 const uint32_t jend = uint32_t(en - t) < n - j ? j + uint32_t(en - t) : n;
-                if (!skip_of[sq]) keep |= ((1u << jend) - 1u) & ~((1u << j) - 1u);
+                if (!tskip[sq]) keep |= ((1u << jend) - 1u) & ~((1u << j) - 1u);
                 j = jend;
             }
         }
@@ -1374,11 +1391,16 @@ hipError_t launch_ws(const FwdTokParams &p, hipStream_t s) {
                                      ((uint32_t(p.dim) + kHeadChans - 1) / kHeadChans);
         // chunk workgroups, then (stream-ordered) the head workgroups that
         // rewrite each sequence's first outputs and write its state
-        fwd_tok_varlen_kernel<W, SILU><<<dim3(chunk_blocks), dim3(kVarWaves * kWaveSize), 0, s>>>(
-            p, chunk_blocks, 0u);
+        // (batches of at most 64 sequences keep the table in registers)
+        if (p.sb.batch <= kWaveSize)
+            fwd_tok_varlen_kernel<W, SILU, true><<<dim3(chunk_blocks), dim3(kVarWaves * kWaveSize), 0, s>>>(
+                p, chunk_blocks, 0u);
+        else
+            fwd_tok_varlen_kernel<W, SILU, false><<<dim3(chunk_blocks), dim3(kVarWaves * kWaveSize), 0, s>>>(
+                p, chunk_blocks, 0u);
         const hipError_t e1 = hipGetLastError();
         if (e1 != hipSuccess) return e1;
-        fwd_tok_varlen_kernel<W, SILU><<<dim3(head_blocks), dim3(kVarWaves * kWaveSize), 0, s>>>(
+        fwd_tok_varlen_kernel<W, SILU, false><<<dim3(head_blocks), dim3(kVarWaves * kWaveSize), 0, s>>>(
             p, chunk_blocks, chunk_blocks);
     } else if (p.sb.batch > 1) {
         fwd_tokmajor_kernel<W, SILU, true><<<grid, block, 0, s>>>(p);
