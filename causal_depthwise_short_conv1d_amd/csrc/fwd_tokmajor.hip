@@ -1097,7 +1097,16 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     };
     // the sequence of the wave's first element; lanes of the first row walk
     // forward from it (a wave spans a few sequences), the second row searches
-    const int32_t s_wave = __builtin_amdgcn_readfirstlane(seq_search(tq, B, int64_t(e_first - row_a)));
+    int32_t s_wave;
+    if constexpr (SMALLB) {
+        // the last sequence starting at or before the wave's first token:
+        // one ballot over the lanes' starts instead of a search
+        const uint32_t n = uint32_t(__builtin_popcountll(
+            __ballot(lane < B && int64_t(a) <= int64_t(e_first - row_a))));
+        s_wave = n > 0 ? int32_t(n) - 1 : 0;
+    } else {
+        s_wave = __builtin_amdgcn_readfirstlane(seq_search(tq, B, int64_t(e_first - row_a)));
+    }
 
     const int src_lane = (lane + kWaveSize - 1) & (kWaveSize - 1);
     uint32_t hz[kTokRounds], hw[kTokRounds];
@@ -1120,11 +1129,17 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
         asm volatile("");
         const int64_t ta0 = int64_t(e_first) - int64_t(row_a);     // the wave's tokens [ta0, ta1)
         const int64_t ta1 = ta0 + int64_t(e_end - e_first);
-        plain = int64_t(__builtin_amdgcn_readfirstlane(tq[0])) <= ta0 &&
-                int64_t(__builtin_amdgcn_readfirstlane(tq[B])) >= ta1;
-        for (int32_t q = s_wave; plain && q < B; ++q) {
-            if (int64_t(__builtin_amdgcn_readfirstlane(tq[q])) >= ta1) break;
-            if (__builtin_amdgcn_readfirstlane(int32_t(tskip[q])) != 0) plain = false;
+        if constexpr (SMALLB) {
+            plain = int64_t(__builtin_amdgcn_readlane(a, 0)) <= ta0 &&
+                    int64_t(__builtin_amdgcn_readlane(b, B - 1)) >= ta1 &&
+                    __ballot(lane < B && lane >= s_wave && int64_t(a) < ta1 && pad) == 0;
+        } else {
+            plain = int64_t(__builtin_amdgcn_readfirstlane(tq[0])) <= ta0 &&
+                    int64_t(__builtin_amdgcn_readfirstlane(tq[B])) >= ta1;
+            for (int32_t q = s_wave; plain && q < B; ++q) {
+                if (int64_t(__builtin_amdgcn_readfirstlane(tq[q])) >= ta1) break;
+                if (__builtin_amdgcn_readfirstlane(int32_t(tskip[q])) != 0) plain = false;
+            }
         }
     }
     if (plain) {
