@@ -489,6 +489,30 @@ def test_varlen_long_starts_at_wave_edges(lead, width, init):
     check_full(gd, activation="silu", label=f"wave edges {lead} W{width} {init} silu")
 
 
+@pytest.mark.parametrize("nseq", [63, 64, 65])
+@pytest.mark.parametrize("width", [2, 4, 5])
+def test_varlen_padded_runs_either_side_of_64_sequences(nseq, width):
+    """Token-contiguous rows of 64 and 65 sequences -- either side of the
+    batch size up to which a wave keeps the table in its lanes -- with runs
+    of adjacent padded sequences (long, short and empty ones), so that chunks
+    lie wholly in padded tokens, straddle two padded sequences, or mix padded
+    and live tokens.  Exact values; every output (padded rows keep their
+    fill) and state compared bit for bit."""
+    g = torch.Generator().manual_seed(4000 + 10 * nseq + width)
+    lens = torch.randint(1, 90, (nseq,), generator=g).tolist()
+    lens[3:7] = [700, 5, 0, 301]                  # a padded run in the middle
+    lens[-3:] = [9, 400, 2]                       # and at the end
+    d = W.varlen_batch(lengths=lens, dim=11, width=width, seed=4100 + nseq + width,
+                       num_lines=nseq + 4, n_pad=0, layout="dim_tok", values="exact")
+    for i in (3, 4, 5, 6, nseq - 3, nseq - 2, 20):
+        d["cache_indices"][i] = W.PAD_SLOT_ID
+    assert int(d["query_start_loc"][-1]) >= 2048
+    say(f"[fwd] padded runs nseq {nseq} W{width} T={int(d['query_start_loc'][-1])}")
+    gd = to_dev(d)
+    check_full(gd, activation=None, exact=True, label=f"padded runs {nseq} W{width}")
+    check_full(gd, activation="silu", label=f"padded runs {nseq} W{width} silu")
+
+
 @pytest.mark.parametrize("layout", ["dim_tok", "tok_dim"])
 @pytest.mark.parametrize("nseq", [2047, 2048])
 def test_varlen_batch_size_at_lds_table_limit(nseq, layout):
