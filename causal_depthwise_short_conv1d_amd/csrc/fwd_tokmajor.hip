@@ -897,7 +897,8 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     const int32_t B = p.sb.batch;
     const uint32_t T = p.T;
 
-    // A chunk wave issues its x loads before the tables are staged, so the
+    // A chunk wave issues its x loads before the table is staged (or, for
+    // small batches, right after reading its lanes' entries), so the
     // staging's round trip and barrier overlap them.  Full chunks go through
     // a descriptor that ends at the last one (no branch); only the last wave
     // reads a ragged last chunk element by element.  The wave-uniform rows'
@@ -1008,12 +1009,13 @@ __global__ __launch_bounds__(kVarWaves * kWaveSize) void fwd_tok_varlen_kernel(F
     const uint32_t row_a = cA * T, row_end = row_a + T;
     const uint32_t e_end = e_first + kWaveElems <= p.n_elems ? e_first + kWaveElems : p.n_elems;
 
-    // A chunk whose tokens all lie in padded sequences is never stored and
-    // feeds no stored output (an output at position width-1 or later of a
-    // sequence reads that sequence's inputs only; earlier ones are rewritten
-    // by the head launch), so its load is skipped.  Finding those chunks
-    // takes one read of the batch's table first: batches of at most 64
-    // sequences, one sequence per lane; larger batches load every chunk.
+    // Batches of at most 64 sequences read the table first, one sequence per
+    // lane (the lanes keep it; the chunk path below copies it into the
+    // wave's LDS rows).  A chunk whose tokens all lie in padded sequences is
+    // never stored and feeds no stored output (an output at position width-1
+    // or later of a sequence reads that sequence's inputs only; earlier ones
+    // are rewritten by the head launch), so its load is skipped.  Larger
+    // batches load every chunk.
     uint32_t dead = 0;                                      // bit r: round r's chunk
     int32_t a = 0, b = 0;                                   // lane q: query_start_loc[q], [q+1]
     bool pad = false;                                       // lane q: sequence q is padded
