@@ -9,8 +9,11 @@
 // The taps pair two rows' values of a channel with one byte permute and
 // accumulate them with the gfx950 dot2 instruction (exact products, fp32
 // sums); keeping rows and weights packed halves the registers, which is what
-// sets the occupancy of this streaming kernel.  All lanes of a wave share
-// the token, so the sequence bookkeeping is wave-uniform.
+// sets the occupancy of this streaming kernel.  A pair of consecutive rows
+// serves every second output after it, so the tile walk forms each pair
+// once.  All lanes of a wave share the token, so the sequence bookkeeping is
+// wave-uniform, and a lane with no channels stores through an offset past
+// the descriptor's extent rather than behind a branch.
 //
 // Ownership of a sequence's history: the tile holding the sequence's first
 // token processes the first width-1 tokens of that sequence (spilling past
@@ -128,6 +131,39 @@ __device__ __forceinline__ u32x2 conv_row(const LaneTaps<W> &tp, const u32x2 (&w
     return u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
 }
 
+// The 4 cross-row pairs (x[s-1][ch], x[s][ch]) of a lane's channels.
+struct RowPairs {
+    uint32_t v[kCpl];
+};
+__device__ __forceinline__ RowPairs row_pairs(const u32x2 &ra, const u32x2 &rb) {
+    RowPairs r;
+#pragma unroll
+    for (int ch = 0; ch < kCpl; ++ch) r.v[ch] = cross_pair(ra, rb, ch);
+    return r;
+}
+
+// conv_row from pairs: pw[k] holds the pairs ending at row t-(W-2)+k, so
+// tap pair q is pw[2q] (the newest, pw[W-2], ends at row t itself).  Each
+// pair is formed once and serves every second row after it; the sums are
+// the same, in the same order, as conv_row's.
+template <int W, bool SILU>
+__device__ __forceinline__ u32x2 conv_row_pairs(const LaneTaps<W> &tp,
+                                                const RowPairs (&pw)[W - 1], const u32x2 &x) {
+    float o[kCpl];
+#pragma unroll
+    for (int ch = 0; ch < kCpl; ++ch) {
+        float acc = tp.b[ch];
+#pragma unroll
+        for (int q = 0; q < W / 2; ++q) acc = dot2(pw[2 * q].v[ch], tp.wp[q][ch], acc);
+        if constexpr (W & 1) {
+            const uint32_t d = (ch >> 1) ? x.y : x.x;
+            acc = __builtin_fmaf(tp.wl[ch], (ch & 1) ? bf_hi(d) : bf_lo(d), acc);
+        }
+        o[ch] = act<SILU>(acc);
+    }
+    return u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+}
+
 template <int W, bool SILU, bool FULL>
 __device__ __forceinline__ void run_segment(const FwdClParams &p, const SeqInfo &si,
                                             int64_t b, int64_t e, bool head, int32_t c0,
@@ -217,6 +253,12 @@ __device__ __forceinline__ void run_segment(const FwdClParams &p, const SeqInfo 
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) xn[u] = ld_rows(xr, b + u, voff);
     }
+    // pw[k] = pairs ending at row t-H+1+k; the newest is formed at each row
+    const uint32_t soff = nv > 0 ? voff : kOob;
+    RowPairs pw[H];
+#pragma unroll
+    for (int k = 0; k + 1 < H; ++k) pw[k] = row_pairs(win[k], win[k + 1]);
+    u32x2 prev = win[H - 1];
     for (int64_t t = b; t < e; t += kUnroll) {
         const int n = (e - t) < kUnroll ? int(e - t) : kUnroll;
         u32x2 xv[kUnroll];
@@ -229,19 +271,26 @@ __device__ __forceinline__ void run_segment(const FwdClParams &p, const SeqInfo 
                 xv[u] = ld_row<FULL>(p.x + (t + u) * p.x_st + c0, nv);
             }
         }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            if (u < n) {
-                const u32x2 o = conv_row<W, SILU>(tp, win, xv[u]);
-                if constexpr (FULL) {
-                    if (nv > 0) st_rows(orr, t + u, voff, o);
-                } else {
-                    st_row<FULL>(p.out + (t + u) * p.o_st + c0, o, nv);
-                }
-#pragma unroll
-                for (int k = 0; k + 1 < H; ++k) win[k] = win[k + 1];
-                win[H - 1] = xv[u];
+        auto row = [&](int u) {
+            pw[H - 1] = row_pairs(prev, xv[u]);
+            const u32x2 o = conv_row_pairs<W, SILU>(tp, pw, xv[u]);
+            if constexpr (FULL) {
+                st_rows(orr, t + u, soff, o);                  // idle lanes: dropped
+            } else {
+                st_row<FULL>(p.out + (t + u) * p.o_st + c0, o, nv);
             }
+#pragma unroll
+            for (int k = 0; k + 1 < H; ++k) pw[k] = pw[k + 1];
+            prev = xv[u];
+        };
+        // a whole batch runs unguarded, so the window shifts are renamings
+        if (n == kUnroll) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) row(u);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                if (u < n) row(u);
         }
     }
 }
@@ -369,6 +418,7 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_cl_one_kerne
     const int nv = c0 < p.dim ? kCpl : 0;            // whole lanes
     if (nv == 0) c0 = 0;                             // idle lane: in-range reads, no writes
     const uint32_t voff = uint32_t(c0) * 2;
+    const uint32_t soff = nv > 0 ? voff : kOob;
     const int64_t T = p.sb.total_T;
     const int64_t g0 = int64_t(grp) * kOneGroup;
     const int64_t t0 = g0 + int64_t(wave) * kOneRows;
@@ -411,7 +461,7 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_cl_one_kerne
 #pragma unroll
         for (int k = 0; k < H; ++k) own[k] = xv[u - H + k];
         const u32x2 o = conv_row<W, SILU>(tp, own, xv[u]);
-        if (nv > 0) st_rows(orr, t0 + u, voff, o);     // rows past T: dropped
+        st_rows(orr, t0 + u, soff, o);     // rows past T, idle lanes: dropped
     }
 #pragma unroll
     for (int k = 0; k < H; ++k) edge[wave][k][lane] = xv[kOneRows - H + k];
@@ -458,7 +508,7 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_cl_one_kerne
 #pragma unroll
     for (int u = 0; u < H; ++u) {
         const u32x2 o = conv_row<W, SILU>(tp, win, xv[u]);
-        if (nv > 0) st_rows(orr, t0 + u, voff, o);     // rows past T: dropped
+        st_rows(orr, t0 + u, soff, o);     // rows past T, idle lanes: dropped
 #pragma unroll
         for (int k = 0; k + 1 < H; ++k) win[k] = win[k + 1];
         win[H - 1] = xv[u];

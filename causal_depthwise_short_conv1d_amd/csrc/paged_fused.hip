@@ -99,6 +99,9 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
     // byte offsets of the lane's 4 channels inside a block and inside a row
     const uint32_t coff = uint32_t((int64_t(c0 / st.ws) * p.c_sh + (st.off_s + c0 % st.ws)) * 2);
     const uint32_t xoff = uint32_t(c0) * 2;
+    // store offsets: an idle lane's stores land past every extent (dropped)
+    const uint32_t coff_st = active ? coff : kOob;
+    const uint32_t xoff_st = active ? xoff : kOob;
 
     // What depends only on the tile is issued before the query_start_loc
     // staging and the metadata round trips: the token's slot and position
@@ -246,10 +249,10 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
                 float o[kPCpl];
                 if (!pad) {
                     const int32_t sblk = __builtin_amdgcn_readlane(m_sblk, uu);
-                    if (sblk >= 0 && active) {
+                    if (sblk >= 0) {
                         const int32_t sn = __builtin_amdgcn_readlane(m_sn, uu);
                         const __amdgpu_buffer_rsrc_t cr = rsrc(p.cache + int64_t(sblk) * p.c_sb, p.c_sb * 2);
-                        st8<0>(cr, coff, int64_t(sn) * p.c_sn * 2, xv[u]);
+                        st8<0>(cr, coff_st, int64_t(sn) * p.c_sn * 2, xv[u]);
                     }
                     // the taps' input rows: a window row, a cached row or zero
                     u32x2 in[W];
@@ -283,8 +286,7 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
                 }
                 // a temporal store: the L2 gathers each output row from the
                 // pieces the waves of its other slabs write
-                if (active)
-                    st8<0>(orr, xoff, (t - tile_start) * st.o_st * 2,
+                st8<0>(orr, xoff_st, (t - tile_start) * st.o_st * 2,
                            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
 #pragma unroll
                 for (int k = 0; k + 1 < H; ++k) win[k] = win[k + 1];
