@@ -372,8 +372,9 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_chanlast_ker
     // wave index within the block: uniform, and marked so for the compiler
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
     const uint32_t wt = blockIdx.x * kClWavesPerBlock + wave;
-    const int32_t slab = int32_t(wt % uint32_t(p.n_slabs));
-    const int32_t tt = int32_t(wt / uint32_t(p.n_slabs));
+    const uint32_t tq = p.div_slabs.div(wt);
+    const int32_t slab = int32_t(wt - tq * uint32_t(p.n_slabs));
+    const int32_t tt = int32_t(tq);
     if (tt >= p.n_tiles) return;
 
     int32_t c0 = slab * kClSlab + lane * kCpl;
@@ -410,8 +411,9 @@ __global__ __launch_bounds__(kClWavesPerBlock * kWaveSize) void fwd_cl_one_kerne
     __shared__ u32x2 edge[kClWavesPerBlock][H][kWaveSize];   // each wave's last H rows
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
-    const int32_t slab = int32_t(blockIdx.x % uint32_t(p.n_slabs));
-    const int32_t grp = int32_t(blockIdx.x / uint32_t(p.n_slabs));
+    const uint32_t gq = p.div_slabs.div(blockIdx.x);
+    const int32_t slab = int32_t(blockIdx.x - gq * uint32_t(p.n_slabs));
+    const int32_t grp = int32_t(gq);
     if (grp >= n_groups) return;                     // the whole workgroup
 
     int32_t c0 = slab * kClSlab + lane * kCpl;

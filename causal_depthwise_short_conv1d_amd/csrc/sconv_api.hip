@@ -202,6 +202,7 @@ int conv1d_fwd_varlen(const void *x, int64_t x_stride_dim, int64_t x_stride_tok,
         p.sb = sb;
         p.dim = dim;
         p.n_slabs = (dim + kClSlab - 1) / kClSlab;
+        p.div_slabs = FastDivU32::make(uint32_t(p.n_slabs));
         p.bt = chanlast_tile(T, p.n_slabs, batch);
         // one descriptor spans a tile's rows (plus the spilled head) and one
         // state line

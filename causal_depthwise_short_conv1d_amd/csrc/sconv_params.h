@@ -79,7 +79,8 @@ struct FwdClParams {           // channel-contiguous (T, dim) storage
     const uint16_t *bias;
     SeqBatch sb;
     int32_t dim;
-    int32_t n_slabs;           // ceil(dim / 512)
+    int32_t n_slabs;           // ceil(dim / 256): 256-channel slabs
+    FastDivU32 div_slabs;      // division by n_slabs (a wave's tile and slab)
     int32_t bt;                // tokens per wave tile
     int32_t n_tiles;           // ceil(T / bt)
 };
