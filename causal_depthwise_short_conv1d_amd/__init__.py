@@ -14,7 +14,8 @@ Entry points (same names as the C ABI):
   sconv_paged_fused    -- paged sliding-window cache insert + conv
   sconv_paged_fused_multi -- several conv streams sharing one paged cache
   sconv_seq_metadata   -- per-token (request, first row) buffers
-bind_update_decode marshals a decode step once for repeated launches.
+bind_fwd_varlen and bind_update_decode marshal a forward or a decode step
+once for repeated launches.
 """
 from __future__ import annotations
 
@@ -24,7 +25,8 @@ import os
 import torch
 
 __all__ = ["conv1d_fwd_varlen", "conv1d_update_decode", "conv1d_update", "sconv_paged_fused",
-           "sconv_paged_fused_multi", "sconv_seq_metadata", "new_output", "bind_update_decode",
+           "sconv_paged_fused_multi", "sconv_seq_metadata", "new_output", "bind_fwd_varlen",
+           "bind_update_decode",
            "SconvError", "library_path", "load_library", "exported_symbols",
            "version", "status_string"]
 
@@ -182,16 +184,10 @@ def new_output(x: torch.Tensor) -> torch.Tensor:
     return torch.empty((total, pitch), dtype=x.dtype, device=x.device)[:, :dim].t()
 
 
-def conv1d_fwd_varlen(x, weight, bias, conv_states, query_start_loc,
-                      cache_indices=None, has_initial_state=None,
-                      activation="silu", pad_slot_id: int = -1, out=None):
-    """Varlen prefill.  x: logical (dim, total_T) bf16 with any strides
-    (compact (dim, T) and 16-byte aligned (T, dim) rows take the vector
-    kernels); weight (dim, width); bias (dim,) or None; conv_states
-    (lines, dim, width-1) or None, updated in place; query_start_loc int32
-    (batch+1,); cache_indices int32 (batch,) or None; has_initial_state bool
-    (batch,) or None.  Returns out (a new tensor with x's strides unless
-    given; see new_output)."""
+def _fwd_varlen_args(x, weight, bias, conv_states, query_start_loc, cache_indices,
+                     has_initial_state, activation, pad_slot_id, out):
+    """Checked and marshalled arguments of conv1d_fwd_varlen (all but the
+    stream), and the output tensor."""
     dev = x.device
     dim, total = x.shape
     width = weight.shape[1]
@@ -221,8 +217,47 @@ def conv1d_fwd_varlen(x, weight, bias, conv_states, query_start_loc,
         batch, total, dim, width, _act(activation), pad_slot_id,
         _dev(out, bf, "out", dev), out.stride(0), out.stride(1),
     )
-    _launch("conv1d_fwd_varlen", dev, args)
+    return args, out
+
+
+def conv1d_fwd_varlen(x, weight, bias, conv_states, query_start_loc,
+                      cache_indices=None, has_initial_state=None,
+                      activation="silu", pad_slot_id: int = -1, out=None):
+    """Varlen prefill.  x: logical (dim, total_T) bf16 with any strides
+    (compact (dim, T) and 16-byte aligned (T, dim) rows take the vector
+    kernels); weight (dim, width); bias (dim,) or None; conv_states
+    (lines, dim, width-1) or None, updated in place; query_start_loc int32
+    (batch+1,); cache_indices int32 (batch,) or None; has_initial_state bool
+    (batch,) or None.  Returns out (a new tensor with x's strides unless
+    given; see new_output)."""
+    args, out = _fwd_varlen_args(x, weight, bias, conv_states, query_start_loc, cache_indices,
+                                 has_initial_state, activation, pad_slot_id, out)
+    _launch("conv1d_fwd_varlen", x.device, args)
     return out
+
+
+def bind_fwd_varlen(x, weight, bias, conv_states, query_start_loc, cache_indices=None,
+                    has_initial_state=None, activation="silu", pad_slot_id: int = -1,
+                    out=None, stream=None):
+    """A pre-bound conv1d_fwd_varlen for a caller that runs the same forward
+    over and over on fixed buffers (a prefill loop over preallocated
+    batches): the tensors are checked and marshalled once, here, and the
+    returned function only enqueues the launch on `stream` (default: the
+    current stream of x's device now) and raises on a non-zero status.  Its
+    `out` attribute is the output tensor.  The tensors must stay alive and
+    in place while the function is used."""
+    args, out = _fwd_varlen_args(x, weight, bias, conv_states, query_start_loc, cache_indices,
+                                 has_initial_state, activation, pad_slot_id, out)
+    st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(x.device)
+    f = load_library().conv1d_fwd_varlen
+    full = (*args, st)
+
+    def launch():
+        rc = f(*full)
+        if rc != 0:
+            raise SconvError("conv1d_fwd_varlen", rc)
+    launch.out = out
+    return launch
 
 
 def conv1d_update_decode(x, conv_state, weight, bias=None, activation=None,

@@ -672,3 +672,27 @@ def test_repeat_is_deterministic():
     b, sb = run_gpu(d, out_fill=0.0)
     assert_bits(a, b, "repeat out")
     assert_bits(sa, sb, "repeat state")
+
+
+@pytest.mark.parametrize("layout", ["dim_tok", "tok_dim"])
+def test_bound_forward_equals_the_call(layout):
+    """bind_fwd_varlen marshals once and then launches exactly what
+    conv1d_fwd_varlen launches: outputs and states bit-identical over
+    repeated steps, each step carrying the state the previous one wrote."""
+    d = W.varlen_batch(lengths=[300, 0, 5, 2100, 1], dim=520, width=4, seed=990, num_lines=8,
+                       n_pad=1, layout=layout, device=DEV)
+    st_a, st_b = d["conv_states"].clone(), d["conv_states"].clone()
+    oa = torch.full_like(S.new_output(d["x"]), -3.0)
+    ob = torch.full_like(oa, -3.0)
+    kw = dict(cache_indices=d["cache_indices"], has_initial_state=d["has_initial_state"],
+              activation="silu")
+    launch = S.bind_fwd_varlen(d["x"], d["weight"], d["bias"], st_b, d["query_start_loc"],
+                               out=ob, **kw)
+    assert launch.out is ob
+    for step in range(3):
+        S.conv1d_fwd_varlen(d["x"], d["weight"], d["bias"], st_a, d["query_start_loc"],
+                            out=oa, **kw)
+        launch()
+        torch.cuda.synchronize()
+        assert_bits(ob, oa, f"bound forward {layout} step {step} out")
+        assert_bits(st_b, st_a, f"bound forward {layout} step {step} state")
