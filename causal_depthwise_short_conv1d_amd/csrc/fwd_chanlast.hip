@@ -253,8 +253,8 @@ __device__ __forceinline__ void run_segment(const FwdClParams &p, const SeqInfo 
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) xn[u] = ld_rows(xr, b + u, voff);
     }
+    const uint32_t soff = nv > 0 ? voff : kOob;    // idle lanes store past the extent
     // pw[k] = pairs ending at row t-H+1+k; the newest is formed at each row
-    const uint32_t soff = nv > 0 ? voff : kOob;
     RowPairs pw[H];
 #pragma unroll
     for (int k = 0; k + 1 < H; ++k) pw[k] = row_pairs(win[k], win[k + 1]);

@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kPagedWavesPerBlock * kWaveSize) void paged_fused_k
                 // a temporal store: the L2 gathers each output row from the
                 // pieces the waves of its other slabs write
                 st8<0>(orr, xoff_st, (t - tile_start) * st.o_st * 2,
-                           u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
+                       u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
 #pragma unroll
                 for (int k = 0; k + 1 < H; ++k) win[k] = win[k + 1];
                 win[H - 1] = xv[u];
